@@ -1,0 +1,373 @@
+"""fp64 CPU oracle for the forward pass of a sparse mixture-of-experts FFN layer
+with a per-expert capacity limit.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, header, table
+or helper with the HIP library and imports nothing from it.
+
+It is written to be slow and obviously right.  Every step follows the order in
+which the pages walk a token through the layer, and every function names the
+passage it restates.  Page titles used in the citations:
+
+* [Mixtral explainer]  "Mixtral 8x7B and MoE explained: sparse mixture of
+  experts, two experts per token" (allinfo.ai.kr)
+* [MoE explained]      "Mixture-of-experts models, explained simply"
+  (welclai.com)
+* [MoE wiki]           "Mixture of experts" (wikiprompt.org)
+* [Routing guide]      "MoE routing, fully explained: Mixtral/DeepSeek
+  structure, load balancing, capacity factor" (allinfo.ai.kr)
+
+Sections of the allinfo.ai.kr pages are "Key messages", "Plain explanation"
+(paragraphs numbered from 1) and "Key insights".
+
+Precision: everything is float64.  bf16 or fp32 inputs are widened exactly.
+No intermediate is rounded.  The matrix products use ``numpy.matmul`` (a library
+primitive); routing and dispatch are explicit loops in token order.
+
+Readings taken where the pages leave a step open (each one also listed in the
+design notes):
+
+* top-k ties go to the lower expert index; -0.0 equals +0.0 (IEEE compare);
+* capacity C = ceil(T*k*cf/E) computed exactly on the decimal value of cf;
+  with no limit (cf <= 0) C = T, the most one expert can ever receive;
+* overflow is dropped latest-first in flat assignment order a = t*k + j;
+* a dropped assignment contributes zero and the surviving gates are NOT
+  renormalised; a token with every assignment dropped outputs only the
+  shared-expert sum (zero without shared experts);
+* expert FFN is SwiGLU with silu on the W1 branch: (silu(x W1) * (x W3)) W2;
+* shared experts are added with gate 1;
+* load-balance statistics use pre-drop fractions f_i = count_i/(T*k) and the
+  mean full softmax P_i over all E experts in both gating modes;
+* "routing entropy" is reported two ways: entropy of the expert-load
+  distribution and the mean per-token router entropy, both in nats.
+
+Nothing here is "parity unpinned": every function is checked by
+``tests/test_oracle_pins.py`` against page values, closed forms, library
+routines or brute force.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from fractions import Fraction
+from typing import Callable, Optional, Sequence
+
+import numpy as np
+
+TOPK_THEN_SOFTMAX = 0  # Mixtral-style gating
+SOFTMAX_THEN_TOPK = 1  # DeepSeek-style gating
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    """Shape and routing options of one MoE layer call."""
+
+    T: int          # tokens in this call (the "batch" of the capacity formula)
+    d: int          # model width
+    F: int          # expert hidden width
+    E: int          # routed experts
+    k: int          # experts kept per token
+    S: int = 0      # always-on shared experts
+    gating: int = TOPK_THEN_SOFTMAX
+    renormalize: bool = True
+    capacity_factor: float = 0.0   # <= 0: no limit
+
+
+# ---------------------------------------------------------------------------
+# Capacity.  [Routing guide] "Plain explanation" paragraph 5: the per-expert
+# buffer is about batch x top-k x capacity factor / number of experts; the
+# page works 2048 tokens, 8 experts, top-2, factor 1.25 to about 640 slots.
+# ---------------------------------------------------------------------------
+def capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
+    """Token slots per expert.
+
+    The pages give the formula only approximately; the reading here rounds up
+    the exact rational value, taking the capacity factor as the decimal number
+    it is written as (1.1 means 11/10, not the nearest binary double).
+    Without a limit the capacity is T: one token never selects one expert twice.
+    """
+    if capacity_factor is None or capacity_factor <= 0:
+        return int(T)
+    cf = Fraction(repr(float(capacity_factor)))
+    q = Fraction(int(T) * int(k)) * cf / int(E)
+    return int(math.ceil(q))
+
+
+# ---------------------------------------------------------------------------
+# Router.  [Mixtral explainer] "Plain explanation" paragraph 3 and [Routing
+# guide] "Plain explanation" paragraph 2: a small learned network scores every
+# expert for each token, like a classifier producing one logit per class.
+# ---------------------------------------------------------------------------
+def router_logits(x: np.ndarray, W_gate: np.ndarray,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """logits[t, i] = sum_c x[t, c] * W_gate[c, i] (+ bias[i]), in float64.
+
+    W_gate is stored [d, E] (input dimension first).  The optional bias is the
+    per-expert logit offset of the skewed-routing workload; it is added before
+    any selection, gating or statistic sees the logits.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    w64 = np.asarray(W_gate, dtype=np.float64)
+    logits = np.matmul(x64, w64)
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+    return logits
+
+
+# ---------------------------------------------------------------------------
+# Top-k selection.  [Mixtral explainer] "Plain explanation" paragraph 3 keeps
+# the two highest-scoring of eight experts; [Routing guide] "Plain explanation"
+# paragraphs 2 and 4 keep the top k (two for Mixtral, six for DeepSeek V2).
+# ---------------------------------------------------------------------------
+def topk_select(logits: np.ndarray, k: int):
+    """Per token, the k experts with the largest logits, best first.
+
+    Experts are ordered by (logit descending, index ascending).  Python's
+    tuple comparison uses IEEE equality on floats, so -0.0 and +0.0 tie and the
+    lower index wins.  Also returns, per token, the smallest gap between
+    neighbours among the top min(k+1, E) sorted logits: the margin by which
+    both the chosen set and its order are decided.
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    if not np.all(np.isfinite(logits)):
+        raise ValueError("router logits must be finite")
+    sel = np.empty((T, k), dtype=np.int64)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        row = logits[t]
+        order = sorted(range(E), key=lambda i: (-row[i], i))
+        sel[t] = order[:k]
+        top = [row[i] for i in order[:min(k + 1, E)]]
+        for a, b in zip(top[:-1], top[1:]):
+            margin[t] = min(margin[t], a - b)
+    return sel, margin
+
+
+def softmax_all(logits: np.ndarray) -> np.ndarray:
+    """Probability over all E experts per token ([Routing guide] "Plain
+    explanation" paragraph 2: the router produces a distribution over every
+    expert).  Shifted by the row maximum before exponentiating."""
+    logits = np.asarray(logits, dtype=np.float64)
+    z = logits - logits.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Gate weights.
+#   Mixtral style ([Mixtral explainer] "Plain explanation" paragraph 3):
+#     softmax taken over the k selected logits only.
+#   DeepSeek style ([Routing guide] "Plain explanation" paragraphs 2 and 4):
+#     softmax over all experts first, then the top-k probabilities are used;
+#     the DeepSeek-shaped workload keeps them without renormalising.
+# ---------------------------------------------------------------------------
+def gate_weights(logits: np.ndarray, sel: np.ndarray, gating: int,
+                 renormalize: bool) -> np.ndarray:
+    logits = np.asarray(logits, dtype=np.float64)
+    T, k = sel.shape
+    w = np.empty((T, k), dtype=np.float64)
+    if gating == TOPK_THEN_SOFTMAX:
+        for t in range(T):
+            chosen = logits[t, sel[t]]
+            e = np.exp(chosen - chosen[0])   # chosen[0] is the largest
+            w[t] = e / e.sum()
+    elif gating == SOFTMAX_THEN_TOPK:
+        p = softmax_all(logits)
+        for t in range(T):
+            w[t] = p[t, sel[t]]
+            if renormalize:
+                w[t] = w[t] / w[t].sum()
+    else:
+        raise ValueError(f"unknown gating mode {gating}")
+    return w
+
+
+# ---------------------------------------------------------------------------
+# Dispatch with a capacity limit.  [Routing guide] "Plain explanation"
+# paragraph 3: each expert takes a fixed number of tokens per batch and the
+# simplest overflow policy drops the excess; paragraph 5 sizes the buffer.
+# ---------------------------------------------------------------------------
+def dispatch(sel: np.ndarray, E: int, C: int) -> dict:
+    """Assign every (token, choice) pair a slot in its expert's buffer.
+
+    Assignments are visited in flat order a = t*k + j.  rank[a] counts the
+    earlier assignments to the same expert; the assignment is kept when
+    rank < C.  Kept rows of expert e occupy slots offsets[e] .. offsets[e+1]-1
+    in visiting order; perm[slot] gives back the assignment.  Dropped
+    assignments get slot -1.
+    """
+    T, k = sel.shape
+    flat = [int(v) for v in sel.reshape(-1)]
+    seen = [0] * E
+    rank = [0] * len(flat)
+    for a, e in enumerate(flat):
+        rank[a] = seen[e]
+        seen[e] += 1
+    counts = np.array(seen, dtype=np.int64)
+    kcount = np.minimum(counts, C)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + kcount[e]
+    slot = np.full(len(flat), -1, dtype=np.int64)
+    perm = np.full(int(offsets[E]), -1, dtype=np.int64)
+    for a, e in enumerate(flat):
+        if rank[a] < C:
+            s = int(offsets[e]) + rank[a]
+            slot[a] = s
+            perm[s] = a
+    return dict(counts=counts, kept=kcount, offsets=offsets,
+                rank=np.array(rank, dtype=np.int64), slot=slot, perm=perm,
+                dropped=int(np.sum(counts - kcount)), capacity=int(C))
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN.  [Mixtral explainer] "Plain explanation" paragraph 2: the
+# feed-forward block widens the token vector (about 4k) to a hidden width
+# (about 14k) and back, token by token.  The gated SwiGLU form is the
+# workload's choice; the pages do not name the activation.
+# ---------------------------------------------------------------------------
+def silu(u: np.ndarray) -> np.ndarray:
+    """u * sigmoid(u), written as u / (1 + exp(-u))."""
+    with np.errstate(over="ignore"):
+        return u / (1.0 + np.exp(-u))
+
+
+def expert_ffn(X: np.ndarray, W1: np.ndarray, W3: np.ndarray,
+               W2: np.ndarray) -> np.ndarray:
+    """(silu(X W1) * (X W3)) W2 for rows X [n, d]; W1, W3 [d, F]; W2 [F, d]."""
+    X = np.asarray(X, dtype=np.float64)
+    u = np.matmul(X, np.asarray(W1, dtype=np.float64))
+    v = np.matmul(X, np.asarray(W3, dtype=np.float64))
+    h = silu(u) * v
+    return np.matmul(h, np.asarray(W2, dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Load-balance and routing statistics.  [Routing guide] "Plain explanation"
+# paragraph 4: per expert, multiply the fraction of tokens it actually got by
+# the total probability the router gave it, and sum; "Key insights" item 3
+# lists per-expert token counts, overflow rate and routing entropy among the
+# quantities to watch.
+# ---------------------------------------------------------------------------
+def routing_stats(counts: np.ndarray, kept: np.ndarray, p: np.ndarray,
+                  T: int, k: int, E: int) -> dict:
+    """aux = E * sum_i f_i * P_i with f_i = count_i / (T k) (before drops) and
+    P_i the mean over tokens of the full softmax.  It equals 1 when both are
+    uniform.  Also: overflow rate = dropped / (T k); entropy of the load
+    distribution f (0 ln 0 = 0); mean per-token entropy of p.  All in nats.
+    An empty call (T = 0) reports zeros."""
+    counts = np.asarray(counts, dtype=np.int64)
+    kept = np.asarray(kept, dtype=np.int64)
+    n_assign = T * k
+    dropped = int(np.sum(counts - kept))
+    if T == 0:
+        return dict(aux_loss=0.0, aux_loss_kept=0.0, overflow_rate=0.0,
+                    entropy_load=0.0, entropy_token=0.0, dropped=0,
+                    assignments=0, P=np.zeros(E))
+    f = counts.astype(np.float64) / n_assign
+    f_kept = kept.astype(np.float64) / n_assign
+    P = np.asarray(p, dtype=np.float64).mean(axis=0)
+    aux = E * float(np.sum(f * P))
+    aux_kept = E * float(np.sum(f_kept * P))
+    h_load = 0.0
+    for fi in f:
+        if fi > 0:
+            h_load -= fi * math.log(fi)
+    pt = np.asarray(p, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(pt > 0, pt * np.log(pt), 0.0)
+    h_tok = float(np.mean(-terms.sum(axis=1)))
+    return dict(aux_loss=aux, aux_loss_kept=aux_kept,
+                overflow_rate=dropped / n_assign, entropy_load=h_load,
+                entropy_token=h_tok, dropped=dropped, assignments=n_assign,
+                P=P)
+
+
+# ---------------------------------------------------------------------------
+# The whole layer.  [Routing guide] "Plain explanation" paragraphs 2-5 and
+# [MoE wiki] "How it works": score, keep top-k, handle overflow, run only the
+# chosen experts, take the gate-weighted sum; [Routing guide] paragraph 4 adds
+# always-on shared experts (DeepSeek V2: two shared plus top-6 routed).
+# ---------------------------------------------------------------------------
+ExpertWeights = Callable[[int], Sequence[np.ndarray]]
+
+
+def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
+            W_gate: Optional[np.ndarray] = None,
+            bias: Optional[np.ndarray] = None,
+            logits: Optional[np.ndarray] = None,
+            tokens: Optional[Sequence[int]] = None) -> dict:
+    """Run the layer for all T tokens' routing and the requested tokens' output.
+
+    expert_weights(e) returns (W1[e], W3[e], W2[e]); experts E .. E+S-1 are the
+    shared ones.  Either W_gate (+ optional bias) or precomputed router logits
+    must be given.  ``tokens`` limits which output rows are computed (routing,
+    dispatch and statistics always cover all T tokens); rows not computed are
+    NaN in ``out``.
+    """
+    T, d, E, k, S = shape.T, shape.d, shape.E, shape.k, shape.S
+    x = np.asarray(x)
+    if logits is None:
+        logits = router_logits(x, W_gate, bias)
+    logits = np.asarray(logits, dtype=np.float64)
+    sel, margin = topk_select(logits, k)
+    w = gate_weights(logits, sel, shape.gating, shape.renormalize)
+    p = softmax_all(logits) if T > 0 else np.zeros((0, E))
+    C = capacity(T, k, E, shape.capacity_factor)
+    disp = dispatch(sel, E, C)
+    stats = routing_stats(disp["counts"], disp["kept"], p, T, k, E)
+
+    want = np.zeros(T, dtype=bool)
+    if tokens is None:
+        want[:] = True
+    else:
+        want[np.asarray(list(tokens), dtype=np.int64)] = True
+    out = np.full((T, d), np.nan)
+    out[want] = 0.0
+
+    # Routed experts: each expert runs once on its kept rows, in slot order.
+    for e in range(E):
+        lo, hi = int(disp["offsets"][e]), int(disp["offsets"][e + 1])
+        rows = [int(a) for a in disp["perm"][lo:hi] if want[int(a) // k]]
+        if not rows:
+            continue
+        W1e, W3e, W2e = expert_weights(e)
+        toks = [a // k for a in rows]
+        Y = expert_ffn(np.asarray(x[toks], dtype=np.float64), W1e, W3e, W2e)
+        for r, a in enumerate(rows):
+            t, j = divmod(a, k)
+            out[t] += w[t, j] * Y[r]
+
+    # Shared experts: every token, gate 1.
+    shared = None
+    if S > 0:
+        idx = np.nonzero(want)[0]
+        shared = np.zeros((len(idx), d))
+        for s in range(S):
+            W1s, W3s, W2s = expert_weights(E + s)
+            shared += expert_ffn(np.asarray(x[idx], dtype=np.float64),
+                                 W1s, W3s, W2s)
+        out[idx] += shared
+
+    return dict(out=out, logits=logits, sel=sel, margin=margin, w=w, p=p,
+                capacity=C, dispatch=disp, stats=stats)
+
+
+# ---------------------------------------------------------------------------
+# Brute-force top-k, used only to pin topk_select on tiny inputs.
+# ---------------------------------------------------------------------------
+def brute_topk_set(row: Sequence[float], k: int) -> tuple:
+    """Among all k-subsets of experts, the one with the largest exact sum of
+    logits; ties between subsets go to the lexicographically smallest sorted
+    index tuple.  Sums are exact rationals, so -0.0 and +0.0 are equal."""
+    from itertools import combinations
+    vals = [Fraction(float(v)) for v in row]
+    best, best_sum = None, None
+    for combo in combinations(range(len(vals)), k):
+        s = sum(vals[i] for i in combo)
+        if best is None or s > best_sum or (s == best_sum and combo < best):
+            best, best_sum = combo, s
+    return best

@@ -1,0 +1,424 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the
+oracle disagrees with a value printed on the pages (fixtures under
+tests/golden/), a closed form, a library routine (torch / scipy), an
+invariant, or brute force on tiny inputs.  tests/test_oracle_pins.py runs
+them on the real oracle; tests/test_oracle_mutations.py plants mistakes in
+the oracle and checks that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from itertools import product
+
+import numpy as np
+import scipy.special
+import scipy.stats
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _torch_ffn(X, W1, W3, W2):
+    """Library reference: torch fp64 SwiGLU FFN."""
+    X = torch.as_tensor(np.asarray(X, dtype=np.float64))
+    W1 = torch.as_tensor(np.asarray(W1, dtype=np.float64))
+    W3 = torch.as_tensor(np.asarray(W3, dtype=np.float64))
+    W2 = torch.as_tensor(np.asarray(W2, dtype=np.float64))
+    h = torch.nn.functional.silu(X @ W1) * (X @ W3)
+    return (h @ W2).numpy()
+
+
+def _experts(n, d, F, seed):
+    r = _rng(seed)
+    return [(r.standard_normal((d, F)) / math.sqrt(d),
+             r.standard_normal((d, F)) / math.sqrt(d),
+             r.standard_normal((F, d)) / math.sqrt(F)) for _ in range(n)]
+
+
+# ---------------------------------------------------------------- capacity
+def pin_capacity_worked_example(O):
+    g = golden("capacity_worked_example.json")
+    assert O.capacity(g["tokens"], g["top_k"], g["experts"],
+                      g["capacity_factor"]) == g["capacity"]
+
+
+def pin_capacity_rounding(O):
+    # Exact decimal reading: 100 tokens x 2 x 1.1 / 2 = 110 exactly (a binary
+    # double product would land just above 110 and round up to 111).
+    assert O.capacity(100, 2, 2, 1.1) == 110
+    # Non-integer value rounds up (the reading for the page's "about").
+    assert O.capacity(10, 1, 4, 1.0) == 3
+    assert O.capacity(1, 1, 8, 1.0) == 1
+    # The recommended range brackets the worked example's factor.
+    g = golden("recommended_capacity_factor.json")
+    lo = O.capacity(2048, 2, 8, g["low"])
+    hi = O.capacity(2048, 2, 8, g["high"])
+    assert (lo, hi) == (640, 768)
+    # No limit: an expert can take every token once.
+    for T in (0, 1, 7, 2048):
+        assert O.capacity(T, 2, 8, 0.0) == T
+        assert O.capacity(T, 2, 8, -1.0) == T
+
+
+# ---------------------------------------------------------------- router
+def pin_router_one_hot(O):
+    # With d == E and one-hot token vectors, token t = e_c must score exactly
+    # row c of W_gate plus the bias; a transposed W_gate or a wrong bias sign
+    # breaks this.
+    r = _rng(1)
+    E = 5
+    Wg = r.standard_normal((E, E))
+    b = r.standard_normal(E)
+    x = np.eye(E)
+    got = O.router_logits(x, Wg, b)
+    assert np.array_equal(got, Wg + b[None, :])
+    got0 = O.router_logits(x, Wg, None)
+    assert np.array_equal(got0, Wg)
+
+
+# ---------------------------------------------------------------- top-k
+def _check_order(row, sel):
+    vals = [row[i] for i in sel]
+    for j in range(len(sel) - 1):
+        assert vals[j] >= vals[j + 1]
+        if vals[j] == vals[j + 1]:
+            assert sel[j] < sel[j + 1]
+
+
+def pin_topk_bruteforce(O):
+    r = _rng(2)
+    cases = []
+    for E in (1, 2, 3, 5, 8):
+        for _ in range(40):
+            row = r.standard_normal(E)
+            # inject exact ties, signed zeros and duplicates
+            if E > 1 and r.random() < 0.5:
+                i, j = r.choice(E, 2, replace=False)
+                row[j] = row[i]
+            if r.random() < 0.3:
+                row[r.integers(E)] = 0.0
+                row[r.integers(E)] = -0.0
+            if r.random() < 0.2:
+                row[:] = np.round(row)
+            cases.append(row)
+    cases.append(np.zeros(8))
+    cases.append(np.array([-0.0, 0.0, -0.0, 0.0]))
+    for row in cases:
+        E = len(row)
+        for k in range(1, E + 1):
+            sel, _ = O.topk_select(row[None, :], k)
+            sel = [int(v) for v in sel[0]]
+            assert tuple(sorted(sel)) == O.brute_topk_set(row, k), (row, k)
+            _check_order(row, sel)
+
+
+def pin_topk_signed_zero(O):
+    sel, margin = O.topk_select(np.array([[-0.0, 0.0, -1.0]]), 1)
+    assert sel[0, 0] == 0 and margin[0] == 0.0
+    sel, _ = O.topk_select(np.array([[0.0, -0.0, -1.0]]), 2)
+    assert list(sel[0]) == [0, 1]
+    sel, _ = O.topk_select(np.array([[-1.0, -0.0, 0.0]]), 2)
+    assert list(sel[0]) == [1, 2]
+
+
+def pin_topk_margin(O):
+    row = np.array([[3.0, 1.0, 2.5, 0.5]])
+    _, m = O.topk_select(row, 2)       # sorted 3, 2.5, 1 -> gaps .5, 1.5
+    assert m[0] == 0.5
+    _, m = O.topk_select(row, 1)       # 3, 2.5
+    assert m[0] == 0.5
+    _, m = O.topk_select(np.array([[4.0, 1.0, 3.9]]), 3)  # 4, 3.9, 1
+    assert abs(m[0] - 0.1) < 1e-12
+
+
+# ---------------------------------------------------------------- gates
+def pin_gates_topk_then_softmax(O):
+    r = _rng(3)
+    L = r.standard_normal((50, 8)) * 3
+    sel, _ = O.topk_select(L, 2)
+    w = O.gate_weights(L, sel, O.TOPK_THEN_SOFTMAX, True)
+    for t in range(50):
+        l0, l1 = L[t, sel[t, 0]], L[t, sel[t, 1]]
+        # two-way softmax is the logistic function of the logit gap
+        assert abs(w[t, 0] - 1.0 / (1.0 + math.exp(l1 - l0))) < 1e-15
+        assert abs(w[t].sum() - 1.0) < 1e-15
+    for k in (1, 3, 8):
+        sel, _ = O.topk_select(L, k)
+        w = O.gate_weights(L, sel, O.TOPK_THEN_SOFTMAX, True)
+        ref = scipy.special.softmax(np.take_along_axis(L, sel, 1), axis=1)
+        assert np.allclose(w, ref, rtol=0, atol=1e-15)
+
+
+def pin_gates_softmax_then_topk(O):
+    r = _rng(4)
+    L = r.standard_normal((40, 16)) * 2
+    sel, _ = O.topk_select(L, 6)
+    p = scipy.special.softmax(L, axis=1)
+    w = O.gate_weights(L, sel, O.SOFTMAX_THEN_TOPK, False)
+    assert np.allclose(w, np.take_along_axis(p, sel, 1), rtol=0, atol=1e-15)
+    assert np.all(w.sum(1) <= 1 + 1e-15)
+    wn = O.gate_weights(L, sel, O.SOFTMAX_THEN_TOPK, True)
+    assert np.allclose(wn.sum(1), 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(O.softmax_all(L), p, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- dispatch
+def pin_dispatch_stable_sort(O):
+    r = _rng(5)
+    for (T, E, k, C) in [(37, 4, 2, 9), (64, 8, 2, 16), (50, 5, 3, 1000),
+                         (29, 3, 1, 4), (40, 8, 8, 40), (33, 6, 2, 1)]:
+        L = r.standard_normal((T, E))
+        L[:, 0] += 1.0   # skew so some experts overflow
+        sel, _ = O.topk_select(L, k)
+        D = O.dispatch(sel, E, C)
+        flat = sel.reshape(-1)
+        order = sorted(range(T * k), key=lambda a: int(flat[a]))  # stable
+        ref_perm = []
+        for e in range(E):
+            mine = [a for a in order if flat[a] == e]
+            ref_perm += mine[:C]
+        assert list(D["perm"]) == ref_perm
+        cnt = np.bincount(flat, minlength=E)
+        assert np.array_equal(D["counts"], cnt)
+        assert np.array_equal(D["kept"], np.minimum(cnt, C))
+        assert int(D["kept"].sum()) == T * k - D["dropped"]
+        assert np.all(D["kept"] <= C)
+        for e in range(E):
+            if cnt[e] <= C:
+                assert D["kept"][e] == cnt[e]
+        assert D["offsets"][0] == 0
+        assert np.array_equal(np.diff(D["offsets"]), D["kept"])
+        for a in range(T * k):
+            s = D["slot"][a]
+            if s >= 0:
+                assert D["perm"][s] == a
+        assert int((D["slot"] >= 0).sum()) == len(D["perm"])
+
+
+def pin_dispatch_hand_example(O):
+    # Four tokens, one expert choice each, all on expert 0, two slots:
+    # the two earliest tokens keep their slots, the later two are dropped.
+    sel = np.array([[0], [0], [0], [0]])
+    D = O.dispatch(sel, 2, 2)
+    assert list(D["slot"]) == [0, 1, -1, -1]
+    assert list(D["perm"]) == [0, 1]
+    assert D["dropped"] == 2 and list(D["counts"]) == [4, 0]
+    # Two choices per token: expert order inside a token does not change the
+    # token-order priority.
+    sel = np.array([[1, 0], [0, 1], [1, 2]])
+    D = O.dispatch(sel, 3, 1)
+    # expert 0: a=1 (t0) kept; a=2 (t1) dropped.  expert 1: a=0 kept,
+    # a=3 and a=4 dropped.  expert 2: a=5 kept.
+    assert list(D["slot"]) == [1, 0, -1, -1, -1, 2]
+    assert list(D["perm"]) == [1, 0, 5]
+    assert list(D["offsets"]) == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------- FFN
+def pin_ffn_library(O):
+    r = _rng(6)
+    for (n, d, F) in [(7, 16, 24), (3, 8, 8), (5, 12, 12)]:
+        X = r.standard_normal((n, d))
+        W1, W3, W2 = _experts(1, d, F, 60 + n)[0]
+        got = O.expert_ffn(X, W1, W3, W2)
+        assert np.allclose(got, _torch_ffn(X, W1, W3, W2), rtol=1e-13,
+                           atol=1e-13)
+    u = np.array([-800.0, -30.0, -1.0, 0.0, 2.0, 40.0])
+    ref = torch.nn.functional.silu(torch.tensor(u, dtype=torch.float64))
+    assert np.allclose(O.silu(u), ref.numpy(), rtol=1e-15, atol=0)
+
+
+def _shape(O, T, d, F, E, k, S=0, gating=None, renorm=True, cf=0.0):
+    return O.LayerShape(T=T, d=d, F=F, E=E, k=k, S=S,
+                        gating=O.TOPK_THEN_SOFTMAX if gating is None else gating,
+                        renormalize=renorm, capacity_factor=cf)
+
+
+def pin_dense_equivalence(O):
+    # k = E, Mixtral gating, no limit: every expert runs on every token and
+    # the layer is the softmax-weighted dense sum; with W_gate = 0 the
+    # weights are uniform and it is the plain mean of the experts.
+    r = _rng(7)
+    T, d, F, E = 12, 16, 20, 4
+    x = r.standard_normal((T, d))
+    ex = _experts(E, d, F, 70)
+    dense = [_torch_ffn(x, *ex[e]) for e in range(E)]
+    res = O.forward(x, _shape(O, T, d, F, E, E), lambda e: ex[e],
+                    W_gate=np.zeros((d, E)))
+    assert np.allclose(res["out"], sum(dense) / E, rtol=1e-12, atol=1e-12)
+    Wg = r.standard_normal((d, E))
+    res = O.forward(x, _shape(O, T, d, F, E, E), lambda e: ex[e], W_gate=Wg)
+    p = scipy.special.softmax(x @ Wg, axis=1)
+    ref = sum(p[:, e:e + 1] * dense[e] for e in range(E))
+    assert np.allclose(res["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_identical_experts(O):
+    r = _rng(8)
+    T, d, F, E = 10, 8, 12, 6
+    x = r.standard_normal((T, d))
+    one = _experts(1, d, F, 80)[0]
+    Wg = r.standard_normal((d, E))
+    ref = _torch_ffn(x, *one)
+    res = O.forward(x, _shape(O, T, d, F, E, 2), lambda e: one, W_gate=Wg)
+    assert np.allclose(res["out"], ref, rtol=1e-12, atol=1e-12)
+    # DeepSeek gating, unrenormalised, plus shared experts: the routed part
+    # is (sum of kept probabilities) x FFN.
+    sh = _experts(2, d, F, 81)
+    experts = lambda e: one if e < E else sh[e - E]  # noqa: E731
+    res = O.forward(x, _shape(O, T, d, F, E, 3, S=2,
+                              gating=O.SOFTMAX_THEN_TOPK, renorm=False),
+                    experts, W_gate=Wg)
+    p = scipy.special.softmax(x @ Wg, axis=1)
+    top = np.sort(p, axis=1)[:, ::-1][:, :3].sum(1)
+    shared = _torch_ffn(x, *sh[0]) + _torch_ffn(x, *sh[1])
+    assert np.allclose(res["out"], top[:, None] * ref + shared, rtol=1e-12,
+                       atol=1e-12)
+
+
+def pin_shared_concat(O):
+    # S shared experts summed with gate 1 equal one FFN whose hidden layer is
+    # the concatenation of theirs.
+    r = _rng(9)
+    T, d, F, E, S = 9, 8, 6, 4, 2
+    x = r.standard_normal((T, d))
+    ex = _experts(E + S, d, F, 90)
+    Wg = r.standard_normal((d, E))
+    with_s = O.forward(x, _shape(O, T, d, F, E, 2, S=S), lambda e: ex[e],
+                       W_gate=Wg)["out"]
+    without = O.forward(x, _shape(O, T, d, F, E, 2, S=0), lambda e: ex[e],
+                        W_gate=Wg)["out"]
+    W1c = np.concatenate([ex[E][0], ex[E + 1][0]], axis=1)
+    W3c = np.concatenate([ex[E][1], ex[E + 1][1]], axis=1)
+    W2c = np.concatenate([ex[E][2], ex[E + 1][2]], axis=0)
+    assert np.allclose(with_s - without, _torch_ffn(x, W1c, W3c, W2c),
+                       rtol=1e-12, atol=1e-12)
+
+
+def pin_drop_semantics(O):
+    # Everything routed to expert 0 with one slot: token 0 keeps both of its
+    # choices only if they fit.  With k=1 and C=1, tokens 1.. output zero.
+    r = _rng(10)
+    T, d, F, E = 5, 8, 8, 2
+    x = r.standard_normal((T, d))
+    ex = _experts(E, d, F, 100)
+    bias = np.array([50.0, 0.0])
+    res = O.forward(x, _shape(O, T, d, F, E, 1, cf=0.4), lambda e: ex[e],
+                    W_gate=np.zeros((d, E)), bias=bias)
+    assert res["capacity"] == 1
+    assert np.allclose(res["out"][0], _torch_ffn(x[:1], *ex[0])[0],
+                       rtol=1e-12, atol=1e-12)
+    assert np.all(res["out"][1:] == 0.0)
+    # k = 2, three experts: every token's first choice is expert 0 and its
+    # second alternates between experts 1 and 2.  C = 3: tokens 3 and 4 lose
+    # expert 0 and keep only their second expert, with the un-renormalised
+    # gate.
+    E = 3
+    ex = _experts(E, d, F, 101)
+    L = np.array([[2.0, 1.0, -1.0] if t % 2 == 0 else [2.0, -1.0, 1.0]
+                  for t in range(T)])
+    res = O.forward(x, _shape(O, T, d, F, E, 2, cf=0.9), lambda e: ex[e],
+                    logits=L)
+    assert res["capacity"] == 3
+    g0 = 1.0 / (1.0 + math.exp(-1.0))
+    assert np.allclose(res["w"][:, 0], g0, rtol=0, atol=1e-15)
+    assert np.allclose(res["w"][:, 1], 1 - g0, rtol=0, atol=1e-15)
+    y = [_torch_ffn(x, *ex[e]) for e in range(E)]
+    for t in range(T):
+        second = 1 if t % 2 == 0 else 2
+        ref = (g0 * y[0][t] if t < 3 else 0.0) + (1 - g0) * y[second][t]
+        assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+    assert res["stats"]["dropped"] == 2
+    assert list(res["dispatch"]["counts"]) == [5, 3, 2]
+
+
+# ---------------------------------------------------------------- stats
+def pin_stats_closed_forms(O):
+    E, k, T = 8, 2, 64
+    counts = np.full(E, T * k // E)
+    p = np.full((T, E), 1.0 / E)
+    st = O.routing_stats(counts, counts, p, T, k, E)
+    assert abs(st["aux_loss"] - 1.0) < 1e-15
+    assert abs(st["entropy_load"] - math.log(E)) < 1e-15
+    assert abs(st["entropy_token"] - math.log(E)) < 1e-15
+    assert st["overflow_rate"] == 0.0
+    # hand example: k=1, T=4, counts [3, 1], two distinct token distributions
+    p = np.array([[0.9, 0.1], [0.6, 0.4], [0.7, 0.3], [0.2, 0.8]])
+    st = O.routing_stats(np.array([3, 1]), np.array([2, 1]), p, 4, 1, 2)
+    P0, P1 = p.mean(0)
+    assert abs(st["aux_loss"] - 2 * (0.75 * P0 + 0.25 * P1)) < 1e-15
+    assert abs(st["aux_loss_kept"] - 2 * (0.5 * P0 + 0.25 * P1)) < 1e-15
+    assert abs(st["overflow_rate"] - 0.25) < 1e-15
+    assert abs(st["entropy_load"] - scipy.stats.entropy([0.75, 0.25])) < 1e-15
+    ht = np.mean([scipy.stats.entropy(row) for row in p])
+    assert abs(st["entropy_token"] - ht) < 1e-15
+    # one-hot load: zero entropy (0 ln 0 = 0)
+    st = O.routing_stats(np.array([4, 0, 0]), np.array([4, 0, 0]),
+                         np.full((4, 3), 1 / 3), 4, 1, 3)
+    assert st["entropy_load"] == 0.0
+
+
+def pin_stats_skew_direction(O):
+    # Concentrating both load and probability on one expert raises aux above
+    # the balanced value of 1 and up to E in the limit.
+    E, T, k = 4, 100, 1
+    p = np.zeros((T, E))
+    p[:, 0] = 1.0
+    st = O.routing_stats(np.array([T, 0, 0, 0]), np.array([T, 0, 0, 0]), p,
+                         T, k, E)
+    assert abs(st["aux_loss"] - E) < 1e-12
+
+
+def pin_active_fraction(O):
+    # Without drops each token is processed by exactly k of E experts, so the
+    # active share of expert parameters per token is k/E (1/4 for top-2 of 8).
+    g = golden("active_fraction.json")
+    E, k = g["experts"], g["top_k"]
+    r = _rng(11)
+    T = 200
+    sel, _ = O.topk_select(r.standard_normal((T, E)), k)
+    D = O.dispatch(sel, E, O.capacity(T, k, E, 0.0))
+    per_token = np.zeros(T, dtype=int)
+    for a in D["perm"]:
+        per_token[a // k] += 1
+    assert np.all(per_token == k)
+    assert per_token.mean() / E == g["active_fraction"]
+
+
+def pin_decode_single_token(O):
+    # One token with top-2 hits exactly two experts; with DeepSeek routing
+    # it hits six routed experts.
+    r = _rng(12)
+    for E, k in [(8, 2), (160, 6)]:
+        sel, _ = O.topk_select(r.standard_normal((1, E)), k)
+        D = O.dispatch(sel, E, O.capacity(1, k, E, 0.0))
+        assert int((D["counts"] > 0).sum()) == k
+    g = golden("deepseek_routing.json")
+    assert g["top_k"] == 6 and g["shared_experts"] == 2
+
+
+def pin_empty_call(O):
+    res = O.forward(np.zeros((0, 8)), _shape(O, 0, 8, 8, 4, 2),
+                    lambda e: _experts(1, 8, 8, 1)[0],
+                    W_gate=np.zeros((8, 4)))
+    assert res["out"].shape == (0, 8)
+    assert res["capacity"] == 0
+    assert res["stats"]["aux_loss"] == 0.0
+    assert list(res["dispatch"]["counts"]) == [0, 0, 0, 0]
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

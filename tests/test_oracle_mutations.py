@@ -1,0 +1,179 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that at least
+one pin catches each.  This is evidence that the pins constrain every step of
+the oracle, not only that the oracle agrees with itself."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.oracle as O
+import pins
+
+_orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _drop_earliest(sel, E, C):
+    # keeps the LATEST C assignments per expert instead of the earliest
+    T, k = sel.shape
+    rev = sel.reshape(-1)[::-1].reshape(T, k)
+    D = _orig["dispatch"](rev, E, C)
+    n = T * k
+    slot = D["slot"][::-1].copy()
+    perm = np.array([n - 1 - a for a in D["perm"]], dtype=np.int64)
+    D.update(slot=slot, perm=perm)
+    return D
+
+
+def _silu_on_w3(X, W1, W3, W2):
+    return _orig["expert_ffn"](X, W3, W1, W2)
+
+
+def _w2_transposed(X, W1, W3, W2):
+    X = np.asarray(X, dtype=np.float64)
+    h = O.silu(X @ np.asarray(W1, np.float64)) * (X @ np.asarray(W3, np.float64))
+    W2 = np.asarray(W2, np.float64)
+    return h @ (W2.T if W2.shape[0] == W2.shape[1] else W2)
+
+
+def _router_transposed(x, W_gate, bias=None):
+    W = np.asarray(W_gate, np.float64)
+    return _orig["router_logits"](x, W.T if W.shape[0] == W.shape[1] else W, bias)
+
+
+def _router_bias_sign(x, W_gate, bias=None):
+    return _orig["router_logits"](x, W_gate, None if bias is None else -np.asarray(bias))
+
+
+def _topk_high_index(logits, k):
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    sel = np.empty((T, k), dtype=np.int64)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        order = sorted(range(E), key=lambda i: (-logits[t, i], -i))
+        sel[t] = order[:k]
+    return sel, margin
+
+
+def _topk_signed_zero_order(logits, k):
+    # sorts with -0.0 below +0.0 (the sortable-integer trick)
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    sel = np.empty((T, k), dtype=np.int64)
+    margin = np.full(T, np.inf)
+    for t in range(T):
+        key = lambda i: (-(logits[t, i] + (0.0 if math.copysign(1, logits[t, i]) > 0 else -1e-300)), i)  # noqa
+        order = sorted(range(E), key=key)
+        sel[t] = order[:k]
+        top = [logits[t, i] for i in order[:min(k + 1, E)]]
+        for a, b in zip(top[:-1], top[1:]):
+            margin[t] = min(margin[t], a - b)
+    return sel, margin
+
+
+def _gates_all_softmax(logits, sel, gating, renormalize):
+    return _orig["gate_weights"](logits, sel, O.SOFTMAX_THEN_TOPK, False)
+
+
+def _gates_renormalised_b(logits, sel, gating, renormalize):
+    return _orig["gate_weights"](logits, sel, gating, True)
+
+
+def _capacity_floor(T, k, E, cf):
+    if cf is None or cf <= 0:
+        return int(T)
+    return int(math.floor(Fraction(T * k) * Fraction(repr(float(cf))) / E))
+
+
+def _capacity_binary(T, k, E, cf):
+    if cf is None or cf <= 0:
+        return int(T)
+    return int(math.ceil(T * k * cf / E))
+
+
+def _capacity_no_k(T, k, E, cf):
+    return _orig["capacity"](T, 1, E, cf)
+
+
+def _stats_no_E(counts, kept, p, T, k, E):
+    st = _orig["routing_stats"](counts, kept, p, T, k, E)
+    if T:
+        st["aux_loss"] /= E
+    return st
+
+
+def _stats_post_drop_f(counts, kept, p, T, k, E):
+    return _orig["routing_stats"](kept, kept, p, T, k, E)
+
+
+def _stats_entropy_sign(counts, kept, p, T, k, E):
+    st = _orig["routing_stats"](counts, kept, p, T, k, E)
+    st["entropy_token"] = -st["entropy_token"]
+    return st
+
+
+def _softmax_no_shift_bug(logits):
+    # forgets to normalise
+    z = np.asarray(logits, np.float64)
+    return np.exp(z - z.max(axis=1, keepdims=True))
+
+
+def _forward_no_shared(x, shape, expert_weights, **kw):
+    from dataclasses import replace
+    return _orig["forward"](x, replace(shape, S=0), expert_weights, **kw)
+
+
+def _forward_renorm_after_drop(x, shape, expert_weights, **kw):
+    res = _orig["forward"](x, shape, expert_weights, **kw)
+    # rescale each token's routed part by 1 / (sum of kept gates)
+    k = shape.k
+    slot = res["dispatch"]["slot"].reshape(-1, k)
+    kept_w = np.where(slot >= 0, res["w"], 0.0).sum(1)
+    if shape.S == 0:
+        scale = np.where(kept_w > 0, 1.0 / np.where(kept_w > 0, kept_w, 1), 1)
+        res["out"] = res["out"] * scale[:, None]
+    return res
+
+
+def _ffn_relu(X, W1, W3, W2):
+    X = np.asarray(X, dtype=np.float64)
+    u = X @ np.asarray(W1, np.float64)
+    h = np.maximum(u, 0) * (X @ np.asarray(W3, np.float64))
+    return h @ np.asarray(W2, np.float64)
+
+
+MUTATIONS = {
+    "dispatch_drops_earliest": ("dispatch", _drop_earliest),
+    "silu_on_w3_branch": ("expert_ffn", _silu_on_w3),
+    "w2_transposed": ("expert_ffn", _w2_transposed),
+    "ffn_relu": ("expert_ffn", _ffn_relu),
+    "router_transposed": ("router_logits", _router_transposed),
+    "router_bias_sign": ("router_logits", _router_bias_sign),
+    "topk_ties_to_high_index": ("topk_select", _topk_high_index),
+    "topk_signed_zero_ordered": ("topk_select", _topk_signed_zero_order),
+    "mixtral_gates_over_all": ("gate_weights", _gates_all_softmax),
+    "deepseek_gates_renormalised": ("gate_weights", _gates_renormalised_b),
+    "capacity_floor": ("capacity", _capacity_floor),
+    "capacity_binary_double": ("capacity", _capacity_binary),
+    "capacity_without_k": ("capacity", _capacity_no_k),
+    "aux_without_E": ("routing_stats", _stats_no_E),
+    "aux_post_drop_fraction": ("routing_stats", _stats_post_drop_f),
+    "entropy_sign": ("routing_stats", _stats_entropy_sign),
+    "softmax_unnormalised": ("softmax_all", _softmax_no_shift_bug),
+    "shared_experts_skipped": ("forward", _forward_no_shared),
+    "renormalise_after_drop": ("forward", _forward_renorm_after_drop),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(O)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutation {name}"
