@@ -1,0 +1,202 @@
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one full layer forward (router, top-k gating, capacity dispatch,
+expert SwiGLU FFNs, shared experts, gate-weighted combine) over one batch of
+seeded synthetic input already resident in HBM.  The default workload is the
+Mixtral-shaped 2048-token prefill layer (d 4096, d_ff 14336, 8 experts, top-2,
+capacity factor 1.25).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def algorithmic_work(w, kept: int, hit_experts: int):
+    """Flops and bytes the layer must do (no padding, no dropped rows, no
+    unhit experts, no intermediates)."""
+    es = 4 if w.dtype == "f32" else 2
+    ffn_flops_per_row = 2 * 3 * w.d * w.F
+    flops = (ffn_flops_per_row * kept + ffn_flops_per_row * w.S * w.T
+             + 2 * w.T * w.d * w.E)
+    weight_bytes = es * 3 * w.d * w.F * (hit_experts + w.S)
+    io_bytes = es * (2 * w.T * w.d + w.d * w.E)
+    gemm1_flops = 2 * w.d * 2 * w.F * kept
+    gemm1_bytes = es * 2 * w.d * w.F * hit_experts
+    return dict(flops=flops, bytes=weight_bytes + io_bytes, gemm1_flops=gemm1_flops,
+                gemm1_bytes=gemm1_bytes)
+
+
+def cpu_baseline(w, inp, n_tokens: int):
+    """Time the fp64 oracle on the host: routing and dispatch of all T tokens,
+    expert outputs for a seeded sample of n_tokens tokens."""
+    import numpy as np
+    import torch
+
+    import oracle.oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    hx = inp.x.cpu()
+    hWg = inp.W_gate.cpu()
+    W1, W3, W2 = inp.W1.cpu(), inp.W3.cpu(), inp.W2.cpu()
+    bias = None if inp.bias is None else inp.bias.cpu().double().numpy()
+
+    def w64(t):
+        return t.to(torch.float64).numpy()
+
+    rng = np.random.default_rng(0)
+    toks = sorted(rng.choice(w.T, size=min(n_tokens, w.T), replace=False).tolist())
+    shape = O.LayerShape(T=w.T, d=w.d, F=w.F, E=w.E, k=w.k, S=w.S, gating=w.gating,
+                         renormalize=w.renormalize, capacity_factor=w.capacity_factor)
+    t0 = time.perf_counter()
+    O.forward(w64(hx), shape, lambda e: (w64(W1[e]), w64(W3[e]), w64(W2[e])),
+              W_gate=w64(hWg), bias=bias, tokens=toks)
+    dt = time.perf_counter() - t0
+    return dict(value=len(toks) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=(f"{w.name}: routing, capacity dispatch and statistics of all {w.T} "
+                        f"tokens plus expert and shared-expert outputs of {len(toks)} "
+                        f"seeded sampled tokens, fp64 NumPy on the host; value = "
+                        f"{len(toks)} tokens / {dt:.2f} s wall"),
+                seconds=dt)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import sparse_mixture_experts_capacity_amd as moe
+    from workloads import PRESETS, make_inputs
+
+    w = PRESETS[args.workload]
+    dev = "cuda"
+    torch.cuda.init()
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    path = {"auto": moe.PATH_AUTO, "grouped": moe.PATH_GROUPED, "stream": moe.PATH_STREAM}[args.path]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        cfg = moe.make_config(T=w.T, d_model=w.d, d_ff=w.F, n_experts=w.E, top_k=w.k,
+                              n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
+                              capacity_factor=w.capacity_factor, dtype=w.dtype,
+                              ffn_path=path, logit_bias=inp.bias, stream=stream)
+        ws = moe.Workspace(moe.moe_workspace_size(cfg))
+        ws.bind(cfg)
+        out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+
+        def step(stats=False):
+            return moe.moe_forward(inp.x, inp.W_gate, inp.W1, inp.W3, inp.W2, cfg, out,
+                                   stats=stats)
+
+        st = step(stats=True)   # routing statistics of this batch (not timed)
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        moe.moe_timing_reset()
+        moe.moe_timing_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        stream.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        moe.moe_timing_enable(False)
+        kern = moe.moe_timing_read()
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    kept = int(sum(st["kept"]))
+    hit = int(sum(1 for c in st["kept"] if c > 0))
+    work = algorithmic_work(w, kept, hit)
+    per_kernel = {name: dict(launches=n, avg_ms=tot / max(n, 1) if n else 0.0)
+                  for name, (n, tot) in kern.items()}
+    decode = w.T <= 64
+    if decode:
+        dom = "ffn1_swiglu_stream" if "ffn1_swiglu_stream" in per_kernel else "ffn1_swiglu"
+    else:
+        dom = "ffn1_swiglu" if w.dtype == "bf16" else "ffn1_swiglu_f32"
+    dom_ms = per_kernel.get(dom, {}).get("avg_ms", float("nan"))
+    if decode:
+        achieved = work["gemm1_bytes"] / (dom_ms * 1e-3) / 1e9
+        roof = dict(kernel=dom, bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS,
+                    unit="GB/s", frac=achieved / PEAK_HBM_GBS, traffic=None,
+                    per_launch=f"{work['gemm1_bytes']} bytes (W1+W3 of {hit} hit experts)")
+    else:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = work["gemm1_flops"] / (dom_ms * 1e-3) / 1e12
+        roof = dict(kernel=dom, bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
+                    frac=achieved / peak, traffic=None,
+                    per_launch=f"{work['gemm1_flops']} flops (2*d*2F per kept row, {kept} rows)")
+    layer_tflops = work["flops"] / (ms * 1e-3) / 1e12
+    layer_gbs = work["bytes"] / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": w.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian inputs and weights of the workload's shapes)",
+        "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F,
+                   "n_experts": w.E, "top_k": w.k, "n_shared": w.S,
+                   "capacity_factor": w.capacity_factor,
+                   "gating": "softmax_then_topk" if w.gating else "topk_then_softmax",
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer": {"active_tflops": layer_tflops,
+                  "active_frac_of_bf16_peak": layer_tflops / PEAK_BF16_TFLOPS,
+                  "algorithmic_gbs": layer_gbs,
+                  "frac_of_hbm_peak": layer_gbs / PEAK_HBM_GBS,
+                  "kept_assignments": kept, "experts_hit": hit,
+                  "capacity": st["capacity"], "dropped": st["dropped"],
+                  "aux_loss": st["aux_loss"], "overflow_rate": st["overflow_rate"],
+                  "entropy_load": st["entropy_load"], "entropy_token": st["entropy_token"],
+                  "counts": [int(c) for c in st["counts"]]},
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or (64 if w.T > 64 else w.T)
+        cb = cpu_baseline(w, inp, n)
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * moe.h -- C ABI of libmoe: the forward pass of a sparse mixture-of-experts
+ * feed-forward layer with a per-expert capacity limit, on one AMD Instinct
+ * MI355X (gfx950) GPU with every expert resident in HBM.
+ *
+ * Pages this interface follows (titles; sections named, not numbered lines):
+ *   [Mixtral explainer] "Mixtral 8x7B and MoE explained" (allinfo.ai.kr)
+ *   [MoE wiki]          "Mixture of experts" (wikiprompt.org)
+ *   [Routing guide]     "MoE routing, fully explained: Mixtral/DeepSeek
+ *                        structure, load balancing, capacity factor"
+ *                        (allinfo.ai.kr)
+ *
+ * The layer, per token x (a row of d values):
+ *   1. router scores   l = x . W_gate (+ bias)         [Mixtral explainer]
+ *      "Plain explanation" para 3; [Routing guide] "Plain explanation" para 2
+ *   2. top-k experts by score (ties: lower index; -0 == +0), gates either
+ *      softmax over the k chosen scores (Mixtral) or the full softmax over all
+ *      E experts read at the chosen ones (DeepSeek), optionally renormalised
+ *      [Mixtral explainer] para 3; [Routing guide] paras 2 and 4
+ *   3. dispatch with capacity C = ceil(T*k*cf/E) slots per expert; excess
+ *      assignments, latest first in flat order a = t*k + j, are dropped
+ *      [Routing guide] "Plain explanation" paras 3 and 5
+ *   4. expert FFN, SwiGLU: y = (silu(x W1[e]) * (x W3[e])) W2[e]
+ *      [Mixtral explainer] "Plain explanation" para 2
+ *   5. out = sum over kept j of w[t,j] * y[t,j]  +  sum of S shared experts
+ *      (gate 1); dropped choices contribute nothing and the surviving gates
+ *      are not renormalised   [MoE wiki] "How it works"; [Routing guide]
+ *      "Plain explanation" para 4
+ *   6. statistics: aux = E * sum_i f_i P_i with f_i = count_i/(T k) before
+ *      drops and P_i the mean full softmax; overflow rate; entropy of the
+ *      load and mean per-token router entropy (nats)
+ *      [Routing guide] "Plain explanation" para 4, "Key insights" item 3
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     allocates nothing on any call.  Scratch memory is the caller's
+ *     workspace (cfg->workspace, at least moe_workspace_size(cfg) bytes,
+ *     256-byte aligned).  One workspace must not be used by two calls that
+ *     may overlap in time.
+ *   - All layouts are dense row-major with no padding:
+ *       x [T, d]; W_gate [d, E]; W1, W3 [E+S, d, F]; W2 [E+S, F, d];
+ *       out [T, d]; logits [T, E] fp32; bias [E] fp32.
+ *     The S shared experts follow the E routed experts in W1/W3/W2.
+ *   - x, W_gate, W1, W3, W2 and out share cfg->dtype (fp32 or bf16); router
+ *     logits, bias and gate weights are fp32; indices int32.
+ *   - Work is enqueued on cfg->stream (a hipStream_t; NULL = the null
+ *     stream) and returns before it finishes, unless a host-side result is
+ *     requested (stats != NULL, moe_aux_loss), in which case the call waits
+ *     for the stream.
+ *   - Return value: MOE_OK (0) or a negative moe_status_t.  Arguments are
+ *     checked completely before anything is enqueued.  The reason for the
+ *     last failure on the calling thread is in moe_last_error().
+ *   - T = 0 is a valid, empty call: nothing is launched and stats are zero.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, size, k > E, ... */
+  MOE_EUNSUPPORTED = -2,  /* valid layer the library does not build */
+  MOE_EWORKSPACE = -3,    /* workspace missing, too small or misaligned */
+  MOE_EHIP = -4           /* a HIP runtime call failed */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_TOPK_THEN_SOFTMAX = 0,  /* Mixtral: softmax over the k chosen logits */
+  MOE_SOFTMAX_THEN_TOPK = 1   /* DeepSeek: softmax over all E, read top-k */
+} moe_gating_t;
+
+typedef enum {
+  MOE_PATH_AUTO = 0,     /* grouped GEMM when T > 64 (bf16), else streaming */
+  MOE_PATH_GROUPED = 1,  /* MFMA grouped GEMM, weight tiles shared via L2 */
+  MOE_PATH_STREAM = 2    /* weight-streaming kernels for few rows/expert */
+} moe_ffn_path_t;
+
+typedef struct {
+  int64_t T;             /* tokens in this call, >= 0 */
+  int32_t d_model;       /* d */
+  int32_t d_ff;          /* F, hidden width of one expert */
+  int32_t n_experts;     /* E routed experts, 1..256 */
+  int32_t top_k;         /* k, 1..E */
+  int32_t n_shared;      /* S always-on shared experts, >= 0 */
+  int32_t gating;        /* moe_gating_t */
+  int32_t renormalize;   /* DeepSeek gating: divide kept gates by their sum */
+  double capacity_factor;/* <= 0: no limit (C = T) */
+  int32_t dtype;         /* moe_dtype_t */
+  int32_t ffn_path;      /* moe_ffn_path_t */
+  const float* logit_bias; /* device [E] fp32 added to the router scores, or NULL */
+  void* workspace;       /* device scratch, see moe_workspace_size */
+  size_t workspace_bytes;
+  void* stream;          /* hipStream_t */
+} moe_config_t;
+
+typedef struct {
+  int64_t capacity;      /* C */
+  int64_t assignments;   /* T * k */
+  int64_t dropped;       /* assignments beyond capacity */
+  int64_t* counts;       /* host [E] per-expert assignments before drops, or NULL */
+  int64_t* kept;         /* host [E] per-expert assignments kept, or NULL */
+  double aux_loss;       /* E * sum f_i P_i, f_i = counts_i / (T k) */
+  double aux_loss_kept;  /* same with kept counts */
+  double overflow_rate;  /* dropped / (T k) */
+  double entropy_load;   /* -sum f_i ln f_i */
+  double entropy_token;  /* mean over tokens of -sum_i p_ti ln p_ti */
+} moe_stats_t;
+
+/* Validate cfg without touching the GPU.  Bounds: T >= 0, T*k < 2^31,
+ * d, F > 0; bf16 additionally needs d % 64 == 0 and F % 64 == 0
+ * (MOE_EUNSUPPORTED otherwise); 1 <= E <= 256; 1 <= k <= E; S >= 0; the
+ * enums in range.  The workspace is not checked here. */
+int moe_check_config(const moe_config_t* cfg);
+
+/* Bytes of workspace moe_forward / moe_route / moe_route_logits need for
+ * cfg (workspace fields ignored).  0 when cfg is invalid. */
+size_t moe_workspace_size(const moe_config_t* cfg);
+
+/* Capacity C for cfg: ceil(T*k*cf/E) with cf read as the shortest decimal
+ * that round-trips the double (1.1 means 11/10), or T without a limit.
+ * [Routing guide] "Plain explanation" para 5.  -1 when cfg is invalid. */
+int64_t moe_capacity(const moe_config_t* cfg);
+
+/* Full layer forward, steps 1-5 (and 6 when stats != NULL).
+ *   x [T, d], W_gate [d, E], W1/W3 [E+S, d, F], W2 [E+S, F, d]: inputs,
+ *   out [T, d]: output, fully overwritten.  stats: host struct or NULL. */
+int moe_forward(const void* x, const void* W_gate, const void* W1,
+                const void* W3, const void* W2, const moe_config_t* cfg,
+                void* out, moe_stats_t* stats);
+
+/* Steps 1-3 (and 6 when stats != NULL): router scores, top-k, gates and
+ * dispatch, without the experts.  Outputs (device, caller-owned):
+ *   logits   [T, E] fp32  scores seen by top-k (bias included)
+ *   topk_idx [T, k] int32 chosen experts, best first
+ *   topk_w   [T, k] fp32  gate weights
+ *   counts   [E]    int32 assignments per expert before drops
+ *   offsets  [E+1]  int32 exclusive prefix sum of kept counts
+ *   perm     [T*k]  int32 perm[s] = assignment a = t*k + j held in slot s;
+ *                          entries at and after offsets[E] are -1
+ *   slot     [T*k]  int32 slot of assignment a, or -1 when dropped
+ * Any output pointer except topk_idx may be NULL to skip it. */
+int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg,
+              float* logits, int32_t* topk_idx, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* perm,
+              int32_t* slot, moe_stats_t* stats);
+
+/* Steps 2-3 (and 6) from caller-supplied router scores logits [T, E] fp32
+ * (device), which must already include any bias: cfg->logit_bias must be
+ * NULL (MOE_EINVAL otherwise).  Outputs as for moe_route. */
+int moe_route_logits(const float* logits, const moe_config_t* cfg,
+                     int32_t* topk_idx, float* topk_w, int32_t* counts,
+                     int32_t* offsets, int32_t* perm, int32_t* slot,
+                     moe_stats_t* stats);
+
+/* Step 6's auxiliary load-balancing value alone, E * sum_i f_i P_i, from
+ * router scores logits [T, E] fp32 and pre-drop counts [E] int32 (both
+ * device).  Uses cfg's T, E, k, stream and workspace; waits for the stream
+ * and writes the value to *aux_out (host).  [Routing guide] "Plain
+ * explanation" para 4. */
+int moe_aux_loss(const float* logits, const int32_t* counts,
+                 const moe_config_t* cfg, double* aux_out);
+
+/* Reason for the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Per-kernel timing for measurement.  While enabled, every kernel the
+ * library launches is bracketed by HIP events on cfg->stream.
+ * moe_timing_read waits for those events and returns, for each kernel name,
+ * the number of launches and the summed duration in milliseconds since the
+ * last reset; names is filled with up to max entries of NUL-terminated
+ * names (each at most 63 chars) in a caller buffer of max*64 bytes.
+ * Returns the number of distinct kernels (may exceed max). */
+int moe_timing_enable(int enable);
+int moe_timing_reset(void);
+int moe_timing_read(char* names, int64_t* launches, double* total_ms,
+                    int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

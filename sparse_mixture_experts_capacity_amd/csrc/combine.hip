@@ -1,0 +1,98 @@
+// Gate-weighted combine for libmoe (gfx950).
+//
+// out[t] = sum over j with slot[t,j] >= 0 of w[t,j] * Y[slot[t,j]]
+//          + (shared-expert sum for token t)
+// [MoE wiki] "Mixture of experts" (wikiprompt.org), "How it works": the chosen
+// experts' outputs are combined, weighted by the router's confidence;
+// [Routing guide] "MoE routing, fully explained" (allinfo.ai.kr), "Plain
+// explanation" para 4: shared experts see every token; para 3: a dropped
+// assignment is simply not computed, so it adds nothing (the surviving gates
+// are not rescaled).
+//
+// Y may be split into `ysplit` partial sums over K (weight-streaming path);
+// the partials are added in a fixed order, so results are bitwise
+// reproducible.  One workgroup per token, columns strided over threads so
+// each Y row is read with coalesced 16-byte loads.
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ Y, int ysplit, int64_t ysplit_stride,
+    const int32_t* __restrict__ slot, const float* __restrict__ topk_w,
+    const float* __restrict__ Ys, int ys_split, int64_t ys_stride, int64_t T,
+    int k, int d, void* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  const int tid = threadIdx.x;
+  const bool vec = (d & 3) == 0;
+  const int ncols = vec ? d / 4 : d;
+  for (int c = tid; c < ncols; c += blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int s = slot[t * k + j];
+      if (s < 0) continue;
+      const float w = topk_w[t * k + j];
+      float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < ysplit; ++p) {
+        const float* row = Y + p * ysplit_stride + static_cast<int64_t>(s) * d;
+        if (vec) {
+          const float4 v = reinterpret_cast<const float4*>(row)[c];
+          y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
+        } else {
+          y.x += row[c];
+        }
+      }
+      acc.x = fmaf(w, y.x, acc.x);
+      acc.y = fmaf(w, y.y, acc.y);
+      acc.z = fmaf(w, y.z, acc.z);
+      acc.w = fmaf(w, y.w, acc.w);
+    }
+    if (Ys) {
+      for (int p = 0; p < ys_split; ++p) {
+        const float* row = Ys + p * ys_stride + t * d;
+        if (vec) {
+          const float4 v = reinterpret_cast<const float4*>(row)[c];
+          acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        } else {
+          acc.x += row[c];
+        }
+      }
+    }
+    if (BF16OUT) {
+      uint16_t* o = static_cast<uint16_t*>(out) + t * d;
+      if (vec) {
+        const uint32_t lo = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+        const uint32_t hi = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+        reinterpret_cast<uint2*>(o)[c] = make_uint2(lo, hi);
+      } else {
+        o[c] = f32_to_bf16(acc.x);
+      }
+    } else {
+      float* o = static_cast<float*>(out) + t * d;
+      if (vec) reinterpret_cast<float4*>(o)[c] = acc;
+      else o[c] = acc.x;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
+                          const int32_t* slot, const float* topk_w,
+                          const float* Ys, int ys_split, int64_t ys_stride,
+                          int64_t T, int k, int d, void* out, bool bf16,
+                          hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (bf16)
+    combine_kernel<true><<<T, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+                                           ys_split, ys_stride, T, k, d, out);
+  else
+    combine_kernel<false><<<T, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+                                            ys_split, ys_stride, T, k, d, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,68 @@
+// Launchers of the libmoe HIP kernels, called by the host layer
+// (moe_api.cpp).  Internal; the public interface is include/moe.h.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ---- routing.hip ----------------------------------------------------------
+hipError_t launch_router(const void* x, const void* Wg, const float* bias,
+                         float* logits, int64_t T, int d, int E, bool bf16,
+                         hipStream_t s);
+int topk_group_size(int E);
+hipError_t launch_topk_gate(const float* logits, int64_t T, int E, int k,
+                            int gating, int renorm, int32_t* topk_idx,
+                            float* topk_w, float* Ppart, float* Hpart,
+                            int nblocks, int tokens_per_block, hipStream_t s);
+hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
+                           int32_t* lrank, int32_t* blkcnt, int32_t* counts,
+                           int32_t* kcount, int32_t* offsets, int32_t* slot,
+                           int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
+                           int bm2, Tile* tiles2, int32_t* ntiles2,
+                           hipStream_t s);
+hipError_t launch_stats(const float* Ppart, const float* Hpart, int nblk,
+                        const int32_t* counts, const int32_t* kcount, int64_t T,
+                        int k, int E, double* out, hipStream_t s);
+
+// ---- grouped expert GEMMs (ffn_grouped.hip) --------------------------------
+// One launch covers every M-tile of every group.  Rows of a tile are either
+// gathered (A row = perm[row] / topk: token rows of routed assignments) or
+// taken as is (slot rows, or token rows for shared experts).
+struct GroupedGemm {
+  const void* A;            // bf16 or fp32 rows
+  int64_t lda;
+  const int32_t* perm;      // non-null: gather A rows through perm / topk
+  int topk;
+  const void* B;            // W1 (SwiGLU) or W2 base
+  const void* B3;           // W3 base (SwiGLU only)
+  int64_t b_stride;         // elements between consecutive experts
+  int group_base;           // expert index of group 0
+  int ldb;                  // row stride of B (its N)
+  int K;                    // contraction length
+  int N;                    // output columns per group
+  int ngroups_n;            // groups laid side by side along N (shared GEMM1)
+  void* C;                  // output rows
+  int64_t ldc;
+  int64_t c_group_col;      // output column offset per N-group
+  const Tile* tiles;        // device tile list, or null for static tiling
+  const int32_t* ntiles;
+  int static_rows;          // rows when tiles == null
+  int max_mtiles;           // upper bound of M-tiles
+};
+constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels
+constexpr int kF32BM = 64;        // M-tile of the fp32 kernels
+hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s);
+hipError_t launch_grouped_plain_f32(const GroupedGemm& g, hipStream_t s);
+
+// ---- combine.hip -------------------------------------------------------------
+// out[t] = sum_j [slot >= 0] w[t,j] * sum_p Y[p][slot] + sum_p Ys[p][t]
+hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
+                          const int32_t* slot, const float* topk_w,
+                          const float* Ys, int ys_split, int64_t ys_stride,
+                          int64_t T, int k, int d, void* out, bool bf16,
+                          hipStream_t s);
+
+}  // namespace moe

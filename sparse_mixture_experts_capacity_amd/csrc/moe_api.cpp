@@ -1,0 +1,634 @@
+// Host layer of libmoe: argument checks, the capacity rule, workspace
+// carving, path choice and the launch sequence of every entry point declared
+// in include/moe.h.  No memory is allocated here; scratch comes from the
+// caller's workspace.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+// ----------------------------------------------------------------- timing
+struct TimedLaunch {
+  std::string name;
+  hipEvent_t start, stop;
+};
+struct TimingState {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> free_events;
+  std::vector<std::string> names;
+  std::vector<int64_t> launches;
+  std::vector<double> total_ms;
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+hipEvent_t take_event(TimingState& t) {
+  if (!t.free_events.empty()) {
+    hipEvent_t e = t.free_events.back();
+    t.free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when timing is enabled.
+class Timed {
+ public:
+  Timed(const char* name, hipStream_t s) : name_(name), s_(s) {
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.enabled) return;
+    start_ = take_event(t);
+    stop_ = take_event(t);
+    if (start_ && stop_) hipEventRecord(start_, s_);
+  }
+  ~Timed() {
+    if (!start_ || !stop_) return;
+    hipEventRecord(stop_, s_);
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.pending.push_back(TimedLaunch{name_, start_, stop_});
+  }
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+// ----------------------------------------------------------------- plan
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct Plan {
+  int64_t T = 0;
+  int d = 0, F = 0, E = 0, k = 0, S = 0;
+  int gating = 0, renorm = 0;
+  bool bf16 = false;
+  int path = MOE_PATH_GROUPED;   // resolved
+  int64_t capacity = 0;          // exact C
+  int Ceff = 0;                  // min(C, T): the value that can bind
+  int64_t TK = 0;
+  int64_t rows_max = 0;          // most kept rows possible
+  int nblk_dispatch = 0;
+  int topk_blocks = 0, topk_tpb = 0;
+  int bm = 0;                    // M-tile of the grouped kernels
+  int max_mtiles = 0;
+  // workspace regions
+  Region logits, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
+      tiles, ntiles, ppart, hpart, stats, H, Hs, Y, Ys;
+  size_t total = 0;
+};
+
+// Shortest decimal that round-trips the double, as digits D and exponent X:
+// cf = D * 10^X.  Returns false for non-finite input.
+bool decimal_of(double cf, __int128* D, int* X) {
+  if (!isfinite(cf)) return false;
+  char buf[64];
+  for (int prec = 0; prec <= 17; ++prec) {
+    snprintf(buf, sizeof(buf), "%.*e", prec, cf);
+    if (strtod(buf, nullptr) == cf) break;
+  }
+  // buf = "d.ddddde[+-]XX"
+  __int128 digits = 0;
+  int ndec = 0;
+  bool after_point = false;
+  const char* p = buf;
+  for (; *p && *p != 'e'; ++p) {
+    if (*p == '.') { after_point = true; continue; }
+    if (*p >= '0' && *p <= '9') {
+      digits = digits * 10 + (*p - '0');
+      if (after_point) ++ndec;
+    }
+  }
+  int ex = (*p == 'e') ? atoi(p + 1) : 0;
+  *D = digits;
+  *X = ex - ndec;
+  return true;
+}
+
+// Capacity C = ceil(T*k*cf/E), exactly, with cf its shortest decimal.
+// [Routing guide] "MoE routing, fully explained" (allinfo.ai.kr), "Plain
+// explanation" para 5: batch x top-k x capacity factor / experts.
+int64_t exact_capacity(int64_t T, int k, int E, double cf) {
+  if (!(cf > 0.0)) return T;  // no limit
+  __int128 D;
+  int X;
+  if (!decimal_of(cf, &D, &X)) return -1;
+  __int128 num = static_cast<__int128>(T) * k * D;
+  __int128 den = E;
+  for (; X > 0; --X) num *= 10;
+  for (; X < 0; ++X) den *= 10;
+  __int128 q = (num + den - 1) / den;
+  return static_cast<int64_t>(q);
+}
+
+int check(const moe_config_t* c) {
+  if (!c) return fail(MOE_EINVAL, "cfg is NULL");
+  if (c->T < 0) return fail(MOE_EINVAL, "T = %lld must be >= 0", (long long)c->T);
+  if (c->d_model <= 0 || c->d_ff <= 0)
+    return fail(MOE_EINVAL, "d_model = %d and d_ff = %d must be positive", c->d_model, c->d_ff);
+  if (c->n_experts < 1 || c->n_experts > moe::kMaxExperts)
+    return fail(MOE_EINVAL, "n_experts = %d must be in [1, %d]", c->n_experts, moe::kMaxExperts);
+  if (c->top_k < 1 || c->top_k > c->n_experts)
+    return fail(MOE_EINVAL, "top_k = %d must be in [1, n_experts = %d]", c->top_k, c->n_experts);
+  if (c->n_shared < 0) return fail(MOE_EINVAL, "n_shared = %d must be >= 0", c->n_shared);
+  if (c->gating != MOE_TOPK_THEN_SOFTMAX && c->gating != MOE_SOFTMAX_THEN_TOPK)
+    return fail(MOE_EINVAL, "gating = %d is not a moe_gating_t", c->gating);
+  if (c->renormalize != 0 && c->renormalize != 1)
+    return fail(MOE_EINVAL, "renormalize = %d must be 0 or 1", c->renormalize);
+  if (c->dtype != MOE_DTYPE_F32 && c->dtype != MOE_DTYPE_BF16)
+    return fail(MOE_EINVAL, "dtype = %d is not a moe_dtype_t", c->dtype);
+  if (c->ffn_path < MOE_PATH_AUTO || c->ffn_path > MOE_PATH_STREAM)
+    return fail(MOE_EINVAL, "ffn_path = %d is not a moe_ffn_path_t", c->ffn_path);
+  if (isnan(c->capacity_factor) || c->capacity_factor > 1e6)
+    return fail(MOE_EINVAL, "capacity_factor must be a number <= 1e6");
+  if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
+    return fail(MOE_EINVAL, "T * top_k must be < 2^31");
+  if (static_cast<int64_t>(c->n_experts + c->n_shared) * c->d_model * c->d_ff >= (int64_t(1) << 40))
+    return fail(MOE_EINVAL, "expert weights too large");
+  if (c->dtype == MOE_DTYPE_BF16) {
+    if (c->d_model % 64 != 0 || c->d_ff % 64 != 0)
+      return fail(MOE_EUNSUPPORTED, "bf16 layers need d_model and d_ff divisible by 64 (got %d, %d)",
+                  c->d_model, c->d_ff);
+    if (c->ffn_path == MOE_PATH_STREAM)
+      return fail(MOE_EUNSUPPORTED, "the weight-streaming path is not built in this library");
+  } else {
+    if (c->ffn_path == MOE_PATH_STREAM)
+      return fail(MOE_EUNSUPPORTED, "fp32 layers run on the fp32 grouped kernels only");
+  }
+  return MOE_OK;
+}
+
+void add(Region& r, size_t bytes, size_t& cursor) {
+  r.off = cursor;
+  r.bytes = bytes;
+  cursor = align_up(cursor + bytes);
+}
+
+int make_plan(const moe_config_t* c, Plan* p) {
+  int rc = check(c);
+  if (rc != MOE_OK) return rc;
+  p->T = c->T;
+  p->d = c->d_model;
+  p->F = c->d_ff;
+  p->E = c->n_experts;
+  p->k = c->top_k;
+  p->S = c->n_shared;
+  p->gating = c->gating;
+  p->renorm = c->renormalize;
+  p->bf16 = c->dtype == MOE_DTYPE_BF16;
+  p->path = MOE_PATH_GROUPED;
+  p->capacity = exact_capacity(c->T, c->top_k, c->n_experts, c->capacity_factor);
+  if (p->capacity < 0) return fail(MOE_EINVAL, "capacity_factor is not finite");
+  p->Ceff = static_cast<int>(p->capacity < p->T ? p->capacity : p->T);
+  p->TK = p->T * p->k;
+  p->rows_max = p->TK;
+  if (static_cast<int64_t>(p->E) * p->Ceff < p->rows_max) p->rows_max = static_cast<int64_t>(p->E) * p->Ceff;
+  p->nblk_dispatch = static_cast<int>((p->TK + moe::kDispatchChunk - 1) / moe::kDispatchChunk);
+  const int G = moe::topk_group_size(p->E);
+  const int groups = 256 / G;
+  int64_t tpb = (p->T + 1023) / 1024;
+  tpb = (tpb + groups - 1) / groups * groups;
+  if (tpb < groups) tpb = groups;
+  p->topk_tpb = static_cast<int>(tpb);
+  p->topk_blocks = static_cast<int>((p->T + tpb - 1) / tpb);
+  p->bm = p->bf16 ? moe::kGroupedBM : moe::kF32BM;
+  p->max_mtiles = static_cast<int>(p->rows_max / p->bm + p->E);
+
+  const size_t es = p->bf16 ? 2 : 4;
+  size_t cur = 0;
+  add(p->logits, sizeof(float) * p->T * p->E, cur);
+  add(p->idx, sizeof(int32_t) * p->TK, cur);
+  add(p->w, sizeof(float) * p->TK, cur);
+  add(p->lrank, sizeof(int32_t) * p->TK, cur);
+  add(p->blkcnt, sizeof(int32_t) * static_cast<size_t>(p->nblk_dispatch) * p->E, cur);
+  add(p->counts, sizeof(int32_t) * p->E, cur);
+  add(p->kcount, sizeof(int32_t) * p->E, cur);
+  add(p->offsets, sizeof(int32_t) * (p->E + 1), cur);
+  add(p->slot, sizeof(int32_t) * p->TK, cur);
+  add(p->perm, sizeof(int32_t) * p->TK, cur);
+  add(p->tiles, sizeof(moe::Tile) * (p->max_mtiles + 1), cur);
+  add(p->ntiles, sizeof(int32_t) * 4, cur);
+  add(p->ppart, sizeof(float) * static_cast<size_t>(p->topk_blocks) * p->E, cur);
+  add(p->hpart, sizeof(float) * p->topk_blocks, cur);
+  add(p->stats, sizeof(double) * 8, cur);
+  add(p->H, es * p->rows_max * p->F, cur);
+  add(p->Hs, es * p->T * p->S * p->F, cur);
+  add(p->Y, sizeof(float) * p->rows_max * p->d, cur);
+  add(p->Ys, sizeof(float) * (p->S > 0 ? p->T : 0) * p->d, cur);
+  p->total = cur;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, const Region& r) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + r.off);
+}
+
+int check_workspace(const moe_config_t* c, const Plan& p) {
+  if (p.T == 0) return MOE_OK;
+  if (!c->workspace) return fail(MOE_EWORKSPACE, "workspace is NULL (need %zu bytes)", p.total);
+  if (reinterpret_cast<uintptr_t>(c->workspace) % kAlign != 0)
+    return fail(MOE_EWORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+  if (c->workspace_bytes < p.total)
+    return fail(MOE_EWORKSPACE, "workspace has %zu bytes, need %zu", c->workspace_bytes, p.total);
+  return MOE_OK;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (expr);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return fail(MOE_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+// Steps 2-3 (top-k, gates, dispatch) from logits already in `logits`.
+int run_route(const Plan& p, void* ws, const float* logits, int32_t* idx, float* w,
+              hipStream_t s) {
+  {
+    Timed t("topk_gate", s);
+    HIP_TRY(moe::launch_topk_gate(logits, p.T, p.E, p.k, p.gating, p.renorm, idx, w,
+                                  at<float>(ws, p.ppart), at<float>(ws, p.hpart),
+                                  p.topk_blocks, p.topk_tpb, s));
+  }
+  {
+    Timed t("dispatch", s);
+    HIP_TRY(moe::launch_dispatch(idx, p.TK, p.E, p.Ceff, at<int32_t>(ws, p.lrank),
+                                 at<int32_t>(ws, p.blkcnt), at<int32_t>(ws, p.counts),
+                                 at<int32_t>(ws, p.kcount), at<int32_t>(ws, p.offsets),
+                                 at<int32_t>(ws, p.slot), at<int32_t>(ws, p.perm), p.bm,
+                                 at<moe::Tile>(ws, p.tiles), at<int32_t>(ws, p.ntiles), 0,
+                                 nullptr, nullptr, s));
+  }
+  return MOE_OK;
+}
+
+int fill_stats(const Plan& p, void* ws, hipStream_t s, moe_stats_t* st,
+               const int32_t* counts_dev, const int32_t* kcount_dev) {
+  memset(&st->aux_loss, 0, sizeof(double) * 5);
+  st->capacity = p.capacity;
+  st->assignments = p.TK;
+  st->dropped = 0;
+  if (p.T == 0) {
+    if (st->counts) memset(st->counts, 0, sizeof(int64_t) * p.E);
+    if (st->kept) memset(st->kept, 0, sizeof(int64_t) * p.E);
+    return MOE_OK;
+  }
+  {
+    Timed t("stats", s);
+    HIP_TRY(moe::launch_stats(at<float>(ws, p.ppart), at<float>(ws, p.hpart), p.topk_blocks,
+                              counts_dev, kcount_dev, p.T, p.k, p.E, at<double>(ws, p.stats), s));
+  }
+  double out[8];
+  std::vector<int32_t> cnt(p.E), kc(p.E);
+  HIP_TRY(hipMemcpyAsync(out, at<double>(ws, p.stats), sizeof(double) * 6, hipMemcpyDeviceToHost, s));
+  if (counts_dev)
+    HIP_TRY(hipMemcpyAsync(cnt.data(), counts_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
+  if (kcount_dev)
+    HIP_TRY(hipMemcpyAsync(kc.data(), kcount_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  st->aux_loss = out[0];
+  st->aux_loss_kept = out[1];
+  st->overflow_rate = out[2];
+  st->entropy_load = out[3];
+  st->entropy_token = out[4];
+  st->dropped = static_cast<int64_t>(out[5]);
+  for (int e = 0; e < p.E; ++e) {
+    if (st->counts) st->counts[e] = cnt[e];
+    if (st->kept) st->kept[e] = kc[e];
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_check_config(const moe_config_t* cfg) {
+  int rc = check(cfg);
+  if (rc == MOE_OK) g_err.clear();
+  return rc;
+}
+
+size_t moe_workspace_size(const moe_config_t* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK) return 0;
+  return p.total;
+}
+
+int64_t moe_capacity(const moe_config_t* cfg) {
+  Plan p;
+  if (make_plan(cfg, &p) != MOE_OK) return -1;
+  return p.capacity;
+}
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W3,
+                const void* W2, const moe_config_t* cfg, void* out, moe_stats_t* stats) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.T > 0 && (!x || !W_gate || !W1 || !W3 || !W2 || !out))
+    return fail(MOE_EINVAL, "x, W_gate, W1, W3, W2 and out must be non-NULL");
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  if (p.T == 0) {
+    if (stats) fill_stats(p, nullptr, s, stats, nullptr, nullptr);
+    g_err.clear();
+    return MOE_OK;
+  }
+  void* ws = cfg->workspace;
+  float* logits = at<float>(ws, p.logits);
+  int32_t* idx = at<int32_t>(ws, p.idx);
+  float* w = at<float>(ws, p.w);
+  {
+    Timed t("router", s);
+    HIP_TRY(moe::launch_router(x, W_gate, cfg->logit_bias, logits, p.T, p.d, p.E, p.bf16, s));
+  }
+  rc = run_route(p, ws, logits, idx, w, s);
+  if (rc != MOE_OK) return rc;
+
+  const size_t es = p.bf16 ? 2 : 4;
+  const int64_t dF = static_cast<int64_t>(p.d) * p.F;
+  // GEMM1 (routed): H[slot] = silu(x[token] W1[e]) * (x[token] W3[e])
+  moe::GroupedGemm g1{};
+  g1.A = x; g1.lda = p.d; g1.perm = at<int32_t>(ws, p.perm); g1.topk = p.k;
+  g1.B = W1; g1.B3 = W3; g1.b_stride = dF; g1.group_base = 0; g1.ldb = p.F;
+  g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
+  g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
+  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles;
+  // GEMM2 (routed): Y[slot] = H[slot] W2[e]
+  moe::GroupedGemm g2 = g1;
+  g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
+  g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
+  // Shared experts: all T token rows; GEMM1 lays the S experts side by side
+  // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
+  // the S stacked W2 blocks in one pass (their sum).
+  moe::GroupedGemm s1{}, s2{};
+  if (p.S > 0) {
+    s1 = g1;
+    s1.perm = nullptr; s1.group_base = p.E; s1.ngroups_n = p.S; s1.C = at<void>(ws, p.Hs);
+    s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
+    s1.ntiles = nullptr; s1.static_rows = static_cast<int>(p.T);
+    s1.max_mtiles = static_cast<int>((p.T + p.bm - 1) / p.bm);
+    s2 = s1;
+    s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
+    s2.b_stride = dF; s2.group_base = p.E; s2.ngroups_n = 1; s2.ldb = p.d;
+    s2.K = p.S * p.F; s2.N = p.d; s2.C = at<void>(ws, p.Ys); s2.ldc = p.d; s2.c_group_col = 0;
+  }
+  (void)es;
+  if (p.bf16) {
+    {
+      Timed t("ffn1_swiglu", s);
+      HIP_TRY(moe::launch_grouped_swiglu_bf16(g1, s));
+    }
+    if (p.S > 0) {
+      Timed t("ffn1_swiglu_shared", s);
+      HIP_TRY(moe::launch_grouped_swiglu_bf16(s1, s));
+    }
+    {
+      Timed t("ffn2", s);
+      HIP_TRY(moe::launch_grouped_plain_bf16(g2, s));
+    }
+    if (p.S > 0) {
+      Timed t("ffn2_shared", s);
+      HIP_TRY(moe::launch_grouped_plain_bf16(s2, s));
+    }
+  } else {
+    {
+      Timed t("ffn1_swiglu_f32", s);
+      HIP_TRY(moe::launch_grouped_swiglu_f32(g1, s));
+    }
+    if (p.S > 0) {
+      Timed t("ffn1_swiglu_f32_shared", s);
+      HIP_TRY(moe::launch_grouped_swiglu_f32(s1, s));
+    }
+    {
+      Timed t("ffn2_f32", s);
+      HIP_TRY(moe::launch_grouped_plain_f32(g2, s));
+    }
+    if (p.S > 0) {
+      Timed t("ffn2_f32_shared", s);
+      HIP_TRY(moe::launch_grouped_plain_f32(s2, s));
+    }
+  }
+  {
+    Timed t("combine", s);
+    HIP_TRY(moe::launch_combine(at<float>(ws, p.Y), 1, 0, at<int32_t>(ws, p.slot), w,
+                                p.S > 0 ? at<float>(ws, p.Ys) : nullptr, 1, 0, p.T, p.k, p.d,
+                                out, p.bf16, s));
+  }
+  if (stats) {
+    rc = fill_stats(p, ws, s, stats, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount));
+    if (rc != MOE_OK) return rc;
+  }
+  g_err.clear();
+  return MOE_OK;
+}
+
+static int route_common(const Plan& p, const moe_config_t* cfg, const float* logits,
+                        int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* slot, moe_stats_t* stats) {
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  void* ws = cfg->workspace;
+  int32_t* idx = topk_idx;
+  float* w = topk_w ? topk_w : at<float>(ws, p.w);
+  int rc = run_route(p, ws, logits, idx, w, s);
+  if (rc != MOE_OK) return rc;
+  if (counts)
+    HIP_TRY(hipMemcpyAsync(counts, at<int32_t>(ws, p.counts), sizeof(int32_t) * p.E,
+                           hipMemcpyDeviceToDevice, s));
+  if (offsets)
+    HIP_TRY(hipMemcpyAsync(offsets, at<int32_t>(ws, p.offsets), sizeof(int32_t) * (p.E + 1),
+                           hipMemcpyDeviceToDevice, s));
+  if (perm)
+    HIP_TRY(hipMemcpyAsync(perm, at<int32_t>(ws, p.perm), sizeof(int32_t) * p.TK,
+                           hipMemcpyDeviceToDevice, s));
+  if (slot)
+    HIP_TRY(hipMemcpyAsync(slot, at<int32_t>(ws, p.slot), sizeof(int32_t) * p.TK,
+                           hipMemcpyDeviceToDevice, s));
+  if (stats) {
+    rc = fill_stats(p, ws, s, stats, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount));
+    if (rc != MOE_OK) return rc;
+  }
+  return MOE_OK;
+}
+
+int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg, float* logits,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+              int32_t* perm, int32_t* slot, moe_stats_t* stats) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.T > 0 && (!x || !W_gate || !topk_idx))
+    return fail(MOE_EINVAL, "x, W_gate and topk_idx must be non-NULL");
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  if (p.T == 0) {
+    if (stats) fill_stats(p, nullptr, s, stats, nullptr, nullptr);
+    g_err.clear();
+    return MOE_OK;
+  }
+  float* lg = logits ? logits : at<float>(cfg->workspace, p.logits);
+  {
+    Timed t("router", s);
+    HIP_TRY(moe::launch_router(x, W_gate, cfg->logit_bias, lg, p.T, p.d, p.E, p.bf16, s));
+  }
+  rc = route_common(p, cfg, lg, topk_idx, topk_w, counts, offsets, perm, slot, stats);
+  if (rc == MOE_OK) g_err.clear();
+  return rc;
+}
+
+int moe_route_logits(const float* logits, const moe_config_t* cfg, int32_t* topk_idx,
+                     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* slot, moe_stats_t* stats) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (cfg->logit_bias)
+    return fail(MOE_EINVAL, "moe_route_logits takes final scores: logit_bias must be NULL");
+  if (p.T > 0 && (!logits || !topk_idx))
+    return fail(MOE_EINVAL, "logits and topk_idx must be non-NULL");
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  if (p.T == 0) {
+    if (stats) fill_stats(p, nullptr, static_cast<hipStream_t>(cfg->stream), stats, nullptr, nullptr);
+    g_err.clear();
+    return MOE_OK;
+  }
+  rc = route_common(p, cfg, logits, topk_idx, topk_w, counts, offsets, perm, slot, stats);
+  if (rc == MOE_OK) g_err.clear();
+  return rc;
+}
+
+int moe_aux_loss(const float* logits, const int32_t* counts, const moe_config_t* cfg,
+                 double* aux_out) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (!aux_out) return fail(MOE_EINVAL, "aux_out must be non-NULL");
+  if (p.T == 0) {
+    *aux_out = 0.0;
+    g_err.clear();
+    return MOE_OK;
+  }
+  if (!logits || !counts) return fail(MOE_EINVAL, "logits and counts must be non-NULL");
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  void* ws = cfg->workspace;
+  {
+    Timed t("softmax_stats", s);
+    HIP_TRY(moe::launch_topk_gate(logits, p.T, p.E, 1, p.gating, p.renorm, nullptr, nullptr,
+                                  at<float>(ws, p.ppart), at<float>(ws, p.hpart), p.topk_blocks,
+                                  p.topk_tpb, s));
+  }
+  {
+    Timed t("stats", s);
+    HIP_TRY(moe::launch_stats(at<float>(ws, p.ppart), at<float>(ws, p.hpart), p.topk_blocks,
+                              counts, nullptr, p.T, p.k, p.E, at<double>(ws, p.stats), s));
+  }
+  double v = 0.0;
+  HIP_TRY(hipMemcpyAsync(&v, at<double>(ws, p.stats), sizeof(double), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  *aux_out = v;
+  g_err.clear();
+  return MOE_OK;
+}
+
+int moe_timing_enable(int enable) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.enabled = enable != 0;
+  return MOE_OK;
+}
+
+int moe_timing_reset(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& l : t.pending) {
+    hipEventSynchronize(l.stop);
+    t.free_events.push_back(l.start);
+    t.free_events.push_back(l.stop);
+  }
+  t.pending.clear();
+  t.names.clear();
+  t.launches.clear();
+  t.total_ms.clear();
+  return MOE_OK;
+}
+
+int moe_timing_read(char* names, int64_t* launches, double* total_ms, int max) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& l : t.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(l.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, l.start, l.stop) == hipSuccess) {
+      size_t i = 0;
+      for (; i < t.names.size(); ++i)
+        if (t.names[i] == l.name) break;
+      if (i == t.names.size()) {
+        t.names.push_back(l.name);
+        t.launches.push_back(0);
+        t.total_ms.push_back(0.0);
+      }
+      t.launches[i] += 1;
+      t.total_ms[i] += ms;
+    }
+    t.free_events.push_back(l.start);
+    t.free_events.push_back(l.stop);
+  }
+  t.pending.clear();
+  const int n = static_cast<int>(t.names.size());
+  for (int i = 0; i < n && i < max; ++i) {
+    if (names) {
+      strncpy(names + 64 * i, t.names[i].c_str(), 63);
+      names[64 * i + 63] = '\0';
+    }
+    if (launches) launches[i] = t.launches[i];
+    if (total_ms) total_ms[i] = t.total_ms[i];
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,469 @@
+// Router scores, top-k gating, capacity-limited dispatch and routing
+// statistics for libmoe (gfx950).
+//
+// Pages: [Mixtral explainer] "Mixtral 8x7B and MoE explained"
+// (allinfo.ai.kr), "Plain explanation" para 3 (router logits, top-2,
+// softmax over the two); [Routing guide] "MoE routing, fully explained"
+// (allinfo.ai.kr), "Plain explanation" paras 2-5 (distribution over all
+// experts, top-k, capacity, dropping the overflow, aux load-balancing
+// product), "Key insights" item 3 (counts, overflow, entropy).
+//
+// Everything here is deterministic: no floating-point atomics, and integer
+// ranks come from wavefront ballots processed in a fixed order.
+#include "kernels.h"
+
+#include <float.h>
+#include <limits.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router scores, few experts (E <= 16): one wavefront per token; each lane
+// walks a strided slice of d and keeps E partial sums, then a fixed butterfly
+// sums across the wavefront.  bf16 x bf16 products are exact in fp32.
+// ---------------------------------------------------------------------------
+template <typename TIn, int EC>
+__global__ __launch_bounds__(256) void router_small_e_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ Wg,
+    const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
+    int d, int E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float acc[EC];
+#pragma unroll
+  for (int e = 0; e < EC; ++e) acc[e] = 0.f;
+  const TIn* xr = x + t * d;
+  for (int c = lane; c < d; c += kWave) {
+    const float xv = load_elem(xr, c);
+    const TIn* wr = Wg + static_cast<int64_t>(c) * E;
+#pragma unroll
+    for (int e = 0; e < EC; ++e)
+      if (e < E) acc[e] = fmaf(xv, load_elem(wr, e), acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EC; ++e) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EC; ++e)
+      if (e < E) logits[t * E + e] = acc[e] + (bias ? bias[e] : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router scores, many experts: a workgroup owns 16 tokens; thread e owns
+// expert e (and e+256 ...); token rows are staged in LDS 256 columns at a
+// time and W_gate rows are read coalesced across experts.
+// ---------------------------------------------------------------------------
+constexpr int kRouterTB = 16;
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_large_e_kernel(
+    const TIn* __restrict__ x, const TIn* __restrict__ Wg,
+    const float* __restrict__ bias, float* __restrict__ logits, int64_t T,
+    int d, int E) {
+  __shared__ float xs[kRouterTB][256];
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouterTB;
+  const int e = tid;
+  float acc[kRouterTB];
+#pragma unroll
+  for (int i = 0; i < kRouterTB; ++i) acc[i] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += 256) {
+    const int cn = min(256, d - c0);
+    for (int i = 0; i < kRouterTB; ++i) {
+      const int64_t t = t0 + i;
+      xs[i][tid] = (t < T && tid < cn) ? load_elem(x + t * d, c0 + tid) : 0.f;
+    }
+    __syncthreads();
+    if (e < E) {
+      for (int cc = 0; cc < cn; ++cc) {
+        const float w = load_elem(Wg, static_cast<int64_t>(c0 + cc) * E + e);
+#pragma unroll
+        for (int i = 0; i < kRouterTB; ++i) acc[i] = fmaf(xs[i][cc], w, acc[i]);
+      }
+    }
+    __syncthreads();
+  }
+  if (e < E) {
+    const float b = bias ? bias[e] : 0.f;
+    for (int i = 0; i < kRouterTB; ++i) {
+      const int64_t t = t0 + i;
+      if (t < T) logits[t * E + e] = acc[i] + b;
+    }
+  }
+}
+
+template <typename TIn>
+hipError_t launch_router_t(const TIn* x, const TIn* Wg, const float* bias,
+                           float* logits, int64_t T, int d, int E,
+                           hipStream_t s) {
+  if (E <= 8) {
+    router_small_e_kernel<TIn, 8><<<(T + 3) / 4, 256, 0, s>>>(x, Wg, bias, logits, T, d, E);
+  } else if (E <= 16) {
+    router_small_e_kernel<TIn, 16><<<(T + 3) / 4, 256, 0, s>>>(x, Wg, bias, logits, T, d, E);
+  } else {
+    router_large_e_kernel<TIn><<<(T + kRouterTB - 1) / kRouterTB, 256, 0, s>>>(
+        x, Wg, bias, logits, T, d, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const void* x, const void* Wg, const float* bias,
+                         float* logits, int64_t T, int d, int E, bool bf16,
+                         hipStream_t s) {
+  if (bf16)
+    return launch_router_t(static_cast<const uint16_t*>(x),
+                           static_cast<const uint16_t*>(Wg), bias, logits, T,
+                           d, E, s);
+  return launch_router_t(static_cast<const float*>(x),
+                         static_cast<const float*>(Wg), bias, logits, T, d, E,
+                         s);
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + gates + softmax statistics.  A group of G lanes (G a power of two,
+// G >= E/4) handles one token; lane g of the group holds the scores of
+// experts g, g+G, g+2G, g+3G.  k rounds of a group-wide argmax by butterfly
+// exchange pick the experts best first; order is (score descending, index
+// ascending) under IEEE comparison, so -0 and +0 tie and the lower index
+// wins.  Each group also accumulates the full softmax p[t, :] and the
+// per-token entropy for the load-balance statistics; the workgroup then sums
+// its groups in a fixed order into one partial row per workgroup.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
+  return (a > b) || (a == b && ia < ib);
+}
+
+template <int V>
+__global__ __launch_bounds__(256) void topk_gate_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int G,
+    int gating, int renorm, int tokens_per_block,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ Ppart, float* __restrict__ Hpart) {
+  __shared__ float pbuf[256 * 4];   // [groups][E], groups*E <= 256*V <= 1024
+  __shared__ float hbuf[256];
+  const int tid = threadIdx.x;
+  const int gl = tid % G;
+  const int grp = tid / G;
+  const int ngroups = blockDim.x / G;
+  float pacc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) pacc[v] = 0.f;
+  float hacc = 0.f;
+
+  const int64_t tb = static_cast<int64_t>(blockIdx.x) * tokens_per_block;
+  const int64_t te = min(T, tb + tokens_per_block);
+  for (int64_t t = tb + grp; t < te; t += ngroups) {
+    const float* row = logits + t * E;
+    float val[V];
+    bool taken[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i = gl + v * G;
+      val[v] = (i < E) ? row[i] : -FLT_MAX;
+      taken[v] = !(i < E);
+    }
+    float m = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bv = -FLT_MAX;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int i = gl + v * G;
+        if (!taken[v] && better(val[v], i, bv, bi)) { bv = val[v]; bi = i; }
+      }
+      for (int off = G >> 1; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, G);
+        const int oi = __shfl_xor(bi, off, G);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (j == 0) m = bv;
+      if ((bi % G) == gl) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          if (gl + v * G == bi) taken[v] = true;
+      }
+      if (gl == 0 && topk_idx) topk_idx[t * k + j] = bi;
+    }
+    // Full softmax over all E experts, shifted by the top score m.
+    float ex[V];
+    float z = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      ex[v] = (gl + v * G < E) ? expf(val[v] - m) : 0.f;
+      z += ex[v];
+    }
+    for (int off = G >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off, G);
+    const float inv_z = 1.0f / z;
+    float plogp = 0.f;  // sum_i p_i (l_i - m)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float p = ex[v] * inv_z;
+      pacc[v] += p;
+      if (gl + v * G < E) plogp += p * (val[v] - m);
+    }
+    for (int off = G >> 1; off >= 1; off >>= 1) plogp += __shfl_xor(plogp, off, G);
+    if (gl == 0) hacc += logf(z) - plogp;
+
+    // Gate weights, written by lane 0 of the group (reads back the chosen
+    // scores; they are in L1).
+    if (gl == 0 && topk_w) {
+      const int32_t* sel = topk_idx + t * k;
+      if (gating == 0) {
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(row[sel[j]] - m);
+        const float inv = 1.0f / s;
+        for (int j = 0; j < k; ++j) topk_w[t * k + j] = expf(row[sel[j]] - m) * inv;
+      } else {
+        float s = 0.f;
+        if (renorm)
+          for (int j = 0; j < k; ++j) s += expf(row[sel[j]] - m) * inv_z;
+        const float inv = renorm ? 1.0f / s : 1.0f;
+        for (int j = 0; j < k; ++j) topk_w[t * k + j] = (expf(row[sel[j]] - m) * inv_z) * inv;
+      }
+    }
+  }
+  // Workgroup reduction of the softmax statistics in a fixed order.
+  if (Ppart) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i = gl + v * G;
+      if (i < E) pbuf[grp * E + i] = pacc[v];
+    }
+    if (gl == 0) hbuf[grp] = hacc;
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+      float s = 0.f;
+      for (int g = 0; g < ngroups; ++g) s += pbuf[g * E + e];
+      Ppart[static_cast<int64_t>(blockIdx.x) * E + e] = s;
+    }
+    if (tid == 0) {
+      float s = 0.f;
+      for (int g = 0; g < ngroups; ++g) s += hbuf[g];
+      Hpart[blockIdx.x] = s;
+    }
+  }
+}
+
+int topk_group_size(int E) {
+  int G = 1;
+  while (G * 4 < E) G <<= 1;
+  // at least E/4 lanes per token, at most a wavefront
+  while (G < 64 && G < E) G <<= 1;
+  return G > 64 ? 64 : G;
+}
+
+hipError_t launch_topk_gate(const float* logits, int64_t T, int E, int k,
+                            int gating, int renorm, int32_t* topk_idx,
+                            float* topk_w, float* Ppart, float* Hpart,
+                            int nblocks, int tokens_per_block, hipStream_t s) {
+  const int G = topk_group_size(E);
+  const int V = (E + G - 1) / G;
+  if (V <= 1)
+    topk_gate_kernel<1><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
+                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+  else if (V <= 2)
+    topk_gate_kernel<2><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
+                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+  else
+    topk_gate_kernel<4><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
+                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch, pass 1: stable rank of each assignment inside its chunk of
+// kDispatchChunk assignments.  One wavefront walks the chunk 64 assignments
+// at a time; lanes with the same expert are found with 8 ballots (one per
+// bit of the expert id) and ranked by popcount of the lower lanes; LDS
+// counters carry the rank across steps.  Writes the chunk's per-expert
+// totals.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void dispatch_rank_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t TK, int E,
+    int32_t* __restrict__ lrank, int32_t* __restrict__ blkcnt) {
+  __shared__ int cnt[kMaxExperts];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int it = 0; it < kDispatchChunk / kWave; ++it) {
+    const int64_t a = base + it * kWave + lane;
+    const bool valid = a < TK;
+    const int e = valid ? topk_idx[a] : 0;
+    uint64_t match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const int before = valid ? cnt[e] : 0;
+    __syncthreads();
+    const bool leader = valid && (__ffsll(static_cast<unsigned long long>(match)) - 1 == lane);
+    if (leader) cnt[e] = before + __popcll(match);
+    __syncthreads();
+    if (valid) lrank[a] = before + __popcll(match & lt);
+  }
+  for (int e = lane; e < E; e += kWave)
+    blkcnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch, pass 2 (one workgroup): per expert, turn chunk totals into
+// exclusive chunk bases (in place) and the total count; apply the capacity;
+// prefix-sum the kept counts into slot offsets; build the M-tile list of the
+// grouped expert GEMMs (tiles of at most `bm` rows, expert by expert).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(
+    int32_t* __restrict__ blkcnt, int nblk, int E, int C,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kcount,
+    int32_t* __restrict__ offsets, int bm, Tile* __restrict__ tiles,
+    int32_t* __restrict__ ntiles, int bm2, Tile* __restrict__ tiles2,
+    int32_t* __restrict__ ntiles2) {
+  __shared__ int kc[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int toff[kMaxExperts + 1];
+  __shared__ int toff2[kMaxExperts + 1];
+  const int e = threadIdx.x;
+  if (e < E) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int64_t i = static_cast<int64_t>(b) * E + e;
+      const int c = blkcnt[i];
+      blkcnt[i] = run;
+      run += c;
+    }
+    counts[e] = run;
+    kc[e] = min(run, C);
+    kcount[e] = kc[e];
+  }
+  __syncthreads();
+  if (e == 0) {
+    int s = 0, ts = 0, ts2 = 0;
+    for (int i = 0; i < E; ++i) {
+      off[i] = s;
+      toff[i] = ts;
+      toff2[i] = ts2;
+      s += kc[i];
+      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+      if (bm2 > 0) ts2 += (kc[i] + bm2 - 1) / bm2;
+    }
+    off[E] = s;
+    toff[E] = ts;
+    toff2[E] = ts2;
+    if (ntiles) *ntiles = ts;
+    if (ntiles2) *ntiles2 = ts2;
+  }
+  __syncthreads();
+  for (int i = e; i <= E; i += blockDim.x) offsets[i] = off[i];
+  if (e < E) {
+    if (tiles && bm > 0) {
+      int n = 0;
+      for (int r = 0; r < kc[e]; r += bm, ++n)
+        tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
+    }
+    if (tiles2 && bm2 > 0) {
+      int n = 0;
+      for (int r = 0; r < kc[e]; r += bm2, ++n)
+        tiles2[toff2[e] + n] = Tile{e, off[e] + r, min(bm2, kc[e] - r), 0};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch, pass 3: final rank = chunk base + rank in chunk; kept iff
+// rank < C; slot = offsets[e] + rank; perm[slot] = a.  Unused perm entries
+// (from offsets[E] on) are set to -1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ blkbase, const int32_t* __restrict__ offsets,
+    int64_t TK, int E, int C, int32_t* __restrict__ slot,
+    int32_t* __restrict__ perm) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (a >= TK) return;
+  const int e = topk_idx[a];
+  const int64_t chunk = a / kDispatchChunk;
+  const int rank = blkbase[chunk * E + e] + lrank[a];
+  const int total = offsets[E];
+  if (a >= total) perm[a] = -1;
+  if (rank < C) {
+    const int s = offsets[e] + rank;
+    slot[a] = s;
+    perm[s] = static_cast<int32_t>(a);
+  } else {
+    slot[a] = -1;
+  }
+}
+
+hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
+                           int32_t* lrank, int32_t* blkcnt, int32_t* counts,
+                           int32_t* kcount, int32_t* offsets, int32_t* slot,
+                           int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
+                           int bm2, Tile* tiles2, int32_t* ntiles2,
+                           hipStream_t s) {
+  const int nblk = static_cast<int>((TK + kDispatchChunk - 1) / kDispatchChunk);
+  dispatch_rank_kernel<<<nblk, 64, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
+  dispatch_scan_kernel<<<1, 256, 0, s>>>(blkcnt, nblk, E, C, counts, kcount,
+                                         offsets, bm, tiles, ntiles, bm2, tiles2,
+                                         ntiles2);
+  dispatch_scatter_kernel<<<(TK + 255) / 256, 256, 0, s>>>(
+      topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Statistics (one workgroup): sums the softmax partial rows in a fixed
+// order and forms, in double precision,
+//   f_i = counts_i / (T k), P_i = mean_t p[t, i], aux = E sum f_i P_i,
+//   aux over kept counts, overflow = dropped / (T k),
+//   H_load = -sum f_i ln f_i, H_tok = mean_t H_t.
+// out[0..5] = aux, aux_kept, overflow, H_load, H_tok, dropped.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stats_kernel(
+    const float* __restrict__ Ppart, const float* __restrict__ Hpart, int nblk,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ kcount,
+    int64_t T, int k, int E, double* __restrict__ out) {
+  __shared__ double P[kMaxExperts];
+  const int e = threadIdx.x;
+  if (e < E) {
+    double s = 0.0;
+    for (int b = 0; b < nblk; ++b) s += static_cast<double>(Ppart[static_cast<int64_t>(b) * E + e]);
+    P[e] = s / static_cast<double>(T);
+  }
+  __syncthreads();
+  if (e == 0) {
+    const double n = static_cast<double>(T) * k;
+    double aux = 0.0, auxk = 0.0, hl = 0.0, ht = 0.0;
+    int64_t dropped = 0;
+    for (int i = 0; i < E; ++i) {
+      const double f = counts ? counts[i] / n : 0.0;
+      const double fk = kcount ? kcount[i] / n : 0.0;
+      aux += f * P[i];
+      auxk += fk * P[i];
+      if (f > 0.0) hl -= f * log(f);
+      if (counts && kcount) dropped += counts[i] - kcount[i];
+    }
+    for (int b = 0; b < nblk; ++b) ht += static_cast<double>(Hpart[b]);
+    out[0] = E * aux;
+    out[1] = E * auxk;
+    out[2] = static_cast<double>(dropped) / n;
+    out[3] = hl;
+    out[4] = ht / static_cast<double>(T);
+    out[5] = static_cast<double>(dropped);
+  }
+}
+
+hipError_t launch_stats(const float* Ppart, const float* Hpart, int nblk,
+                        const int32_t* counts, const int32_t* kcount, int64_t T,
+                        int k, int E, double* out, hipStream_t s) {
+  stats_kernel<<<1, 256, 0, s>>>(Ppart, Hpart, nblk, counts, kcount, T, k, E, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

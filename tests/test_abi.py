@@ -1,0 +1,101 @@
+"""Host-side checks of libmoe: the library loads without a GPU, exports every
+entry point include/moe.h declares, validates configs and computes the
+capacity exactly as the oracle does.  No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle.oracle as O
+import sparse_mixture_experts_capacity_amd as moe
+from sparse_mixture_experts_capacity_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe.h")
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    names = declared_symbols()
+    for must in ("moe_forward", "moe_route", "moe_route_logits", "moe_aux_loss",
+                 "moe_workspace_size", "moe_check_config", "moe_last_error",
+                 "moe_capacity"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert set(declared_symbols()) == set(_lib.EXPORTED_SYMBOLS)
+
+
+def cfg(**kw):
+    base = dict(T=128, d_model=128, d_ff=256, n_experts=8, top_k=2,
+                dtype="bf16", capacity_factor=1.25)
+    base.update(kw)
+    return moe.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), moe.MOE_OK),
+    (dict(T=0), moe.MOE_OK),
+    (dict(T=-1), moe.MOE_EINVAL),
+    (dict(top_k=0), moe.MOE_EINVAL),
+    (dict(top_k=9), moe.MOE_EINVAL),
+    (dict(n_experts=0), moe.MOE_EINVAL),
+    (dict(n_experts=257, top_k=2), moe.MOE_EINVAL),
+    (dict(n_experts=256, top_k=256), moe.MOE_OK),
+    (dict(d_model=0), moe.MOE_EINVAL),
+    (dict(d_ff=-64), moe.MOE_EINVAL),
+    (dict(n_shared=-1), moe.MOE_EINVAL),
+    (dict(gating=2), moe.MOE_EINVAL),
+    (dict(dtype=7), moe.MOE_EINVAL),
+    (dict(ffn_path=3), moe.MOE_EINVAL),
+    (dict(capacity_factor=float("nan")), moe.MOE_EINVAL),
+    (dict(capacity_factor=2e6), moe.MOE_EINVAL),
+    (dict(T=2 ** 30, top_k=2), moe.MOE_EINVAL),
+    (dict(d_model=96), moe.MOE_EUNSUPPORTED),
+    (dict(d_ff=100), moe.MOE_EUNSUPPORTED),
+    (dict(dtype="f32", d_model=5, d_ff=7), moe.MOE_OK),
+    (dict(dtype="f32", ffn_path=moe.PATH_STREAM), moe.MOE_EUNSUPPORTED),
+])
+def test_check_config(kw, code):
+    c = cfg(**kw)
+    if "dtype" in kw and kw["dtype"] == 7:
+        c.dtype = 7
+    rc = moe.moe_check_config(c)
+    assert rc == code, moe.moe_last_error()
+    if code != moe.MOE_OK:
+        assert moe.moe_last_error()
+        assert moe.moe_workspace_size(c) == 0
+        assert moe.moe_capacity(c) == -1
+
+
+def test_null_config():
+    assert moe.LIB.moe_check_config(None) == moe.MOE_EINVAL
+    assert "NULL" in moe.moe_last_error()
+
+
+@pytest.mark.parametrize("T,k,E,cf", [
+    (2048, 2, 8, 1.25), (16384, 2, 8, 1.0), (16384, 2, 8, 1.5), (100, 2, 2, 1.1),
+    (10, 1, 4, 1.0), (1, 1, 8, 1.0), (7, 3, 5, 0.3), (4096, 6, 160, 0.0),
+    (333, 2, 7, 1.3333), (64, 2, 8, -1.0), (1000, 8, 64, 2.0 / 3.0),
+    (12345, 4, 13, 1e-3), (5, 2, 3, 123456.0), (0, 2, 8, 1.25),
+])
+def test_capacity_matches_oracle(T, k, E, cf):
+    c = cfg(T=T, top_k=k, n_experts=E, capacity_factor=cf)
+    assert moe.moe_capacity(c) == O.capacity(T, k, E, cf)
+
+
+def test_workspace_grows_with_tokens():
+    sizes = [moe.moe_workspace_size(cfg(T=T)) for T in (1, 64, 1024, 8192)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert moe.moe_workspace_size(cfg(T=0)) >= 0

@@ -1,0 +1,297 @@
+"""GPU parity of the HIP library against the fp64 oracle, through the C ABI.
+
+* routing / dispatch / statistics from the same fp32 logits: bit-exact
+  indices, counts, offsets, permutation and slots (moe_route_logits);
+* router GEMM scores against fp64, and selections away from near ties;
+* full layer outputs: max|d| <= 2e-2 * RMS(ref) for bf16 and 1e-5 * RMS(ref)
+  for fp32, at sizes spanning several tiles with ragged tails, and on sampled
+  tokens at the full workload sizes;
+* determinism and the empty call.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.oracle as O
+import sparse_mixture_experts_capacity_amd as moe
+from gpu_helpers import (DEV, Run, comparable_tokens, config_for, near_tie_tokens,
+                         output_within_tolerance, rel_max_err, route_buffers, say,
+                         shape_of, to64, tol_for)
+from workloads import PRESETS, SKEW_BIAS, SOFTMAX_THEN_TOPK, Workload, normal, random_logits
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# routing from the same fp32 logits: bit-exact
+# --------------------------------------------------------------------------
+def _logits_case(name):
+    if name == "tiny":
+        w = PRESETS["tiny_f32"]
+        r = Run(w)  # CPU-generated; logits from the oracle's own router
+        L = torch.tensor(O.router_logits(to64(r.hx), to64(r.hWg)), dtype=torch.float32)
+        return w, L
+    if name == "prefill":
+        w = PRESETS["mixtral_prefill"]
+        return w, random_logits(w.T, w.E, seed=1)
+    if name == "skew_cf1.0":
+        w = PRESETS["skew_cf1.0"]
+        return w, random_logits(w.T, w.E, seed=2) + torch.tensor(SKEW_BIAS)
+    if name == "skew_cf1.5":
+        w = PRESETS["skew_cf1.5"]
+        return w, random_logits(w.T, w.E, seed=3) + torch.tensor(SKEW_BIAS)
+    if name == "deepseek":
+        w = PRESETS["deepseek"]
+        return w, random_logits(w.T, w.E, seed=4)
+    if name == "ties_signed_zero":
+        w = Workload("ties", T=3000, d=64, F=64, E=8, k=2, capacity_factor=1.1)
+        L = torch.round(random_logits(w.T, w.E, seed=5))
+        L[L == 0] = 0.0
+        L[::3, 2] = -0.0
+        L[::5, 5] = 0.0
+        return w, L
+    if name == "all_equal":
+        w = Workload("all_equal", T=1500, d=64, F=64, E=16, k=4, capacity_factor=1.0)
+        L = torch.zeros(w.T, w.E)
+        L[torch.rand(w.T, w.E, generator=torch.Generator().manual_seed(6)) < 0.5] = -0.0
+        return w, L
+    if name == "E256_k8":
+        w = Workload("E256", T=700, d=64, F=64, E=256, k=8, capacity_factor=1.0)
+        return w, random_logits(w.T, w.E, seed=7)
+    if name == "k_equals_E":
+        w = Workload("kE", T=100, d=64, F=64, E=8, k=8)
+        return w, random_logits(w.T, w.E, seed=8)
+    if name == "E1":
+        w = Workload("E1", T=50, d=64, F=64, E=1, k=1, capacity_factor=0.5)
+        return w, random_logits(w.T, w.E, seed=9)
+    if name == "T1":
+        w = Workload("T1", T=1, d=64, F=64, E=8, k=2)
+        return w, random_logits(w.T, w.E, seed=10)
+    if name == "tiny_capacity":
+        w = Workload("tinycap", T=5000, d=64, F=64, E=8, k=2, capacity_factor=0.01)
+        return w, random_logits(w.T, w.E, seed=11) * 3
+    if name == "deepseek_renorm_k1":
+        w = Workload("dsr", T=777, d=64, F=64, E=64, k=1, gating=SOFTMAX_THEN_TOPK,
+                     renormalize=True, capacity_factor=1.25)
+        return w, random_logits(w.T, w.E, seed=12)
+    raise KeyError(name)
+
+
+LOGIT_CASES = ["tiny", "prefill", "skew_cf1.0", "skew_cf1.5", "deepseek",
+               "ties_signed_zero", "all_equal", "E256_k8", "k_equals_E", "E1", "T1",
+               "tiny_capacity", "deepseek_renorm_k1"]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES)
+def test_route_logits_bit_exact(case):
+    say(f"[route_logits] {case}")
+    w, L = _logits_case(case)
+    T, E, k = w.T, w.E, w.k
+    # oracle on the same fp32 values, widened exactly
+    L64 = L.to(torch.float64).numpy()
+    sel, margin = O.topk_select(L64, k)
+    gates = O.gate_weights(L64, sel, w.gating, w.renormalize)
+    C = O.capacity(T, k, E, w.capacity_factor)
+    D = O.dispatch(sel, E, C)
+    st_ref = O.routing_stats(D["counts"], D["kept"], O.softmax_all(L64), T, k, E)
+
+    cfg = config_for(w, stream=None)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    r = route_buffers(T, E, k)
+    Ld = L.to(DEV).contiguous()
+    st = moe.moe_route_logits(Ld, cfg, r["idx"], r["w"], r["counts"], r["offsets"],
+                               r["perm"], r["slot"], stats=True)
+    torch.cuda.synchronize()
+    g = {n: v.cpu().numpy() for n, v in r.items()}
+
+    assert np.array_equal(g["idx"].astype(np.int64), sel), "top-k indices differ"
+    assert np.array_equal(g["counts"].astype(np.int64), D["counts"])
+    assert np.array_equal(g["offsets"].astype(np.int64), D["offsets"])
+    total = int(D["offsets"][-1])
+    assert np.array_equal(g["perm"][:total].astype(np.int64), D["perm"])
+    assert np.all(g["perm"][total:] == -1)
+    assert np.array_equal(g["slot"].astype(np.int64), D["slot"])
+    # gates: fp32 exp vs fp64
+    assert np.max(np.abs(g["w"] - gates)) <= 2e-6 * max(1.0, float(np.max(gates)))
+    # statistics
+    assert st["capacity"] == C and st["dropped"] == D["dropped"]
+    assert np.array_equal(st["counts"], D["counts"])
+    assert np.array_equal(st["kept"], D["kept"])
+    for key in ("aux_loss", "aux_loss_kept", "overflow_rate", "entropy_load",
+                "entropy_token"):
+        ref = st_ref[key]
+        assert abs(st[key] - ref) <= 1e-5 * max(abs(ref), 1e-3), (key, st[key], ref)
+    say(f"  ok: C={C} dropped={D['dropped']} aux={st['aux_loss']:.6f} "
+        f"min margin={float(margin.min()) if T else 0:.3g}")
+
+
+def test_aux_loss_entry_point():
+    say("[aux_loss] skew logits")
+    w, L = _logits_case("skew_cf1.0")
+    L64 = L.to(torch.float64).numpy()
+    sel, _ = O.topk_select(L64, w.k)
+    D = O.dispatch(sel, w.E, O.capacity(w.T, w.k, w.E, w.capacity_factor))
+    ref = O.routing_stats(D["counts"], D["kept"], O.softmax_all(L64), w.T, w.k, w.E)
+    cfg = config_for(w, stream=None)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    counts = torch.tensor(D["counts"], dtype=torch.int32, device=DEV)
+    aux = moe.moe_aux_loss(L.to(DEV), counts, cfg)
+    assert abs(aux - ref["aux_loss"]) <= 1e-5 * ref["aux_loss"]
+    assert aux > 1.2   # skew raises it above the balanced value 1
+
+
+# --------------------------------------------------------------------------
+# router GEMM (moe_route): scores against fp64, selections off near ties
+# --------------------------------------------------------------------------
+ROUTE_CASES = {
+    "tiny_f32": PRESETS["tiny_f32"],
+    "bf16_E8": Workload("bf16_E8", T=700, d=256, F=64, E=8, k=2, capacity_factor=1.25),
+    "bf16_skew": Workload("bf16_skew", T=900, d=512, F=64, E=8, k=2, capacity_factor=1.0,
+                          bias=SKEW_BIAS),
+    "bf16_E160": Workload("bf16_E160", T=300, d=512, F=64, E=160, k=6,
+                          gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    "f32_E40_ragged_d": Workload("f32_E40", T=77, d=100, F=30, E=40, k=3, dtype="f32",
+                                 capacity_factor=1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROUTE_CASES))
+def test_route_router_gemm(case):
+    w = ROUTE_CASES[case]
+    say(f"[route] {case}")
+    run = Run(w)
+    g, st = run.route()
+    ref = run.oracle(tokens=[])
+    Lg = g["logits"].numpy().astype(np.float64)
+    scale = float(np.max(np.abs(ref["logits"])))
+    err = float(np.max(np.abs(Lg - ref["logits"])))
+    assert err <= (1e-5 if w.dtype == "bf16" else 1e-5) * max(1.0, scale) * math.sqrt(w.d / 64)
+    ties, _, thr = near_tie_tokens(Lg, ref)
+    ok = np.ones(w.T, dtype=bool)
+    ok[ties] = False
+    assert np.array_equal(g["idx"].numpy()[ok].astype(np.int64), ref["sel"][ok])
+    if len(ties) == 0:
+        assert np.array_equal(g["counts"].numpy().astype(np.int64), ref["dispatch"]["counts"])
+        assert np.array_equal(g["slot"].numpy().astype(np.int64), ref["dispatch"]["slot"])
+    say(f"  ok: logit err {err:.2e}, near ties {len(ties)} (thr {thr:.1e})")
+
+
+# --------------------------------------------------------------------------
+# full layer, every output element
+# --------------------------------------------------------------------------
+FORWARD_CASES = {
+    "tiny_f32": PRESETS["tiny_f32"],
+    "f32_shared_ragged": Workload("f32_shared", T=150, d=72, F=40, E=6, k=2, S=2,
+                                  dtype="f32", capacity_factor=1.0),
+    "bf16_multi_tile": Workload("bf16_multi", T=1000, d=256, F=512, E=8, k=2,
+                                capacity_factor=1.25),
+    "bf16_skew_drops": Workload("bf16_skew", T=1000, d=256, F=384, E=8, k=2,
+                                capacity_factor=1.0, bias=SKEW_BIAS),
+    "bf16_deepseek_like": Workload("bf16_ds", T=256, d=256, F=128, E=32, k=6, S=2,
+                                   gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    "bf16_ragged_n": Workload("bf16_ragged", T=130, d=192, F=320, E=4, k=2,
+                              capacity_factor=1.5),
+    "bf16_dense_k_eq_E": Workload("bf16_dense", T=64, d=128, F=128, E=4, k=4),
+    "bf16_T1": Workload("bf16_T1", T=1, d=256, F=512, E=8, k=2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FORWARD_CASES))
+def test_forward_small(case):
+    w = FORWARD_CASES[case]
+    say(f"[forward] {case}")
+    run = Run(w)
+    out, st = run.forward()
+    g_route, _ = run.route()
+    ref = run.oracle()
+    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref)
+    ok = comparable_tokens(w, ref, ties, w.T)
+    got = to64(out)
+    err, rms = rel_max_err(got[ok], ref["out"][ok])
+    good, ratio, excess = output_within_tolerance(got[ok], ref["out"][ok], w)
+    say(f"  max|d| = {err:.3e}, RMS(ref) = {rms:.3e}, ratio {ratio:.2e}, "
+        f"excess over bound {excess:.2e}, near ties {len(ties)}")
+    assert np.all(np.isfinite(got))
+    assert good
+    if len(ties) == 0:
+        assert np.array_equal(st["counts"], ref["dispatch"]["counts"])
+        assert st["dropped"] == ref["dispatch"]["dropped"]
+        for key in ("aux_loss", "overflow_rate", "entropy_load", "entropy_token"):
+            r = ref["stats"][key]
+            assert abs(st[key] - r) <= 1e-4 * max(abs(r), 1e-3), key
+
+
+def test_forward_empty():
+    say("[forward] T=0")
+    w = Workload("empty", T=0, d=128, F=128, E=8, k=2, capacity_factor=1.25)
+    cfg = config_for(w, stream=None)
+    out = torch.empty((0, w.d), dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((0, w.d), dtype=torch.bfloat16, device=DEV)
+    Wg = torch.zeros((w.d, w.E), dtype=torch.bfloat16, device=DEV)
+    W = torch.zeros((w.E, w.d, w.F), dtype=torch.bfloat16, device=DEV)
+    st = moe.moe_forward(x, Wg, W, W, W, cfg, out, stats=True)
+    assert st["capacity"] == 0 and st["dropped"] == 0 and st["aux_loss"] == 0.0
+
+
+def test_forward_deterministic():
+    w = FORWARD_CASES["bf16_skew_drops"]
+    say("[determinism] bf16 skew with drops")
+    run = Run(w)
+    a, _ = run.forward(stats=False)
+    b, _ = run.forward(stats=False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# full workload sizes, sampled tokens
+# --------------------------------------------------------------------------
+FULL = ["mixtral_prefill", "mixtral_decode_t1", "mixtral_decode_t8", "mixtral_decode_t64",
+        "skew_cf1.0", "skew_cf1.5", "deepseek"]
+
+
+def _sample(ref, T, n=40, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    pick.update({0, T - 1})
+    slot = ref["dispatch"]["slot"].reshape(T, -1)
+    dropped_tok = np.nonzero((slot < 0).any(1))[0]
+    if len(dropped_tok):
+        pick.update(rng.choice(dropped_tok, size=min(8, len(dropped_tok)), replace=False).tolist())
+        pick.add(int(dropped_tok[0]))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(name):
+    w = PRESETS[name]
+    say(f"[full] {name}")
+    run = Run(w, gen_device=DEV)
+    out, st = run.forward()
+    g_route, _ = run.route()
+    routing = run.oracle(tokens=[])
+    toks = _sample(routing, w.T)
+    ref = run.oracle(tokens=toks)
+    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref)
+    ok = comparable_tokens(w, ref, ties, w.T)
+    sel_ok = [t for t in toks if ok[t]]
+    got = to64(out)[sel_ok]
+    err, rms = rel_max_err(got, ref["out"][sel_ok])
+    good, ratio, excess = output_within_tolerance(got, ref["out"][sel_ok], w)
+    say(f"  {len(sel_ok)} tokens: max|d| = {err:.3e}, RMS = {rms:.3e}, ratio "
+        f"{ratio:.2e}, excess over bound {excess:.2e}; near ties {len(ties)}; dropped "
+        f"{ref['dispatch']['dropped']}; aux {st['aux_loss']:.4f}")
+    assert len(sel_ok) >= min(20, w.T)
+    assert np.all(np.isfinite(to64(out)))
+    assert good
+    if len(ties) == 0:
+        assert np.array_equal(st["counts"], ref["dispatch"]["counts"])
+        assert np.array_equal(st["kept"], ref["dispatch"]["kept"])
+        assert st["dropped"] == ref["dispatch"]["dropped"]
+        for key in ("aux_loss", "aux_loss_kept", "overflow_rate", "entropy_load",
+                    "entropy_token"):
+            r = ref["stats"][key]
+            assert abs(st[key] - r) <= 1e-5 * max(abs(r), 1e-3), (key, st[key], r)
