@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB before the steps "
+                         "(a kernel of known traffic for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -120,6 +123,13 @@ def main():
             return moe.moe_forward(inp.x, inp.W_gate, inp.W1, inp.W3, inp.W2, cfg, out,
                                    stats=stats)
 
+        if args.copy_calibration_mib:
+            n = args.copy_calibration_mib * (1 << 20) // 4
+            src = torch.randn(n, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            stream.synchronize()
+            del src, dst
         st = step(stats=True)   # routing statistics of this batch (not timed)
         for _ in range(args.warmup):
             step()

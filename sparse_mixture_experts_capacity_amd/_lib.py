@@ -6,7 +6,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1

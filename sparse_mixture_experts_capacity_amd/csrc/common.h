@@ -13,6 +13,7 @@ constexpr int kDispatchChunk = 1024;  // assignments ranked by one workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-byte staging
 
 // bf16 <-> fp32.  Widening is exact (the bf16 bits are the top half of the
 // fp32 bits).  Narrowing rounds to nearest, ties to even; NaN stays NaN.

@@ -40,27 +40,52 @@ struct TileCoords {
   bool valid;
 };
 
+// Block -> (expert, N-tile, M-tile).  The logical tile order runs expert by
+// expert, N-tile by N-tile, with the expert's M-tiles fastest, so a window of
+// consecutive logical tiles is a compact (all M-tiles) x (a few N-tiles) block
+// of one expert: its weight tiles and its token rows are each fetched once
+// into L2 and shared.  Hardware deals workgroups to the 8 XCDs round-robin
+// (block p -> XCD p % 8); each XCD takes a contiguous eighth of the logical
+// tiles that actually exist (their count is read from the device tile list),
+// so the XCDs stay balanced whatever the routing.
 template <int TBM>
 __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
-                                                  int nblocks) {
+                                                  int /*nblocks*/) {
   TileCoords tc{0, 0, 0, 0, 0, false};
-  const int L = xcd_local_block(blockIdx.x, nblocks);
-  const int mt = L % p.max_mtiles;
-  const int nt_all = L / p.max_mtiles;
-  if (nt_all >= ntn * p.ngroups_n) return tc;
-  tc.ngroup = nt_all / ntn;
-  tc.ntile = nt_all % ntn;
+  const int ntn_all = ntn * p.ngroups_n;
+  const int mtiles = p.tiles ? *p.ntiles : (p.static_rows + TBM - 1) / TBM;
+  const int total = mtiles * ntn_all;
+  const int per = (total + 7) >> 3;
+  const int x = blockIdx.x & 7;
+  const int i = blockIdx.x >> 3;
+  if (i >= per) return tc;
+  const int L = x * per + i;
+  if (L >= total) return tc;
+  int m, n_all;
   if (p.tiles) {
-    if (mt >= *p.ntiles) return tc;
-    const Tile t = p.tiles[mt];
+    // expert e owns logical tiles [tstart[e] * ntn_all, tstart[e+1] * ntn_all)
+    int lo = 0, hi = p.n_experts;            // find e with tstart[e]*ntn_all <= L
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tstart[mid] * ntn_all <= L) lo = mid; else hi = mid;
+    }
+    const int t0 = p.tstart[lo];
+    const int mt = p.tstart[lo + 1] - t0;
+    const int local = L - t0 * ntn_all;
+    n_all = local / mt;
+    m = t0 + local % mt;
+    const Tile t = p.tiles[m];
     tc.group = t.group;
     tc.row0 = t.row0;
     tc.nrows = t.nrows;
   } else {
-    tc.row0 = mt * TBM;
-    if (tc.row0 >= p.static_rows) return tc;
+    n_all = L / mtiles;
+    m = L % mtiles;
+    tc.row0 = m * TBM;
     tc.nrows = min(TBM, p.static_rows - tc.row0);
   }
+  tc.ngroup = n_all / ntn;
+  tc.ntile = n_all % ntn;
   tc.valid = tc.nrows > 0;
   return tc;
 }
@@ -72,10 +97,14 @@ constexpr int BM = kGroupedBM;  // 128
 constexpr int BN = 256;         // B-tile columns (SwiGLU: 128 W1 + 128 W3)
 constexpr int BK = 64;
 constexpr int LDK = BK + 8;     // padded LDS row (144 bytes, conflict-free)
+#ifndef MOE_GEMM_NBUF
+#define MOE_GEMM_NBUF 2
+#endif
+constexpr int NBUF = MOE_GEMM_NBUF;  // LDS stages: 2 = double buffer, 1 = two workgroups per CU
 
 // 8 (k) x 8 (n) bf16 block transpose: in[r] holds row r (n = 0..7, two per
 // dword), out[c] holds column c (k = 0..7, two per dword).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   const uint32_t* r = reinterpret_cast<const uint32_t*>(in);
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
 #pragma unroll
@@ -90,11 +119,90 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[
   }
 }
 
+// Per-thread staging of one K step: 4 chunks of token rows, one 8 x 8 block
+// of weights.
+struct Stage {
+  u32x4 a[4];
+  u32x4 b[8];
+};
+
+__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* const (&aptr)[4],
+                                           const uint16_t* bptr, int64_t ldb, int k0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    st.b[r] = *reinterpret_cast<const u32x4*>(bptr + static_cast<int64_t>(k0 + r) * ldb);
+}
+
+__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* as, uint16_t* bs,
+                                            int tid) {
+  const int akc = tid & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    *reinterpret_cast<u32x4*>(&as[r * LDK + akc * 8]) = st.a[i];
+  }
+  u32x4 col[8];
+  transpose8x8(st.b, col);
+  const int kb = tid & 7, nb = tid >> 3;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    *reinterpret_cast<u32x4*>(&bs[(nb * 8 + c) * LDK + kb * 8]) = col[c];
+}
+
+// B-tile column of MFMA tile j owned by wavefront column wn.
 template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void grouped_bf16_kernel(GroupedGemm p, int ntn,
+__device__ __forceinline__ int bcol_of(int j, int wn) {
+  if constexpr (SWIGLU) return (j < 4) ? (wn * 64 + j * 16) : (128 + wn * 64 + (j - 4) * 16);
+  return wn * 128 + j * 16;
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* bs, int j, int lane, int wn, int koff) {
+  return *reinterpret_cast<const bf16x8*>(&bs[(bcol_of<SWIGLU>(j, wn) + (lane & 15)) * LDK + koff]);
+}
+
+// One K step (64) of the wavefront's 64 x 128 sub-tile: 2 x (4 x 8) MFMAs.
+// The next B fragment is read from LDS while the current one feeds its four
+// MFMAs.
+template <bool SWIGLU>
+__device__ __forceinline__ void mfma_step(f32x4 (&acc)[4][8], const uint16_t* as,
+                                          const uint16_t* bs, int lane, int wm, int wn) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int koff = s * 32 + (lane >> 4) * 8;
+    bf16x8 af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(&as[(wm * 64 + i * 16 + (lane & 15)) * LDK + koff]);
+    bf16x8 bcur = load_bfrag<SWIGLU>(bs, 0, lane, wn, koff);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8 bnext = bcur;
+      if (j + 1 < 8) bnext = load_bfrag<SWIGLU>(bs, j + 1, lane, wn, koff);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bcur, acc[i][j], 0, 0, 0);
+      bcur = bnext;
+    }
+    // Issue order for the scheduler: the A fragments and two B fragments,
+    // then per B fragment its four MFMAs followed by the next fragment read.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 3 - NBUF) void grouped_bf16_kernel(GroupedGemm p, int ntn,
                                                               int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[NBUF][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[NBUF][BN * LDK];
 
   const TileCoords tc = tile_coords<BM>(p, ntn, nblocks);
   if (!tc.valid) return;
@@ -109,20 +217,22 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_kernel(GroupedGemm p, int
   constexpr int NOUT = SWIGLU ? BN / 2 : BN;   // output columns per tile
   const int n0 = tc.ntile * NOUT;
 
-  // ---- A loader: 4 chunks of 8 bf16 per thread (rows tid/8 + 32 i) --------
+  // Token rows: thread loads 16-byte chunk tid%8 of rows tid/8 + 32 i.  Rows
+  // past the tile's end repeat its first row; their results are not stored.
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
-  const int akc = tid & 7;
   const uint16_t* aptr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (tid >> 3) + 32 * i;
     const int rr = tc.row0 + (r < tc.nrows ? r : 0);
     const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
-    aptr[i] = A + src * p.lda + akc * 8;
+    aptr[i] = A + src * p.lda + (tid & 7) * 8;
   }
-  // ---- B loader: one 8 x 8 block per thread --------------------------------
-  const int kb = tid & 7;    // k rows kb*8 .. kb*8+7
-  const int nb = tid >> 3;   // B-tile columns nb*8 .. nb*8+7
+  // Weights: one 8 (k) x 8 (n) block per thread.  A column block past N
+  // reads column 0 instead; those accumulators feed output columns >= N,
+  // which are never stored.
+  const int kb = tid & 7;
+  const int nb = tid >> 3;
   const uint16_t* bsrc;
   int bcol;
   if constexpr (SWIGLU) {
@@ -132,34 +242,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_kernel(GroupedGemm p, int
     bsrc = static_cast<const uint16_t*>(p.B);
     bcol = n0 + nb * 8;
   }
-  const bool bvalid = bcol < p.N;
-  const uint16_t* bptr = bsrc + boff + static_cast<int64_t>(kb * 8) * p.ldb + (bvalid ? bcol : 0);
-
-  uint4 ra[4];
-  uint4 rb[8];
-  auto load_regs = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const uint4*>(aptr[i] + k0);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (bvalid)
-        rb[r] = *reinterpret_cast<const uint4*>(bptr + static_cast<int64_t>(k0 + r) * p.ldb);
-      else
-        rb[r] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(&As[buf][r * LDK + akc * 8]) = ra[i];
-    }
-    uint4 col[8];
-    transpose8x8(rb, col);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *reinterpret_cast<uint4*>(&Bs[buf][(nb * 8 + c) * LDK + kb * 8]) = col[c];
-  };
+  const uint16_t* bptr = bsrc + boff + static_cast<int64_t>(kb * 8) * p.ldb + (bcol < p.N ? bcol : 0);
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -167,40 +250,30 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_kernel(GroupedGemm p, int
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // B-tile column of MFMA tile j owned by this wavefront.
-  auto bcol_of = [&](int j) -> int {
-    if constexpr (SWIGLU) return (j < 4) ? (wn * 64 + j * 16) : (128 + wn * 64 + (j - 4) * 16);
-    return wn * 128 + j * 16;
-  };
-
+  // Pipeline: step ks computes from LDS buffer ks&1 while the global loads of
+  // step ks+1 are in flight in registers; they go to the other buffer after
+  // the MFMAs.  The fences keep the compiler from pulling the LDS stores (and
+  // their wait on the loads) in front of the MFMA block.
   const int nk = p.K / BK;
-  load_regs(0);
-  store_lds(0);
+  Stage st;
+  stage_load(st, aptr, bptr, p.ldb, 0);
+  stage_store(st, As[0], Bs[0], tid);
   __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < nk) load_regs((ks + 1) * BK);
-    const uint16_t* as = As[cur];
-    const uint16_t* bs = Bs[cur];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int koff = s * 32 + (lane >> 4) * 8;
-      bf16x8 af[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&as[(wm * 64 + i * 16 + (lane & 15)) * LDK + koff]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 bf =
-            *reinterpret_cast<const bf16x8*>(&bs[(bcol_of(j) + (lane & 15)) * LDK + koff]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
-      }
-    }
-    if (ks + 1 < nk) store_lds(cur ^ 1);
+  for (int ks = 0; ks < nk - 1; ++ks) {
+    const int cur = NBUF == 2 ? (ks & 1) : 0;
+    const int nxt = NBUF == 2 ? (cur ^ 1) : 0;
+    stage_load(st, aptr, bptr, p.ldb, (ks + 1) * BK);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step<SWIGLU>(acc, As[cur], Bs[cur], lane, wm, wn);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    if (NBUF == 1) __syncthreads();
+    stage_store(st, As[nxt], Bs[nxt], tid);
     __syncthreads();
   }
+  mfma_step<SWIGLU>(acc, As[NBUF == 2 ? ((nk - 1) & 1) : 0], Bs[NBUF == 2 ? ((nk - 1) & 1) : 0],
+                    lane, wm, wn);
 
   // ---- epilogue -----------------------------------------------------------
   // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
@@ -243,6 +316,245 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_kernel(GroupedGemm p, int
     }
   }
 }
+
+// ===========================================================================
+// bf16 MFMA kernel, gfx950 data path
+//
+// Global -> LDS with global_load_lds_dwordx4 (the load unit writes LDS
+// directly: no staging registers, no LDS write instructions) into an
+// NS-deep ring of stages, so NS-1 K steps of loads are in flight while one is
+// computed.  The weight tile stays N-contiguous in LDS, exactly as it sits in
+// memory, and the MFMA B fragments are read with ds_read_b64_tr_b16, which
+// transposes 16-bit elements across each 16-lane group: source lane 4q+r
+// supplies columns 4r..4r+3 of row k_q, and result lane i receives column i
+// of rows k_0..k_3.  Two such reads give a lane the 8 consecutive k values of
+// one column that v_mfma_f32_16x16x32_bf16 takes.
+//
+// LDS layouts (no padding; XOR swizzles keep every read conflict-free):
+//   A stage: BM rows x 128 bytes; 16-byte chunk c of row m sits at chunk
+//            c ^ (m & 7) ^ ((m >> 3) & 1).
+//   B stage: BK rows x 512 bytes; 32-byte segment s (16 columns) of row k
+//            sits at segment s ^ ((k & 3) | ((k >> 1) & 4)).
+// ===========================================================================
+namespace dma {
+
+constexpr int BM = kGroupedBM;           // 128
+constexpr int BN = 256;                  // B-tile columns (SwiGLU: 128 W1 + 128 W3)
+constexpr int BK = 64;
+constexpr int A_STAGE = BM * BK * 2;     // 16 KB
+constexpr int B_STAGE = BK * BN * 2;     // 32 KB
+constexpr int STAGE = A_STAGE + B_STAGE;
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 3
+#endif
+constexpr int NS = MOE_GEMM_STAGES;
+constexpr int LOADS_PER_STAGE = 12;      // per thread: 4 A + 8 B
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ int a_chunk(int m, int c) { return c ^ (m & 7) ^ ((m >> 3) & 1); }
+__device__ __forceinline__ int b_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <bool SWIGLU>
+__device__ __forceinline__ int bcol_of(int j, int wn) {
+  if constexpr (SWIGLU) return (j < 4) ? (wn * 64 + j * 16) : (128 + wn * 64 + (j - 4) * 16);
+  return wn * 128 + j * 16;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// One 16-byte-per-lane global -> LDS transfer: lane i's 16 bytes from src land
+// at LDS byte address lds + 16 i.  Written as asm so that the compiler, which
+// cannot tell these LDS writes apart from the LDS reads of other stages, does
+// not wait for them before every LDS read; the kernel waits on vmcnt itself.
+// The instruction has no result register.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p, int ntn,
+                                                                  int nblocks) {
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  const TileCoords tc = tile_coords<BM>(p, ntn, nblocks);
+  if (!tc.valid) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int e = p.group_base + tc.group + tc.ngroup;
+  const int64_t boff = static_cast<int64_t>(e) * p.b_stride;
+  constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+  const int n0 = tc.ntile * NOUT;
+
+  // ---- DMA sources ---------------------------------------------------------
+  // A: this wavefront fills rows (wave*4 + i)*8 .. +7 of a stage, one
+  // instruction per i; lane -> row + lane/8, stored chunk lane%8.  Rows past
+  // the tile's end repeat its first row (results not stored).
+  const uint16_t* A = static_cast<const uint16_t*>(p.A);
+  const uint16_t* asrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 8 + (lane >> 3);
+    const int rr = tc.row0 + (r < tc.nrows ? r : 0);
+    const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
+    asrc[i] = A + src * p.lda + a_chunk(r, lane & 7) * 8;
+  }
+  // B: this wavefront fills rows (wave*8 + i)*2 + lane/32 of a stage; lane's
+  // stored 16-byte chunk lane%32 is half (lane&1) of segment (lane%32)/2.
+  // Columns past N read column 0 (their outputs are never stored).
+  const uint16_t* bsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int kr = (wave * 8 + i) * 2 + (lane >> 5);
+    const int seg = ((lane & 31) >> 1) ^ b_swz(kr);
+    const int n = seg * 16 + (lane & 1) * 8;
+    const uint16_t* base;
+    int col;
+    if constexpr (SWIGLU) {
+      base = static_cast<const uint16_t*>(n < 128 ? p.B : p.B3);
+      col = n0 + (n & 127);
+    } else {
+      base = static_cast<const uint16_t*>(p.B);
+      col = n0 + n;
+    }
+    if (col >= p.N) col = 0;
+    bsrc[i] = base + boff + static_cast<int64_t>(kr) * p.ldb + col;
+  }
+
+  // LDS byte address of this wavefront's first A / B destination in stage 0
+  // (wave-uniform: M0 takes it).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int step) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + (step % NS) * STAGE;
+    const int k0 = step * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(asrc[i] + k0, sb + (wave_u * 4 + i) * 8 * 128);
+    const int64_t kb = static_cast<int64_t>(k0) * p.ldb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma16(bsrc[i] + kb, sb + A_STAGE + (wave_u * 8 + i) * 2 * 512);
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Fragment addressing (bytes within a stage).
+  const int g = lane >> 4;         // k block of 8 within a 32-k MFMA step
+  const int i16 = lane & 15;
+  const int tq = i16 >> 2, tr = i16 & 3;
+
+  auto compute = [&](int step) __attribute__((always_inline)) {
+    const char* sb = smem + (step % NS) * STAGE;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 64 + i * 16 + i16;
+        const int c = s * 4 + g;
+        af[i] = *reinterpret_cast<const bf16x8*>(sb + m * 128 + a_chunk(m, c) * 16);
+      }
+      const int k_lo = s * 32 + g * 8 + tq;   // rows of the two transposing reads
+      const int k_hi = k_lo + 4;
+      const int sw_lo = b_swz(k_lo), sw_hi = b_swz(k_hi);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sg = bcol_of<SWIGLU>(j, wn) >> 4;
+        const char* blo = sb + A_STAGE + k_lo * 512 + ((sg ^ sw_lo) * 32) + tr * 8;
+        const char* bhi = sb + A_STAGE + k_hi * 512 + ((sg ^ sw_hi) * 32) + tr * 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
+        const bf16x8 bf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- pipeline --------------------------------------------------------------
+  const int nk = p.K / BK;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st);
+  for (int ks = 0; ks < nk; ++ks) {
+    // this thread's loads of step ks are done once at most the later issued
+    // stages remain in flight; the barrier then covers every thread's loads
+    // and every wavefront's reads of the stage about to be refilled.
+    const int later = min(NS - 2, nk - 1 - ks);
+    if (later >= 2) wait_vmcnt<2 * LOADS_PER_STAGE>();
+    else if (later == 1) wait_vmcnt<LOADS_PER_STAGE>();
+    else wait_vmcnt<0>();
+    // A bare barrier: __syncthreads() adds a release fence that would wait
+    // for every load in flight, the later stages' included.  The LDS reads of
+    // the previous step are complete here (their results fed its MFMAs).
+    __builtin_amdgcn_s_barrier();
+    if (ks + NS - 1 < nk) issue(ks + NS - 1);
+    compute(ks);
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  const int64_t cgo = static_cast<int64_t>(tc.ngroup) * p.c_group_col;
+  if constexpr (SWIGLU) {
+    uint16_t* H = static_cast<uint16_t*>(p.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        if (rl >= tc.nrows) continue;
+        uint16_t* hrow = H + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+          if (col < p.N) hrow[col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 4][r]);
+        }
+      }
+    }
+  } else {
+    float* Y = static_cast<float*>(p.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        if (rl >= tc.nrows) continue;
+        float* yrow = Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+          if (col < p.N) yrow[col] = acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace dma
 
 // ===========================================================================
 // fp32 kernel (the fp32 layer): 64 x 64 output tiles, K step 16, each thread
@@ -333,8 +645,11 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedGemm p, int ntn
     for (int j = 0; j < 4; ++j) {
       const int col = n0 + tx * 4 + j;
       if (col < p.N)
-        if constexpr (SWIGLU) crow[col] = silu_f32_accurate(acc[i][j]) * acc3[i][j];
-        else crow[col] = acc[i][j];
+        if constexpr (SWIGLU) {
+          crow[col] = silu_f32_accurate(acc[i][j]) * acc3[i][j];
+        } else {
+          crow[col] = acc[i][j];
+        }
     }
   }
 }
@@ -350,10 +665,17 @@ hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s) 
 
 }  // namespace
 
+#ifndef MOE_GEMM_DMA
+#define MOE_GEMM_DMA 1
+#endif
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s) {
+  if (MOE_GEMM_DMA)
+    return launch_grid(dma::grouped_bf16_dma_kernel<true>, g, (g.N + BN / 2 - 1) / (BN / 2), s);
   return launch_grid(grouped_bf16_kernel<true>, g, (g.N + BN / 2 - 1) / (BN / 2), s);
 }
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s) {
+  if (MOE_GEMM_DMA)
+    return launch_grid(dma::grouped_bf16_dma_kernel<false>, g, (g.N + BN - 1) / BN, s);
   return launch_grid(grouped_bf16_kernel<false>, g, (g.N + BN - 1) / BN, s);
 }
 hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s) {

@@ -19,8 +19,7 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* lrank, int32_t* blkcnt, int32_t* counts,
                            int32_t* kcount, int32_t* offsets, int32_t* slot,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
-                           int bm2, Tile* tiles2, int32_t* ntiles2,
-                           hipStream_t s);
+                           int32_t* tstart, hipStream_t s);
 hipError_t launch_stats(const float* Ppart, const float* Hpart, int nblk,
                         const int32_t* counts, const int32_t* kcount, int64_t T,
                         int k, int E, double* out, hipStream_t s);
@@ -46,7 +45,9 @@ struct GroupedGemm {
   int64_t ldc;
   int64_t c_group_col;      // output column offset per N-group
   const Tile* tiles;        // device tile list, or null for static tiling
-  const int32_t* ntiles;
+  const int32_t* ntiles;    // number of tiles in the list
+  const int32_t* tstart;    // [E+1] first tile of each expert in the list
+  int n_experts;
   int static_rows;          // rows when tiles == null
   int max_mtiles;           // upper bound of M-tiles
 };

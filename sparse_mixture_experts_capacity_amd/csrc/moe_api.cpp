@@ -111,7 +111,7 @@ struct Plan {
   int max_mtiles = 0;
   // workspace regions
   Region logits, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
-      tiles, ntiles, ppart, hpart, stats, H, Hs, Y, Ys;
+      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys;
   size_t total = 0;
 };
 
@@ -245,6 +245,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->perm, sizeof(int32_t) * p->TK, cur);
   add(p->tiles, sizeof(moe::Tile) * (p->max_mtiles + 1), cur);
   add(p->ntiles, sizeof(int32_t) * 4, cur);
+  add(p->tstart, sizeof(int32_t) * (p->E + 1), cur);
   add(p->ppart, sizeof(float) * static_cast<size_t>(p->topk_blocks) * p->E, cur);
   add(p->hpart, sizeof(float) * p->topk_blocks, cur);
   add(p->stats, sizeof(double) * 8, cur);
@@ -293,8 +294,8 @@ int run_route(const Plan& p, void* ws, const float* logits, int32_t* idx, float*
                                  at<int32_t>(ws, p.blkcnt), at<int32_t>(ws, p.counts),
                                  at<int32_t>(ws, p.kcount), at<int32_t>(ws, p.offsets),
                                  at<int32_t>(ws, p.slot), at<int32_t>(ws, p.perm), p.bm,
-                                 at<moe::Tile>(ws, p.tiles), at<int32_t>(ws, p.ntiles), 0,
-                                 nullptr, nullptr, s));
+                                 at<moe::Tile>(ws, p.tiles), at<int32_t>(ws, p.ntiles),
+                                 at<int32_t>(ws, p.tstart), s));
   }
   return MOE_OK;
 }
@@ -394,6 +395,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.B = W1; g1.B3 = W3; g1.b_stride = dF; g1.group_base = 0; g1.ldb = p.F;
   g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
+  g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E;
   g1.static_rows = 0; g1.max_mtiles = p.max_mtiles;
   // GEMM2 (routed): Y[slot] = H[slot] W2[e]
   moe::GroupedGemm g2 = g1;
@@ -407,7 +409,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s1 = g1;
     s1.perm = nullptr; s1.group_base = p.E; s1.ngroups_n = p.S; s1.C = at<void>(ws, p.Hs);
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
-    s1.ntiles = nullptr; s1.static_rows = static_cast<int>(p.T);
+    s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);
     s1.max_mtiles = static_cast<int>((p.T + p.bm - 1) / p.bm);
     s2 = s1;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;

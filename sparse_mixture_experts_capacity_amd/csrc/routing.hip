@@ -317,18 +317,17 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
 // Dispatch, pass 2 (one workgroup): per expert, turn chunk totals into
 // exclusive chunk bases (in place) and the total count; apply the capacity;
 // prefix-sum the kept counts into slot offsets; build the M-tile list of the
-// grouped expert GEMMs (tiles of at most `bm` rows, expert by expert).
+// grouped expert GEMMs (tiles of at most `bm` rows, expert by expert) and the
+// index of each expert's first tile (tstart[E] = number of tiles).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     int32_t* __restrict__ blkcnt, int nblk, int E, int C,
     int32_t* __restrict__ counts, int32_t* __restrict__ kcount,
     int32_t* __restrict__ offsets, int bm, Tile* __restrict__ tiles,
-    int32_t* __restrict__ ntiles, int bm2, Tile* __restrict__ tiles2,
-    int32_t* __restrict__ ntiles2) {
+    int32_t* __restrict__ ntiles, int32_t* __restrict__ tstart) {
   __shared__ int kc[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int toff[kMaxExperts + 1];
-  __shared__ int toff2[kMaxExperts + 1];
   const int e = threadIdx.x;
   if (e < E) {
     int run = 0;
@@ -344,34 +343,26 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
   }
   __syncthreads();
   if (e == 0) {
-    int s = 0, ts = 0, ts2 = 0;
+    int s = 0, ts = 0;
     for (int i = 0; i < E; ++i) {
       off[i] = s;
       toff[i] = ts;
-      toff2[i] = ts2;
       s += kc[i];
       if (bm > 0) ts += (kc[i] + bm - 1) / bm;
-      if (bm2 > 0) ts2 += (kc[i] + bm2 - 1) / bm2;
     }
     off[E] = s;
     toff[E] = ts;
-    toff2[E] = ts2;
     if (ntiles) *ntiles = ts;
-    if (ntiles2) *ntiles2 = ts2;
   }
   __syncthreads();
-  for (int i = e; i <= E; i += blockDim.x) offsets[i] = off[i];
-  if (e < E) {
-    if (tiles && bm > 0) {
-      int n = 0;
-      for (int r = 0; r < kc[e]; r += bm, ++n)
-        tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
-    }
-    if (tiles2 && bm2 > 0) {
-      int n = 0;
-      for (int r = 0; r < kc[e]; r += bm2, ++n)
-        tiles2[toff2[e] + n] = Tile{e, off[e] + r, min(bm2, kc[e] - r), 0};
-    }
+  for (int i = e; i <= E; i += blockDim.x) {
+    offsets[i] = off[i];
+    if (tstart) tstart[i] = toff[i];
+  }
+  if (e < E && tiles && bm > 0) {
+    int n = 0;
+    for (int r = 0; r < kc[e]; r += bm, ++n)
+      tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
   }
 }
 
@@ -405,13 +396,11 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* lrank, int32_t* blkcnt, int32_t* counts,
                            int32_t* kcount, int32_t* offsets, int32_t* slot,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
-                           int bm2, Tile* tiles2, int32_t* ntiles2,
-                           hipStream_t s) {
+                           int32_t* tstart, hipStream_t s) {
   const int nblk = static_cast<int>((TK + kDispatchChunk - 1) / kDispatchChunk);
   dispatch_rank_kernel<<<nblk, 64, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
   dispatch_scan_kernel<<<1, 256, 0, s>>>(blkcnt, nblk, E, C, counts, kcount,
-                                         offsets, bm, tiles, ntiles, bm2, tiles2,
-                                         ntiles2);
+                                         offsets, bm, tiles, ntiles, tstart);
   dispatch_scatter_kernel<<<(TK + 255) / 256, 256, 0, s>>>(
       topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm);
   return hipGetLastError();
