@@ -51,6 +51,8 @@
  *     checked completely before anything is enqueued.  The reason for the
  *     last failure on the calling thread is in moe_last_error().
  *   - T = 0 is a valid, empty call: nothing is launched and stats are zero.
+ *   - A NaN router score ranks as -infinity (chosen only after every
+ *     number; ties by index) and gets gate weight 0.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -77,10 +79,15 @@ typedef enum {
   MOE_SOFTMAX_THEN_TOPK = 1   /* DeepSeek: softmax over all E, read top-k */
 } moe_gating_t;
 
+/* How the bf16 down projections (hidden -> model width) are laid out over the
+ * GPU.  Both paths run the same MFMA kernels and give results equal to
+ * rounding order.  fp32 layers accept AUTO and GROUPED only. */
 typedef enum {
-  MOE_PATH_AUTO = 0,     /* grouped GEMM when T > 64 (bf16), else streaming */
-  MOE_PATH_GROUPED = 1,  /* MFMA grouped GEMM, weight tiles shared via L2 */
-  MOE_PATH_STREAM = 2    /* weight-streaming kernels for few rows/expert */
+  MOE_PATH_AUTO = 0,     /* split K only when the output tiles alone give
+                            fewer than 256 workgroups (short batches) */
+  MOE_PATH_GROUPED = 1,  /* never split K: one workgroup per output tile */
+  MOE_PATH_STREAM = 2    /* always split K toward ~512 workgroups, streaming
+                            each expert's weights through many CUs */
 } moe_ffn_path_t;
 
 typedef struct {

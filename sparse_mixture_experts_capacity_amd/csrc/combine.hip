@@ -26,16 +26,17 @@ __global__ __launch_bounds__(256) void combine_kernel(
     int k, int d, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
   if (t >= T) return;
-  const int tid = threadIdx.x;
   const bool vec = (d & 3) == 0;
   const int ncols = vec ? d / 4 : d;
-  for (int c = tid; c < ncols; c += blockDim.x) {
+  // blockIdx.y picks a chunk of blockDim.x columns (float4 units when d % 4 == 0)
+  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < ncols; c += gridDim.y * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int s = slot[t * k + j];
       if (s < 0) continue;
       const float w = topk_w[t * k + j];
       float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
       for (int p = 0; p < ysplit; ++p) {
         const float* row = Y + p * ysplit_stride + static_cast<int64_t>(s) * d;
         if (vec) {
@@ -86,12 +87,17 @@ hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
                           int64_t T, int k, int d, void* out, bool bf16,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  // enough workgroups to cover the GPU even for a handful of tokens
+  const int ncols = (d & 3) == 0 ? d / 4 : d;
+  int chunks = (ncols + 255) / 256;
+  if (T >= 256) chunks = 1;
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
   if (bf16)
-    combine_kernel<true><<<T, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
-                                           ys_split, ys_stride, T, k, d, out);
+    combine_kernel<true><<<grid, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+                                              ys_split, ys_stride, T, k, d, out);
   else
-    combine_kernel<false><<<T, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
-                                            ys_split, ys_stride, T, k, d, out);
+    combine_kernel<false><<<grid, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+                                               ys_split, ys_stride, T, k, d, out);
   return hipGetLastError();
 }
 

@@ -37,6 +37,7 @@ struct TileCoords {
   int nrows;
   int ntile;   // N-tile within the group
   int ngroup;  // N-group (shared experts laid along N)
+  int kpart;   // part of a split K (static tiling)
   bool valid;
 };
 
@@ -51,16 +52,19 @@ struct TileCoords {
 template <int TBM>
 __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
                                                   int /*nblocks*/) {
-  TileCoords tc{0, 0, 0, 0, 0, false};
+  TileCoords tc{0, 0, 0, 0, 0, 0, false};
   const int ntn_all = ntn * p.ngroups_n;
   const int mtiles = p.tiles ? *p.ntiles : (p.static_rows + TBM - 1) / TBM;
-  const int total = mtiles * ntn_all;
+  const int ks = p.ksplit;
+  const int total = mtiles * ntn_all * ks;
   const int per = (total + 7) >> 3;
   const int x = blockIdx.x & 7;
   const int i = blockIdx.x >> 3;
   if (i >= per) return tc;
-  const int L = x * per + i;
-  if (L >= total) return tc;
+  const int LK = x * per + i;
+  if (LK >= total) return tc;
+  tc.kpart = LK % ks;   // K parts of one tile are adjacent: they share A rows
+  const int L = LK / ks;
   int m, n_all;
   if (p.tiles) {
     // expert e owns logical tiles [tstart[e] * ntn_all, tstart[e+1] * ntn_all)
@@ -91,233 +95,6 @@ __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
 }
 
 // ===========================================================================
-// bf16 MFMA kernel
-// ===========================================================================
-constexpr int BM = kGroupedBM;  // 128
-constexpr int BN = 256;         // B-tile columns (SwiGLU: 128 W1 + 128 W3)
-constexpr int BK = 64;
-constexpr int LDK = BK + 8;     // padded LDS row (144 bytes, conflict-free)
-#ifndef MOE_GEMM_NBUF
-#define MOE_GEMM_NBUF 2
-#endif
-constexpr int NBUF = MOE_GEMM_NBUF;  // LDS stages: 2 = double buffer, 1 = two workgroups per CU
-
-// 8 (k) x 8 (n) bf16 block transpose: in[r] holds row r (n = 0..7, two per
-// dword), out[c] holds column c (k = 0..7, two per dword).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-  const uint32_t* r = reinterpret_cast<const uint32_t*>(in);
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t a = r[(2 * q) * 4 + (c >> 1)];
-      const uint32_t b = r[(2 * q + 1) * 4 + (c >> 1)];
-      o[c * 4 + q] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u))
-                             : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-
-// Per-thread staging of one K step: 4 chunks of token rows, one 8 x 8 block
-// of weights.
-struct Stage {
-  u32x4 a[4];
-  u32x4 b[8];
-};
-
-__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* const (&aptr)[4],
-                                           const uint16_t* bptr, int64_t ldb, int k0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const u32x4*>(aptr[i] + k0);
-#pragma unroll
-  for (int r = 0; r < 8; ++r)
-    st.b[r] = *reinterpret_cast<const u32x4*>(bptr + static_cast<int64_t>(k0 + r) * ldb);
-}
-
-__device__ __forceinline__ void stage_store(const Stage& st, uint16_t* as, uint16_t* bs,
-                                            int tid) {
-  const int akc = tid & 7;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4*>(&as[r * LDK + akc * 8]) = st.a[i];
-  }
-  u32x4 col[8];
-  transpose8x8(st.b, col);
-  const int kb = tid & 7, nb = tid >> 3;
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    *reinterpret_cast<u32x4*>(&bs[(nb * 8 + c) * LDK + kb * 8]) = col[c];
-}
-
-// B-tile column of MFMA tile j owned by wavefront column wn.
-template <bool SWIGLU>
-__device__ __forceinline__ int bcol_of(int j, int wn) {
-  if constexpr (SWIGLU) return (j < 4) ? (wn * 64 + j * 16) : (128 + wn * 64 + (j - 4) * 16);
-  return wn * 128 + j * 16;
-}
-
-template <bool SWIGLU>
-__device__ __forceinline__ bf16x8 load_bfrag(const uint16_t* bs, int j, int lane, int wn, int koff) {
-  return *reinterpret_cast<const bf16x8*>(&bs[(bcol_of<SWIGLU>(j, wn) + (lane & 15)) * LDK + koff]);
-}
-
-// One K step (64) of the wavefront's 64 x 128 sub-tile: 2 x (4 x 8) MFMAs.
-// The next B fragment is read from LDS while the current one feeds its four
-// MFMAs.
-template <bool SWIGLU>
-__device__ __forceinline__ void mfma_step(f32x4 (&acc)[4][8], const uint16_t* as,
-                                          const uint16_t* bs, int lane, int wm, int wn) {
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int koff = s * 32 + (lane >> 4) * 8;
-    bf16x8 af[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(&as[(wm * 64 + i * 16 + (lane & 15)) * LDK + koff]);
-    bf16x8 bcur = load_bfrag<SWIGLU>(bs, 0, lane, wn, koff);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x8 bnext = bcur;
-      if (j + 1 < 8) bnext = load_bfrag<SWIGLU>(bs, j + 1, lane, wn, koff);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bcur, acc[i][j], 0, 0, 0);
-      bcur = bnext;
-    }
-    // Issue order for the scheduler: the A fragments and two B fragments,
-    // then per B fragment its four MFMAs followed by the next fragment read.
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
-#pragma unroll
-    for (int j = 0; j < 7; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-      if (j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  }
-}
-
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 3 - NBUF) void grouped_bf16_kernel(GroupedGemm p, int ntn,
-                                                              int nblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[NBUF][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[NBUF][BN * LDK];
-
-  const TileCoords tc = tile_coords<BM>(p, ntn, nblocks);
-  if (!tc.valid) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int e = p.group_base + tc.group + tc.ngroup;
-  const int64_t boff = static_cast<int64_t>(e) * p.b_stride;
-  constexpr int NOUT = SWIGLU ? BN / 2 : BN;   // output columns per tile
-  const int n0 = tc.ntile * NOUT;
-
-  // Token rows: thread loads 16-byte chunk tid%8 of rows tid/8 + 32 i.  Rows
-  // past the tile's end repeat its first row; their results are not stored.
-  const uint16_t* A = static_cast<const uint16_t*>(p.A);
-  const uint16_t* aptr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    const int rr = tc.row0 + (r < tc.nrows ? r : 0);
-    const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
-    aptr[i] = A + src * p.lda + (tid & 7) * 8;
-  }
-  // Weights: one 8 (k) x 8 (n) block per thread.  A column block past N
-  // reads column 0 instead; those accumulators feed output columns >= N,
-  // which are never stored.
-  const int kb = tid & 7;
-  const int nb = tid >> 3;
-  const uint16_t* bsrc;
-  int bcol;
-  if constexpr (SWIGLU) {
-    bsrc = static_cast<const uint16_t*>(nb < 16 ? p.B : p.B3);
-    bcol = n0 + (nb & 15) * 8;
-  } else {
-    bsrc = static_cast<const uint16_t*>(p.B);
-    bcol = n0 + nb * 8;
-  }
-  const uint16_t* bptr = bsrc + boff + static_cast<int64_t>(kb * 8) * p.ldb + (bcol < p.N ? bcol : 0);
-
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Pipeline: step ks computes from LDS buffer ks&1 while the global loads of
-  // step ks+1 are in flight in registers; they go to the other buffer after
-  // the MFMAs.  The fences keep the compiler from pulling the LDS stores (and
-  // their wait on the loads) in front of the MFMA block.
-  const int nk = p.K / BK;
-  Stage st;
-  stage_load(st, aptr, bptr, p.ldb, 0);
-  stage_store(st, As[0], Bs[0], tid);
-  __syncthreads();
-  for (int ks = 0; ks < nk - 1; ++ks) {
-    const int cur = NBUF == 2 ? (ks & 1) : 0;
-    const int nxt = NBUF == 2 ? (cur ^ 1) : 0;
-    stage_load(st, aptr, bptr, p.ldb, (ks + 1) * BK);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step<SWIGLU>(acc, As[cur], Bs[cur], lane, wm, wn);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-    if (NBUF == 1) __syncthreads();
-    stage_store(st, As[nxt], Bs[nxt], tid);
-    __syncthreads();
-  }
-  mfma_step<SWIGLU>(acc, As[NBUF == 2 ? ((nk - 1) & 1) : 0], Bs[NBUF == 2 ? ((nk - 1) & 1) : 0],
-                    lane, wm, wn);
-
-  // ---- epilogue -----------------------------------------------------------
-  // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
-  const int64_t cgo = static_cast<int64_t>(tc.ngroup) * p.c_group_col;
-  if constexpr (SWIGLU) {
-    uint16_t* H = static_cast<uint16_t*>(p.C);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (rl >= tc.nrows) continue;
-        uint16_t* hrow = H + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-          if (col < p.N) {
-            const float u = acc[i][j][r];
-            const float v = acc[i][j + 4][r];
-            hrow[col] = f32_to_bf16(silu_f32(u) * v);
-          }
-        }
-      }
-    }
-  } else {
-    float* Y = static_cast<float*>(p.C);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (rl >= tc.nrows) continue;
-        float* yrow = Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
-          if (col < p.N) yrow[col] = acc[i][j][r];
-        }
-      }
-    }
-  }
-}
-
-// ===========================================================================
 // bf16 MFMA kernel, gfx950 data path
 //
 // Global -> LDS with global_load_lds_dwordx4 (the load unit writes LDS
@@ -338,20 +115,35 @@ __global__ __launch_bounds__(256, 3 - NBUF) void grouped_bf16_kernel(GroupedGemm
 // ===========================================================================
 namespace dma {
 
-constexpr int BM = kGroupedBM;           // 128
 constexpr int BN = 256;                  // B-tile columns (SwiGLU: 128 W1 + 128 W3)
 constexpr int BK = 64;
-constexpr int A_STAGE = BM * BK * 2;     // 16 KB
 constexpr int B_STAGE = BK * BN * 2;     // 32 KB
-constexpr int STAGE = A_STAGE + B_STAGE;
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 3
-#endif
-constexpr int NS = MOE_GEMM_STAGES;
-constexpr int LOADS_PER_STAGE = 12;      // per thread: 4 A + 8 B
+
+// Two M-tile shapes: 128 rows (2 x 2 wavefronts of 64 x 128, 3-stage ring)
+// for batches with many rows per expert, and 32 rows (1 x 4 wavefronts of
+// 32 x 64, 4-stage ring) for short batches, where each expert has a few rows
+// and the kernel mostly streams weights.
+template <int BM_, int NW_>
+struct Shape {
+  static constexpr int BM = BM_;
+  static constexpr int NW = NW_;                     // wavefronts per workgroup
+  static constexpr int WM = BM_ >= 128 ? 2 : 1;      // wavefronts along M
+  static constexpr int WN = NW_ / WM;                // wavefronts along N
+  static constexpr int WROWS = BM_ / WM;
+  static constexpr int WCOLS = BN / WN;
+  static constexpr int MI = WROWS / 16;              // MFMA tiles per wavefront
+  static constexpr int NJ = WCOLS / 16;
+  static constexpr int A_STAGE = BM_ * BK * 2;
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int NS = BM_ >= 128 ? 3 : 4;
+  static constexpr int A_LOADS = BM_ / (8 * NW_);    // per thread per stage
+  static constexpr int B_LOADS = (BK / 2) / NW_;
+  static constexpr int LOADS = A_LOADS + B_LOADS;
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && NJ % 2 == 0, "shape");
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ int a_chunk(int m, int c) { return c ^ (m & 7) ^ ((m >> 3) & 1); }
@@ -364,11 +156,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait until at most `later` stages of LOADS transfers each are in flight.
+template <int LOADS>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (later >= 2) wait_vmcnt<2 * LOADS>();
+  else if (later == 1) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+}
 
-template <bool SWIGLU>
+// First B-tile column of MFMA tile j of wavefront column wn.
+template <class S, bool SWIGLU>
 __device__ __forceinline__ int bcol_of(int j, int wn) {
-  if constexpr (SWIGLU) return (j < 4) ? (wn * 64 + j * 16) : (128 + wn * 64 + (j - 4) * 16);
-  return wn * 128 + j * 16;
+  if constexpr (SWIGLU) {
+    constexpr int H = S::NJ / 2;   // first half: W1 columns, second half: W3
+    return (j < H) ? (wn * (S::WCOLS / 2) + j * 16) : (BN / 2 + wn * (S::WCOLS / 2) + (j - H) * 16);
+  }
+  return wn * S::WCOLS + j * 16;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -388,10 +191,12 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p, int ntn,
-                                                                  int nblocks) {
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+template <bool SWIGLU, int BM_, int NW_>
+__global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGemm p, int ntn,
+                                                                       int nblocks) {
+  using S = Shape<BM_, NW_>;
+  constexpr int BM = S::BM, NS = S::NS, MI = S::MI, NJ = S::NJ;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S::STAGE];
 
   const TileCoords tc = tile_coords<BM>(p, ntn, nblocks);
   if (!tc.valid) return;
@@ -399,40 +204,40 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / S::WN;
+  const int wn = wave % S::WN;
   const int e = p.group_base + tc.group + tc.ngroup;
   const int64_t boff = static_cast<int64_t>(e) * p.b_stride;
   constexpr int NOUT = SWIGLU ? BN / 2 : BN;
   const int n0 = tc.ntile * NOUT;
 
   // ---- DMA sources ---------------------------------------------------------
-  // A: this wavefront fills rows (wave*4 + i)*8 .. +7 of a stage, one
+  // A: this wavefront fills rows (wave*A_LOADS + i)*8 .. +7 of a stage, one
   // instruction per i; lane -> row + lane/8, stored chunk lane%8.  Rows past
   // the tile's end repeat its first row (results not stored).
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
-  const uint16_t* asrc[4];
+  const uint16_t* asrc[S::A_LOADS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave * 4 + i) * 8 + (lane >> 3);
+  for (int i = 0; i < S::A_LOADS; ++i) {
+    const int r = (wave * S::A_LOADS + i) * 8 + (lane >> 3);
     const int rr = tc.row0 + (r < tc.nrows ? r : 0);
     const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
     asrc[i] = A + src * p.lda + a_chunk(r, lane & 7) * 8;
   }
-  // B: this wavefront fills rows (wave*8 + i)*2 + lane/32 of a stage; lane's
+  // B: this wavefront fills rows (wave*B_LOADS + i)*2 + lane/32 of a stage; lane's
   // stored 16-byte chunk lane%32 is half (lane&1) of segment (lane%32)/2.
   // Columns past N read column 0 (their outputs are never stored).
-  const uint16_t* bsrc[8];
+  const uint16_t* bsrc[S::B_LOADS];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int kr = (wave * 8 + i) * 2 + (lane >> 5);
+  for (int i = 0; i < S::B_LOADS; ++i) {
+    const int kr = (wave * S::B_LOADS + i) * 2 + (lane >> 5);
     const int seg = ((lane & 31) >> 1) ^ b_swz(kr);
     const int n = seg * 16 + (lane & 1) * 8;
     const uint16_t* base;
     int col;
     if constexpr (SWIGLU) {
-      base = static_cast<const uint16_t*>(n < 128 ? p.B : p.B3);
-      col = n0 + (n & 127);
+      base = static_cast<const uint16_t*>(n < BN / 2 ? p.B : p.B3);
+      col = n0 + (n & (BN / 2 - 1));
     } else {
       base = static_cast<const uint16_t*>(p.B);
       col = n0 + n;
@@ -441,25 +246,29 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
     bsrc[i] = base + boff + static_cast<int64_t>(kr) * p.ldb + col;
   }
 
-  // LDS byte address of this wavefront's first A / B destination in stage 0
+  // LDS byte address of this wavefront's destinations in stage 0
   // (wave-uniform: M0 takes it).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
+  const int kper = p.K / p.ksplit;           // this block's share of K
+  const int kbase = tc.kpart * kper;
   auto issue = [&](int step) __attribute__((always_inline)) {
-    const uint32_t sb = lds0 + (step % NS) * STAGE;
-    const int k0 = step * BK;
+    const uint32_t sb = lds0 + (step % NS) * S::STAGE;
+    const int k0 = kbase + step * BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(asrc[i] + k0, sb + (wave_u * 4 + i) * 8 * 128);
+    for (int i = 0; i < S::A_LOADS; ++i)
+      dma16(asrc[i] + k0, sb + (wave_u * S::A_LOADS + i) * 8 * 128);
     const int64_t kb = static_cast<int64_t>(k0) * p.ldb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(bsrc[i] + kb, sb + A_STAGE + (wave_u * 8 + i) * 2 * 512);
+    for (int i = 0; i < S::B_LOADS; ++i)
+      dma16(bsrc[i] + kb, sb + S::A_STAGE + (wave_u * S::B_LOADS + i) * 2 * 512);
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Fragment addressing (bytes within a stage).
   const int g = lane >> 4;         // k block of 8 within a 32-k MFMA step
@@ -467,13 +276,13 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
   const int tq = i16 >> 2, tr = i16 & 3;
 
   auto compute = [&](int step) __attribute__((always_inline)) {
-    const char* sb = smem + (step % NS) * STAGE;
+    const char* sb = smem + (step % NS) * S::STAGE;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8 af[4];
+      bf16x8 af[MI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + i * 16 + i16;
+      for (int i = 0; i < MI; ++i) {
+        const int m = wm * S::WROWS + i * 16 + i16;
         const int c = s * 4 + g;
         af[i] = *reinterpret_cast<const bf16x8*>(sb + m * 128 + a_chunk(m, c) * 16);
       }
@@ -481,23 +290,23 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
       const int k_hi = k_lo + 4;
       const int sw_lo = b_swz(k_lo), sw_hi = b_swz(k_hi);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sg = bcol_of<SWIGLU>(j, wn) >> 4;
-        const char* blo = sb + A_STAGE + k_lo * 512 + ((sg ^ sw_lo) * 32) + tr * 8;
-        const char* bhi = sb + A_STAGE + k_hi * 512 + ((sg ^ sw_hi) * 32) + tr * 8;
+      for (int j = 0; j < NJ; ++j) {
+        const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
+        const char* blo = sb + S::A_STAGE + k_lo * 512 + ((sg ^ sw_lo) * 32) + tr * 8;
+        const char* bhi = sb + S::A_STAGE + k_hi * 512 + ((sg ^ sw_hi) * 32) + tr * 8;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
         const bf16x8 bf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
       }
     }
   };
 
   // ---- pipeline --------------------------------------------------------------
-  const int nk = p.K / BK;
+  const int nk = kper / BK;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st);
@@ -505,10 +314,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
     // this thread's loads of step ks are done once at most the later issued
     // stages remain in flight; the barrier then covers every thread's loads
     // and every wavefront's reads of the stage about to be refilled.
-    const int later = min(NS - 2, nk - 1 - ks);
-    if (later >= 2) wait_vmcnt<2 * LOADS_PER_STAGE>();
-    else if (later == 1) wait_vmcnt<LOADS_PER_STAGE>();
-    else wait_vmcnt<0>();
+    wait_stages<S::LOADS>(min(NS - 2, nk - 1 - ks));
     // A bare barrier: __syncthreads() adds a release fence that would wait
     // for every load in flight, the later stages' included.  The LDS reads of
     // the previous step are complete here (their results fed its MFMAs).
@@ -518,35 +324,37 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_dma_kernel(GroupedGemm p,
   }
 
   // ---- epilogue -----------------------------------------------------------
+  // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
   const int64_t cgo = static_cast<int64_t>(tc.ngroup) * p.c_group_col;
   if constexpr (SWIGLU) {
     uint16_t* H = static_cast<uint16_t*>(p.C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
         if (rl >= tc.nrows) continue;
         uint16_t* hrow = H + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-          if (col < p.N) hrow[col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + 4][r]);
+        for (int j = 0; j < NJ / 2; ++j) {
+          const int col = n0 + wn * (S::WCOLS / 2) + j * 16 + (lane & 15);
+          if (col < p.N)
+            hrow[col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
         }
       }
     }
   } else {
-    float* Y = static_cast<float*>(p.C);
+    float* Y = static_cast<float*>(p.C) + tc.kpart * p.c_split;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
         if (rl >= tc.nrows) continue;
         float* yrow = Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+        for (int j = 0; j < NJ; ++j) {
+          const int col = n0 + wn * S::WCOLS + j * 16 + (lane & 15);
           if (col < p.N) yrow[col] = acc[i][j][r];
         }
       }
@@ -655,28 +463,30 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedGemm p, int ntn
 }
 
 template <typename Kern>
-hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s) {
-  const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n;
+hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, int waves = 4) {
+  const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n * g.ksplit;
   if (logical <= 0) return hipSuccess;
   const int nblocks = static_cast<int>((logical + 7) / 8 * 8);
-  kern<<<nblocks, 256, 0, s>>>(g, ntn, nblocks);
+  kern<<<nblocks, 64 * waves, 0, s>>>(g, ntn, nblocks);
   return hipGetLastError();
 }
 
 }  // namespace
 
-#ifndef MOE_GEMM_DMA
-#define MOE_GEMM_DMA 1
+#ifndef MOE_GEMM_WAVES_LONG
+#define MOE_GEMM_WAVES_LONG 8
 #endif
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s) {
-  if (MOE_GEMM_DMA)
-    return launch_grid(dma::grouped_bf16_dma_kernel<true>, g, (g.N + BN / 2 - 1) / (BN / 2), s);
-  return launch_grid(grouped_bf16_kernel<true>, g, (g.N + BN / 2 - 1) / (BN / 2), s);
+  const int ntn = (g.N + dma::BN / 2 - 1) / (dma::BN / 2);
+  if (g.bm == 32) return launch_grid(dma::grouped_bf16_dma_kernel<true, 32, 4>, g, ntn, s, 4);
+  return launch_grid(dma::grouped_bf16_dma_kernel<true, 128, MOE_GEMM_WAVES_LONG>, g, ntn, s,
+                     MOE_GEMM_WAVES_LONG);
 }
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s) {
-  if (MOE_GEMM_DMA)
-    return launch_grid(dma::grouped_bf16_dma_kernel<false>, g, (g.N + BN - 1) / BN, s);
-  return launch_grid(grouped_bf16_kernel<false>, g, (g.N + BN - 1) / BN, s);
+  const int ntn = (g.N + dma::BN - 1) / dma::BN;
+  if (g.bm == 32) return launch_grid(dma::grouped_bf16_dma_kernel<false, 32, 4>, g, ntn, s, 4);
+  return launch_grid(dma::grouped_bf16_dma_kernel<false, 128, MOE_GEMM_WAVES_LONG>, g, ntn, s,
+                     MOE_GEMM_WAVES_LONG);
 }
 hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s) {
   return launch_grid(grouped_f32_kernel<true>, g, (g.N + FBN - 1) / FBN, s);

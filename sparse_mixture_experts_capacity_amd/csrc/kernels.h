@@ -11,8 +11,12 @@ hipError_t launch_router(const void* x, const void* Wg, const float* bias,
                          float* logits, int64_t T, int d, int E, bool bf16,
                          hipStream_t s);
 int topk_group_size(int E);
-hipError_t launch_topk_gate(const float* logits, int64_t T, int E, int k,
-                            int gating, int renorm, int32_t* topk_idx,
+// Router scores are read as the sum of `nsplit` partial arrays (split_stride
+// apart) plus the optional bias, in a fixed order; when logits_out is given
+// the summed scores are also stored there.
+hipError_t launch_topk_gate(const float* lpart, int nsplit, int64_t split_stride,
+                            const float* bias, float* logits_out, int64_t T, int E,
+                            int k, int gating, int renorm, int32_t* topk_idx,
                             float* topk_w, float* Ppart, float* Hpart,
                             int nblocks, int tokens_per_block, hipStream_t s);
 hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
@@ -50,8 +54,12 @@ struct GroupedGemm {
   int n_experts;
   int static_rows;          // rows when tiles == null
   int max_mtiles;           // upper bound of M-tiles
+  int bm;                   // M-tile rows (bf16: 128 or 32; fp32: 64); tiles match it
+  int ksplit;               // K is split in this many parts (plain fp32 output only);
+  int64_t c_split;          // part p writes C + p * c_split (fp32 partial sums)
 };
-constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels
+constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels, long batches
+constexpr int kGroupedBMShort = 32;  // M-tile for short batches (few rows per expert)
 constexpr int kF32BM = 64;        // M-tile of the fp32 kernels
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s);

@@ -109,8 +109,13 @@ struct Plan {
   int topk_blocks = 0, topk_tpb = 0;
   int bm = 0;                    // M-tile of the grouped kernels
   int max_mtiles = 0;
+  int static_bm = 0;             // M-tile of the GEMMs over all T token rows
+  bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
+  int router_split = 1;          // K parts of the router GEMM
+  int ffn2_split = 1;            // K parts of the routed down projection
+  int shared2_split = 1;         // K parts of the shared down projection
   // workspace regions
-  Region logits, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
+  Region logits, lpart, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
       tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys;
   size_t total = 0;
 };
@@ -186,13 +191,25 @@ int check(const moe_config_t* c) {
     if (c->d_model % 64 != 0 || c->d_ff % 64 != 0)
       return fail(MOE_EUNSUPPORTED, "bf16 layers need d_model and d_ff divisible by 64 (got %d, %d)",
                   c->d_model, c->d_ff);
-    if (c->ffn_path == MOE_PATH_STREAM)
-      return fail(MOE_EUNSUPPORTED, "the weight-streaming path is not built in this library");
   } else {
     if (c->ffn_path == MOE_PATH_STREAM)
       return fail(MOE_EUNSUPPORTED, "fp32 layers run on the fp32 grouped kernels only");
   }
   return MOE_OK;
+}
+
+// K parts for a GEMM with `tiles` output tiles and `ksteps` 64-deep K
+// steps: enough for ~512 workgroups (more than 1 only when the tiles alone
+// give fewer than 256), a divisor of ksteps.
+int split_for(int64_t tiles, int ksteps, bool force) {
+  if (tiles <= 0) return 1;
+  if (!force && tiles >= 256) return 1;
+  int64_t ks = (512 + tiles - 1) / tiles;
+  if (ks > ksteps) ks = ksteps;
+  if (ks > 64) ks = 64;
+  if (ks < 1) ks = 1;
+  while (ksteps % ks) --ks;
+  return static_cast<int>(ks);
 }
 
 void add(Region& r, size_t bytes, size_t& cursor) {
@@ -213,7 +230,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->gating = c->gating;
   p->renorm = c->renormalize;
   p->bf16 = c->dtype == MOE_DTYPE_BF16;
-  p->path = MOE_PATH_GROUPED;
+  p->path = c->ffn_path;
   p->capacity = exact_capacity(c->T, c->top_k, c->n_experts, c->capacity_factor);
   if (p->capacity < 0) return fail(MOE_EINVAL, "capacity_factor is not finite");
   p->Ceff = static_cast<int>(p->capacity < p->T ? p->capacity : p->T);
@@ -228,12 +245,50 @@ int make_plan(const moe_config_t* c, Plan* p) {
   if (tpb < groups) tpb = groups;
   p->topk_tpb = static_cast<int>(tpb);
   p->topk_blocks = static_cast<int>((p->T + tpb - 1) / tpb);
-  p->bm = p->bf16 ? moe::kGroupedBM : moe::kF32BM;
+  // M-tile: 32 rows when the hit experts average at most 48 rows each (short
+  // batches), else 128; the tile list is built for it.
+  if (p->bf16) {
+    const int64_t hit = p->TK < p->E ? p->TK : p->E;
+    const bool short_rows = hit > 0 && p->TK <= 48 * hit;
+    p->bm = short_rows ? moe::kGroupedBMShort : moe::kGroupedBM;
+    p->static_bm = p->T <= 64 ? moe::kGroupedBMShort : moe::kGroupedBM;
+  } else {
+    p->bm = p->static_bm = moe::kF32BM;
+  }
   p->max_mtiles = static_cast<int>(p->rows_max / p->bm + p->E);
+  // Router scores x W_gate on the MFMA GEMM when the weight rows are 16-byte
+  // aligned; K is split so that even short batches give ~512 workgroups, and
+  // the top-k pass adds the parts in a fixed order.
+  p->mfma_router = p->bf16 && (p->E % 8 == 0);
+  if (p->mfma_router) {
+    const int kk = p->d / 64;
+    const int64_t mt = (p->T + p->static_bm - 1) / p->static_bm;
+    int64_t ks = mt > 0 ? (512 + mt - 1) / mt : 1;
+    if (ks > kk) ks = kk;
+    if (ks < 1) ks = 1;
+    while (kk % ks) --ks;
+    p->router_split = static_cast<int>(ks);
+  }
+  // Down projections with few tiles (short batches: a few rows per expert)
+  // split K so ~512 workgroups stream the weights; the combine adds the
+  // parts in a fixed order.  The estimate of routed M-tiles assumes at most
+  // min(E, T*k) experts are hit.  The grouped path never splits; the
+  // streaming path always splits as far as the workgroup target allows.
+  if (p->bf16 && p->path != MOE_PATH_GROUPED) {
+    const int ntn2 = (p->d + 255) / 256;
+    const int64_t hit = p->TK < p->E ? p->TK : p->E;
+    const int64_t mt_est = p->rows_max / p->bm + hit;
+    p->ffn2_split = split_for(mt_est * ntn2, p->F / 64, p->path == MOE_PATH_STREAM);
+    if (p->S > 0) {
+      const int64_t mts = (p->T + p->static_bm - 1) / p->static_bm;
+      p->shared2_split = split_for(mts * ntn2, p->S * p->F / 64, p->path == MOE_PATH_STREAM);
+    }
+  }
 
   const size_t es = p->bf16 ? 2 : 4;
   size_t cur = 0;
   add(p->logits, sizeof(float) * p->T * p->E, cur);
+  add(p->lpart, sizeof(float) * (p->mfma_router ? p->router_split : 0) * p->T * p->E, cur);
   add(p->idx, sizeof(int32_t) * p->TK, cur);
   add(p->w, sizeof(float) * p->TK, cur);
   add(p->lrank, sizeof(int32_t) * p->TK, cur);
@@ -251,8 +306,8 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->stats, sizeof(double) * 8, cur);
   add(p->H, es * p->rows_max * p->F, cur);
   add(p->Hs, es * p->T * p->S * p->F, cur);
-  add(p->Y, sizeof(float) * p->rows_max * p->d, cur);
-  add(p->Ys, sizeof(float) * (p->S > 0 ? p->T : 0) * p->d, cur);
+  add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
+  add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
   p->total = cur;
   return MOE_OK;
 }
@@ -279,12 +334,48 @@ int check_workspace(const moe_config_t* c, const Plan& p) {
       return fail(MOE_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
   } while (0)
 
-// Steps 2-3 (top-k, gates, dispatch) from logits already in `logits`.
-int run_route(const Plan& p, void* ws, const float* logits, int32_t* idx, float* w,
-              hipStream_t s) {
+// Step 1: router scores.  Returns, through lsrc/nsplit/bias, where the
+// top-k pass finds them: K-split partial sums of the MFMA GEMM (bias added
+// by the top-k pass) or complete scores from the vector kernels.
+struct Scores {
+  const float* lsrc;
+  int nsplit;
+  int64_t split_stride;
+  const float* bias;
+};
+
+int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
+               const float* bias, hipStream_t s, Scores* sc) {
+  if (p.mfma_router) {
+    moe::GroupedGemm r{};
+    r.A = x; r.lda = p.d; r.perm = nullptr; r.topk = 1;
+    r.B = W_gate; r.B3 = nullptr; r.b_stride = 0; r.group_base = 0; r.ldb = p.E;
+    r.K = p.d; r.N = p.E; r.ngroups_n = 1; r.C = at<float>(ws, p.lpart); r.ldc = p.E;
+    r.c_group_col = 0; r.tiles = nullptr; r.ntiles = nullptr; r.tstart = nullptr;
+    r.n_experts = 1; r.static_rows = static_cast<int>(p.T);
+    r.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
+    r.bm = p.static_bm;
+    r.ksplit = p.router_split; r.c_split = p.T * p.E;
+    Timed t("router", s);
+    HIP_TRY(moe::launch_grouped_plain_bf16(r, s));
+    *sc = Scores{at<float>(ws, p.lpart), p.router_split, p.T * p.E, bias};
+  } else {
+    Timed t("router", s);
+    HIP_TRY(moe::launch_router(x, W_gate, bias, at<float>(ws, p.logits), p.T, p.d, p.E,
+                               p.bf16, s));
+    *sc = Scores{at<float>(ws, p.logits), 1, 0, nullptr};
+  }
+  return MOE_OK;
+}
+
+// Steps 2-3 (top-k, gates, dispatch) from router scores `sc`; the summed
+// scores are also written to logits_out when it is given.
+int run_route(const Plan& p, void* ws, const Scores& sc, float* logits_out, int32_t* idx,
+              float* w, hipStream_t s) {
   {
     Timed t("topk_gate", s);
-    HIP_TRY(moe::launch_topk_gate(logits, p.T, p.E, p.k, p.gating, p.renorm, idx, w,
+    HIP_TRY(moe::launch_topk_gate(sc.lsrc, sc.nsplit, sc.split_stride, sc.bias, logits_out,
+                                  p.T, p.E, p.k, p.gating, p.renorm, idx, w,
                                   at<float>(ws, p.ppart), at<float>(ws, p.hpart),
                                   p.topk_blocks, p.topk_tpb, s));
   }
@@ -377,14 +468,12 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     return MOE_OK;
   }
   void* ws = cfg->workspace;
-  float* logits = at<float>(ws, p.logits);
   int32_t* idx = at<int32_t>(ws, p.idx);
   float* w = at<float>(ws, p.w);
-  {
-    Timed t("router", s);
-    HIP_TRY(moe::launch_router(x, W_gate, cfg->logit_bias, logits, p.T, p.d, p.E, p.bf16, s));
-  }
-  rc = run_route(p, ws, logits, idx, w, s);
+  Scores sc;
+  rc = run_router(p, ws, x, W_gate, cfg->logit_bias, s, &sc);
+  if (rc != MOE_OK) return rc;
+  rc = run_route(p, ws, sc, nullptr, idx, w, s);
   if (rc != MOE_OK) return rc;
 
   const size_t es = p.bf16 ? 2 : 4;
@@ -395,12 +484,13 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.B = W1; g1.B3 = W3; g1.b_stride = dF; g1.group_base = 0; g1.ldb = p.F;
   g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
-  g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E;
-  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles;
+  g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
+  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm;
   // GEMM2 (routed): Y[slot] = H[slot] W2[e]
   moe::GroupedGemm g2 = g1;
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
   g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
+  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
   // the S stacked W2 blocks in one pass (their sum).
@@ -410,11 +500,13 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s1.perm = nullptr; s1.group_base = p.E; s1.ngroups_n = p.S; s1.C = at<void>(ws, p.Hs);
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
     s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);
-    s1.max_mtiles = static_cast<int>((p.T + p.bm - 1) / p.bm);
+    s1.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
+    s1.bm = p.static_bm;
     s2 = s1;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
     s2.b_stride = dF; s2.group_base = p.E; s2.ngroups_n = 1; s2.ldb = p.d;
     s2.K = p.S * p.F; s2.N = p.d; s2.C = at<void>(ws, p.Ys); s2.ldc = p.d; s2.c_group_col = 0;
+    s2.ksplit = p.shared2_split; s2.c_split = p.T * p.d;
   }
   (void)es;
   if (p.bf16) {
@@ -454,9 +546,10 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   }
   {
     Timed t("combine", s);
-    HIP_TRY(moe::launch_combine(at<float>(ws, p.Y), 1, 0, at<int32_t>(ws, p.slot), w,
-                                p.S > 0 ? at<float>(ws, p.Ys) : nullptr, 1, 0, p.T, p.k, p.d,
-                                out, p.bf16, s));
+    HIP_TRY(moe::launch_combine(at<float>(ws, p.Y), p.ffn2_split, p.rows_max * p.d,
+                                at<int32_t>(ws, p.slot), w,
+                                p.S > 0 ? at<float>(ws, p.Ys) : nullptr, p.shared2_split,
+                                p.T * p.d, p.T, p.k, p.d, out, p.bf16, s));
   }
   if (stats) {
     rc = fill_stats(p, ws, s, stats, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount));
@@ -466,14 +559,14 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   return MOE_OK;
 }
 
-static int route_common(const Plan& p, const moe_config_t* cfg, const float* logits,
-                        int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* slot, moe_stats_t* stats) {
+static int route_common(const Plan& p, const moe_config_t* cfg, const Scores& sc,
+                        float* logits_out, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, int32_t* slot, moe_stats_t* stats) {
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   void* ws = cfg->workspace;
   int32_t* idx = topk_idx;
   float* w = topk_w ? topk_w : at<float>(ws, p.w);
-  int rc = run_route(p, ws, logits, idx, w, s);
+  int rc = run_route(p, ws, sc, logits_out, idx, w, s);
   if (rc != MOE_OK) return rc;
   if (counts)
     HIP_TRY(hipMemcpyAsync(counts, at<int32_t>(ws, p.counts), sizeof(int32_t) * p.E,
@@ -510,12 +603,16 @@ int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg, float*
     g_err.clear();
     return MOE_OK;
   }
-  float* lg = logits ? logits : at<float>(cfg->workspace, p.logits);
-  {
-    Timed t("router", s);
-    HIP_TRY(moe::launch_router(x, W_gate, cfg->logit_bias, lg, p.T, p.d, p.E, p.bf16, s));
-  }
-  rc = route_common(p, cfg, lg, topk_idx, topk_w, counts, offsets, perm, slot, stats);
+  Scores sc;
+  rc = run_router(p, cfg->workspace, x, W_gate, cfg->logit_bias, s, &sc);
+  if (rc != MOE_OK) return rc;
+  // the vector router writes finished scores to the workspace; copy them out
+  float* lout = logits;
+  if (logits && !p.mfma_router)
+    HIP_TRY(hipMemcpyAsync(logits, sc.lsrc, sizeof(float) * p.T * p.E,
+                           hipMemcpyDeviceToDevice, s));
+  if (!p.mfma_router) lout = nullptr;
+  rc = route_common(p, cfg, sc, lout, topk_idx, topk_w, counts, offsets, perm, slot, stats);
   if (rc == MOE_OK) g_err.clear();
   return rc;
 }
@@ -537,7 +634,8 @@ int moe_route_logits(const float* logits, const moe_config_t* cfg, int32_t* topk
     g_err.clear();
     return MOE_OK;
   }
-  rc = route_common(p, cfg, logits, topk_idx, topk_w, counts, offsets, perm, slot, stats);
+  rc = route_common(p, cfg, Scores{logits, 1, 0, nullptr}, nullptr, topk_idx, topk_w, counts,
+                    offsets, perm, slot, stats);
   if (rc == MOE_OK) g_err.clear();
   return rc;
 }
@@ -560,9 +658,9 @@ int moe_aux_loss(const float* logits, const int32_t* counts, const moe_config_t*
   void* ws = cfg->workspace;
   {
     Timed t("softmax_stats", s);
-    HIP_TRY(moe::launch_topk_gate(logits, p.T, p.E, 1, p.gating, p.renorm, nullptr, nullptr,
-                                  at<float>(ws, p.ppart), at<float>(ws, p.hpart), p.topk_blocks,
-                                  p.topk_tpb, s));
+    HIP_TRY(moe::launch_topk_gate(logits, 1, 0, nullptr, nullptr, p.T, p.E, 1, p.gating,
+                                  p.renorm, nullptr, nullptr, at<float>(ws, p.ppart),
+                                  at<float>(ws, p.hpart), p.topk_blocks, p.topk_tpb, s));
   }
   {
     Timed t("stats", s);

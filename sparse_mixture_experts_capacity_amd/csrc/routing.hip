@@ -139,8 +139,9 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
 
 template <int V>
 __global__ __launch_bounds__(256) void topk_gate_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k, int G,
-    int gating, int renorm, int tokens_per_block,
+    const float* __restrict__ lpart, int nsplit, int64_t split_stride,
+    const float* __restrict__ bias, float* __restrict__ logits_out, int64_t T,
+    int E, int k, int G, int gating, int renorm, int tokens_per_block,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ Ppart, float* __restrict__ Hpart) {
   __shared__ float pbuf[256 * 4];   // [groups][E], groups*E <= 256*V <= 1024
@@ -157,18 +158,29 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
   const int64_t tb = static_cast<int64_t>(blockIdx.x) * tokens_per_block;
   const int64_t te = min(T, tb + tokens_per_block);
   for (int64_t t = tb + grp; t < te; t += ngroups) {
-    const float* row = logits + t * E;
     float val[V];
     bool taken[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int i = gl + v * G;
-      val[v] = (i < E) ? row[i] : -FLT_MAX;
+      float l = -INFINITY;
+      if (i < E) {
+        l = lpart[t * E + i];
+        for (int q = 1; q < nsplit; ++q) l += lpart[q * split_stride + t * E + i];
+        if (bias) l += bias[i];
+        if (logits_out) logits_out[t * E + i] = l;
+        // A NaN score ranks as -infinity: never ahead of a number, ties by
+        // index, so a valid expert index is always chosen.
+        if (l != l) l = -INFINITY;
+      }
+      val[v] = l;
       taken[v] = !(i < E);
     }
     float m = 0.f;
+    float esum = 0.f;  // sum of e^(l_j - m) over the chosen experts (lane 0)
     for (int j = 0; j < k; ++j) {
-      float bv = -FLT_MAX;
+      // sentinel loses to every real expert, -infinity scores included
+      float bv = -INFINITY;
       int bi = INT_MAX;
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -187,13 +199,19 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
           if (gl + v * G == bi) taken[v] = true;
       }
       if (gl == 0 && topk_idx) topk_idx[t * k + j] = bi;
+      if (gl == 0 && topk_w) {
+        // un-normalised gate e^(l_j - m); scaled below once Z is known
+        const float ej = bv > -INFINITY ? expf(bv - m) : 0.f;
+        topk_w[t * k + j] = ej;
+        esum += ej;
+      }
     }
     // Full softmax over all E experts, shifted by the top score m.
     float ex[V];
     float z = 0.f;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      ex[v] = (gl + v * G < E) ? expf(val[v] - m) : 0.f;
+      ex[v] = (gl + v * G < E && val[v] > -INFINITY) ? expf(val[v] - m) : 0.f;
       z += ex[v];
     }
     for (int off = G >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off, G);
@@ -203,27 +221,17 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
     for (int v = 0; v < V; ++v) {
       const float p = ex[v] * inv_z;
       pacc[v] += p;
-      if (gl + v * G < E) plogp += p * (val[v] - m);
+      if (p > 0.f) plogp += p * (val[v] - m);
     }
     for (int off = G >> 1; off >= 1; off >>= 1) plogp += __shfl_xor(plogp, off, G);
     if (gl == 0) hacc += logf(z) - plogp;
 
-    // Gate weights, written by lane 0 of the group (reads back the chosen
-    // scores; they are in L1).
+    // Gate weights: Mixtral order w_j = e_j / sum_j' e_j; DeepSeek order
+    // w_j = e_j / Z (the full softmax at the chosen expert), or e_j / sum e
+    // when renormalised.  Lane 0 rescales the values it wrote above.
     if (gl == 0 && topk_w) {
-      const int32_t* sel = topk_idx + t * k;
-      if (gating == 0) {
-        float s = 0.f;
-        for (int j = 0; j < k; ++j) s += expf(row[sel[j]] - m);
-        const float inv = 1.0f / s;
-        for (int j = 0; j < k; ++j) topk_w[t * k + j] = expf(row[sel[j]] - m) * inv;
-      } else {
-        float s = 0.f;
-        if (renorm)
-          for (int j = 0; j < k; ++j) s += expf(row[sel[j]] - m) * inv_z;
-        const float inv = renorm ? 1.0f / s : 1.0f;
-        for (int j = 0; j < k; ++j) topk_w[t * k + j] = (expf(row[sel[j]] - m) * inv_z) * inv;
-      }
+      const float scale = (gating == 0 || renorm) ? 1.0f / esum : inv_z;
+      for (int j = 0; j < k; ++j) topk_w[t * k + j] *= scale;
     }
   }
   // Workgroup reduction of the softmax statistics in a fixed order.
@@ -256,21 +264,23 @@ int topk_group_size(int E) {
   return G > 64 ? 64 : G;
 }
 
-hipError_t launch_topk_gate(const float* logits, int64_t T, int E, int k,
-                            int gating, int renorm, int32_t* topk_idx,
+hipError_t launch_topk_gate(const float* lpart, int nsplit, int64_t split_stride,
+                            const float* bias, float* logits_out, int64_t T, int E,
+                            int k, int gating, int renorm, int32_t* topk_idx,
                             float* topk_w, float* Ppart, float* Hpart,
                             int nblocks, int tokens_per_block, hipStream_t s) {
   const int G = topk_group_size(E);
   const int V = (E + G - 1) / G;
+#define MOE_TOPK_ARGS                                                                \
+  lpart, nsplit, split_stride, bias, logits_out, T, E, k, G, gating, renorm,        \
+      tokens_per_block, topk_idx, topk_w, Ppart, Hpart
   if (V <= 1)
-    topk_gate_kernel<1><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
-                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+    topk_gate_kernel<1><<<nblocks, 256, 0, s>>>(MOE_TOPK_ARGS);
   else if (V <= 2)
-    topk_gate_kernel<2><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
-                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+    topk_gate_kernel<2><<<nblocks, 256, 0, s>>>(MOE_TOPK_ARGS);
   else
-    topk_gate_kernel<4><<<nblocks, 256, 0, s>>>(logits, T, E, k, G, gating, renorm,
-                                                tokens_per_block, topk_idx, topk_w, Ppart, Hpart);
+    topk_gate_kernel<4><<<nblocks, 256, 0, s>>>(MOE_TOPK_ARGS);
+#undef MOE_TOPK_ARGS
   return hipGetLastError();
 }
 
@@ -293,8 +303,9 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int it = 0; it < kDispatchChunk / kWave; ++it) {
     const int64_t a = base + it * kWave + lane;
-    const bool valid = a < TK;
-    const int e = valid ? topk_idx[a] : 0;
+    const int ein = a < TK ? topk_idx[a] : -1;
+    const bool valid = ein >= 0 && ein < E;   // ids outside [0, E) are ignored
+    const int e = valid ? ein : 0;
     uint64_t match = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -379,10 +390,14 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int64_t a = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (a >= TK) return;
   const int e = topk_idx[a];
-  const int64_t chunk = a / kDispatchChunk;
-  const int rank = blkbase[chunk * E + e] + lrank[a];
   const int total = offsets[E];
   if (a >= total) perm[a] = -1;
+  if (e < 0 || e >= E) {  // not produced by the top-k pass; never dispatched
+    slot[a] = -1;
+    return;
+  }
+  const int64_t chunk = a / kDispatchChunk;
+  const int rank = blkbase[chunk * E + e] + lrank[a];
   if (rank < C) {
     const int s = offsets[e] + rank;
     slot[a] = s;

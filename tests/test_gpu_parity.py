@@ -72,6 +72,16 @@ def _logits_case(name):
     if name == "tiny_capacity":
         w = Workload("tinycap", T=5000, d=64, F=64, E=8, k=2, capacity_factor=0.01)
         return w, random_logits(w.T, w.E, seed=11) * 3
+    if name == "nan_scores":
+        # NaN scores rank as -infinity; every row keeps at least one number
+        w = Workload("nan", T=500, d=64, F=64, E=8, k=2, capacity_factor=1.0)
+        L = random_logits(w.T, w.E, seed=13)
+        g = torch.Generator().manual_seed(14)
+        mask = torch.rand(w.T, w.E, generator=g) < 0.3
+        mask[:, 0] = False
+        mask[::7, 1:] = True      # rows with a single number
+        L[mask] = float("nan")
+        return w, L
     if name == "deepseek_renorm_k1":
         w = Workload("dsr", T=777, d=64, F=64, E=64, k=1, gating=SOFTMAX_THEN_TOPK,
                      renormalize=True, capacity_factor=1.25)
@@ -81,7 +91,7 @@ def _logits_case(name):
 
 LOGIT_CASES = ["tiny", "prefill", "skew_cf1.0", "skew_cf1.5", "deepseek",
                "ties_signed_zero", "all_equal", "E256_k8", "k_equals_E", "E1", "T1",
-               "tiny_capacity", "deepseek_renorm_k1"]
+               "tiny_capacity", "deepseek_renorm_k1", "nan_scores"]
 
 
 @pytest.mark.parametrize("case", LOGIT_CASES)
@@ -89,8 +99,10 @@ def test_route_logits_bit_exact(case):
     say(f"[route_logits] {case}")
     w, L = _logits_case(case)
     T, E, k = w.T, w.E, w.k
-    # oracle on the same fp32 values, widened exactly
+    # oracle on the same fp32 values, widened exactly (a NaN score ranks as
+    # -infinity in the library; the oracle, which takes numbers only, gets -1e30)
     L64 = L.to(torch.float64).numpy()
+    L64 = np.where(np.isnan(L64), -1e30, L64)
     sel, margin = O.topk_select(L64, k)
     gates = O.gate_weights(L64, sel, w.gating, w.renormalize)
     C = O.capacity(T, k, E, w.capacity_factor)
@@ -197,6 +209,9 @@ FORWARD_CASES = {
                               capacity_factor=1.5),
     "bf16_dense_k_eq_E": Workload("bf16_dense", T=64, d=128, F=128, E=4, k=4),
     "bf16_T1": Workload("bf16_T1", T=1, d=256, F=512, E=8, k=2),
+    # short-batch tiles (32 rows): several tiles per expert, drops, ragged N
+    "bf16_short_tiles": Workload("bf16_short", T=64, d=128, F=192, E=2, k=1,
+                                 capacity_factor=0.9),
 }
 
 
@@ -295,3 +310,29 @@ def test_forward_full_size_sampled(name):
                     "entropy_token"):
             r = ref["stats"][key]
             assert abs(st[key] - r) <= 1e-5 * max(abs(r), 1e-3), (key, st[key], r)
+
+
+# --------------------------------------------------------------------------
+# both FFN paths: grouped (no K split) and streaming (K split as far as
+# possible), every output element
+# --------------------------------------------------------------------------
+PATH_CASES = ["bf16_T1", "bf16_multi_tile", "bf16_deepseek_like", "bf16_skew_drops",
+              "bf16_ragged_n", "bf16_short_tiles"]
+
+
+@pytest.mark.parametrize("path", [moe.PATH_GROUPED, moe.PATH_STREAM], ids=["grouped", "stream"])
+@pytest.mark.parametrize("case", PATH_CASES)
+def test_forward_paths(case, path):
+    w = FORWARD_CASES[case]
+    say(f"[forward path={path}] {case}")
+    run = Run(w)
+    out, st = run.forward(path=path)
+    g_route, _ = run.route()
+    ref = run.oracle()
+    ties, _, _ = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref)
+    ok = comparable_tokens(w, ref, ties, w.T)
+    got = to64(out)
+    good, ratio, excess = output_within_tolerance(got[ok], ref["out"][ok], w)
+    say(f"  ratio {ratio:.2e}, excess over bound {excess:.2e}, near ties {len(ties)}")
+    assert np.all(np.isfinite(got))
+    assert good
