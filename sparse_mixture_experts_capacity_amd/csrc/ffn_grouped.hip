@@ -108,45 +108,61 @@ __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
 // one column that v_mfma_f32_16x16x32_bf16 takes.
 //
 // LDS layouts (no padding; XOR swizzles keep every read conflict-free):
-//   A stage: BM rows x 128 bytes; 16-byte chunk c of row m sits at chunk
-//            c ^ (m & 7) ^ ((m >> 3) & 1).
-//   B stage: BK rows x 512 bytes; 32-byte segment s (16 columns) of row k
+//   A stage: BM rows x 2*BK bytes; 16-byte chunk c of row m is stored at
+//            a_chunk(m, c) (an XOR of c with low bits of m).
+//   B stage: BK rows x 2*BN bytes; 32-byte segment s (16 columns) of row k
 //            sits at segment s ^ ((k & 3) | ((k >> 1) & 4)).
+//
+// The shape is a compile-time configuration: M-tile BM, B-tile width BN
+// (SwiGLU: BN/2 columns each of W1 and W3), K step BK, wavefronts NW (WM
+// along M), NS stages.  Configurations with at most 80 KB of LDS run two
+// workgroups per CU, so one workgroup's barrier, tile set-up and epilogue
+// overlap the other's MFMAs.
 // ===========================================================================
 namespace dma {
 
-constexpr int BN = 256;                  // B-tile columns (SwiGLU: 128 W1 + 128 W3)
-constexpr int BK = 64;
-constexpr int B_STAGE = BK * BN * 2;     // 32 KB
-
-// Two M-tile shapes: 128 rows (2 x 2 wavefronts of 64 x 128, 3-stage ring)
-// for batches with many rows per expert, and 32 rows (1 x 4 wavefronts of
-// 32 x 64, 4-stage ring) for short batches, where each expert has a few rows
-// and the kernel mostly streams weights.
-template <int BM_, int NW_>
+template <int BM_, int BN_, int BK_, int NW_, int WM_, int NS_>
 struct Shape {
-  static constexpr int BM = BM_;
-  static constexpr int NW = NW_;                     // wavefronts per workgroup
-  static constexpr int WM = BM_ >= 128 ? 2 : 1;      // wavefronts along M
-  static constexpr int WN = NW_ / WM;                // wavefronts along N
-  static constexpr int WROWS = BM_ / WM;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, NW = NW_, WM = WM_, NS = NS_;
+  static constexpr int WN = NW / WM;
+  static constexpr int WROWS = BM / WM;
   static constexpr int WCOLS = BN / WN;
   static constexpr int MI = WROWS / 16;              // MFMA tiles per wavefront
   static constexpr int NJ = WCOLS / 16;
-  static constexpr int A_STAGE = BM_ * BK * 2;
+  static constexpr int HALVES = BK / 32;             // 32-deep MFMA steps per stage
+  static constexpr int A_ROW = 2 * BK;               // bytes per A row
+  static constexpr int CA = BK / 8;                  // 16-byte chunks per A row
+  static constexpr int B_ROW = 2 * BN;               // bytes per B row
+  static constexpr int A_STAGE = BM * A_ROW;
+  static constexpr int B_STAGE = BK * B_ROW;
   static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int NS = BM_ >= 128 ? 3 : 4;
-  static constexpr int A_LOADS = BM_ / (8 * NW_);    // per thread per stage
-  static constexpr int B_LOADS = (BK / 2) / NW_;
+  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;   // one 64-lane x 16 B load
+  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
+  static constexpr int A_LOADS = A_STAGE / 1024 / NW;    // per thread per stage
+  static constexpr int B_LOADS = B_STAGE / 1024 / NW;
   static constexpr int LOADS = A_LOADS + B_LOADS;
-  static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && NJ % 2 == 0, "shape");
+  static constexpr int LDS = NS * STAGE;
+  static constexpr int BLOCKS_PER_CU = LDS <= 80 * 1024 ? 2 : 1;
+  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && NJ % 2 == 0 && MI >= 1, "shape");
+  static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "loads");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BN / 16 <= 16 && BN >= 128, "B segments");
+  static_assert(2 * LOADS < 64, "vmcnt");
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ int a_chunk(int m, int c) { return c ^ (m & 7) ^ ((m >> 3) & 1); }
+// Stored position of 16-byte chunk c of A row m.  With 8 chunks per row
+// (BK = 64): c ^ (m & 7) ^ ((m >> 3) & 1); with 4 (BK = 32):
+// c ^ (m & 3) ^ ((m >> 2) & 3).  Either way 16 consecutive rows read at one
+// chunk hit 16 different 16-byte bank groups.
+template <int CA>
+__device__ __forceinline__ int a_chunk(int m, int c) {
+  if constexpr (CA == 8) return c ^ (m & 7) ^ ((m >> 3) & 1);
+  return c ^ (m & 3) ^ ((m >> 2) & 3);
+}
 __device__ __forceinline__ int b_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -169,7 +185,8 @@ template <class S, bool SWIGLU>
 __device__ __forceinline__ int bcol_of(int j, int wn) {
   if constexpr (SWIGLU) {
     constexpr int H = S::NJ / 2;   // first half: W1 columns, second half: W3
-    return (j < H) ? (wn * (S::WCOLS / 2) + j * 16) : (BN / 2 + wn * (S::WCOLS / 2) + (j - H) * 16);
+    return (j < H) ? (wn * (S::WCOLS / 2) + j * 16)
+                   : (S::BN / 2 + wn * (S::WCOLS / 2) + (j - H) * 16);
   }
   return wn * S::WCOLS + j * 16;
 }
@@ -191,12 +208,11 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <bool SWIGLU, int BM_, int NW_>
-__global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGemm p, int ntn,
-                                                                       int nblocks) {
-  using S = Shape<BM_, NW_>;
-  constexpr int BM = S::BM, NS = S::NS, MI = S::MI, NJ = S::NJ;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S::STAGE];
+template <bool SWIGLU, class S>
+__global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma_kernel(
+    GroupedGemm p, int ntn, int nblocks) {
+  constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NS = S::NS, MI = S::MI, NJ = S::NJ;
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
 
   const TileCoords tc = tile_coords<BM>(p, ntn, nblocks);
   if (!tc.valid) return;
@@ -212,27 +228,30 @@ __global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGe
   const int n0 = tc.ntile * NOUT;
 
   // ---- DMA sources ---------------------------------------------------------
-  // A: this wavefront fills rows (wave*A_LOADS + i)*8 .. +7 of a stage, one
-  // instruction per i; lane -> row + lane/8, stored chunk lane%8.  Rows past
-  // the tile's end repeat its first row (results not stored).
+  // A: load i of this wavefront fills rows (wave*A_LOADS + i)*A_ROWS_PER_LOAD
+  // onward; lane -> row + lane/CA, stored chunk lane%CA.  Rows past the
+  // tile's end repeat its first row (their results are not stored).
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* asrc[S::A_LOADS];
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
-    const int r = (wave * S::A_LOADS + i) * 8 + (lane >> 3);
+    const int r = (wave * S::A_LOADS + i) * S::A_ROWS_PER_LOAD + lane / S::CA;
     const int rr = tc.row0 + (r < tc.nrows ? r : 0);
     const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
-    asrc[i] = A + src * p.lda + a_chunk(r, lane & 7) * 8;
+    asrc[i] = A + src * p.lda + a_chunk<S::CA>(r, lane % S::CA) * 8;
   }
-  // B: this wavefront fills rows (wave*B_LOADS + i)*2 + lane/32 of a stage; lane's
-  // stored 16-byte chunk lane%32 is half (lane&1) of segment (lane%32)/2.
-  // Columns past N read column 0 (their outputs are never stored).
+  // B: load i fills rows (wave*B_LOADS + i)*B_ROWS_PER_LOAD onward; lane ->
+  // row + lane/(BN/8), stored 16-byte chunk q = lane%(BN/8), which is half
+  // (q&1) of stored segment q/2.  Columns past N read column 0 (their
+  // outputs are never stored).
+  constexpr int BCH = BN / 8;                 // 16-byte chunks per B row
   const uint16_t* bsrc[S::B_LOADS];
 #pragma unroll
   for (int i = 0; i < S::B_LOADS; ++i) {
-    const int kr = (wave * S::B_LOADS + i) * 2 + (lane >> 5);
-    const int seg = ((lane & 31) >> 1) ^ b_swz(kr);
-    const int n = seg * 16 + (lane & 1) * 8;
+    const int kr = (wave * S::B_LOADS + i) * S::B_ROWS_PER_LOAD + lane / BCH;
+    const int q = lane % BCH;
+    const int seg = (q >> 1) ^ b_swz(kr);
+    const int n = seg * 16 + (q & 1) * 8;
     const uint16_t* base;
     int col;
     if constexpr (SWIGLU) {
@@ -257,11 +276,11 @@ __global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGe
     const int k0 = kbase + step * BK;
 #pragma unroll
     for (int i = 0; i < S::A_LOADS; ++i)
-      dma16(asrc[i] + k0, sb + (wave_u * S::A_LOADS + i) * 8 * 128);
+      dma16(asrc[i] + k0, sb + (wave_u * S::A_LOADS + i) * 1024);
     const int64_t kb = static_cast<int64_t>(k0) * p.ldb;
 #pragma unroll
     for (int i = 0; i < S::B_LOADS; ++i)
-      dma16(bsrc[i] + kb, sb + S::A_STAGE + (wave_u * S::B_LOADS + i) * 2 * 512);
+      dma16(bsrc[i] + kb, sb + S::A_STAGE + (wave_u * S::B_LOADS + i) * 1024);
   };
 
   f32x4 acc[MI][NJ];
@@ -275,52 +294,71 @@ __global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGe
   const int i16 = lane & 15;
   const int tq = i16 >> 2, tr = i16 & 3;
 
-  auto compute = [&](int step) __attribute__((always_inline)) {
+  // One 32-deep half of a stage for this wavefront: MI A fragments
+  // (ds_read_b128) and NJ B fragments (two transposing reads each).
+  struct Frags {
+    bf16x8 a[MI];
+    bf16x8 b[NJ];
+  };
+  auto load_frags = [&](Frags& f, int step, int h) __attribute__((always_inline)) {
     const char* sb = smem + (step % NS) * S::STAGE;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 af[MI];
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int m = wm * S::WROWS + i * 16 + i16;
-        const int c = s * 4 + g;
-        af[i] = *reinterpret_cast<const bf16x8*>(sb + m * 128 + a_chunk(m, c) * 16);
-      }
-      const int k_lo = s * 32 + g * 8 + tq;   // rows of the two transposing reads
-      const int k_hi = k_lo + 4;
-      const int sw_lo = b_swz(k_lo), sw_hi = b_swz(k_hi);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
-        const char* blo = sb + S::A_STAGE + k_lo * 512 + ((sg ^ sw_lo) * 32) + tr * 8;
-        const char* bhi = sb + S::A_STAGE + k_hi * 512 + ((sg ^ sw_hi) * 32) + tr * 8;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
-        const bf16x8 bf = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
-      }
+    for (int i = 0; i < MI; ++i) {
+      const int m = wm * S::WROWS + i * 16 + i16;
+      f.a[i] = *reinterpret_cast<const bf16x8*>(sb + m * S::A_ROW +
+                                                a_chunk<S::CA>(m, h * 4 + g) * 16);
     }
+    const int k_lo = h * 32 + g * 8 + tq;   // rows of the two transposing reads
+    const int k_hi = k_lo + 4;
+    const int sw_lo = b_swz(k_lo), sw_hi = b_swz(k_hi);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
+      const char* blo = sb + S::A_STAGE + k_lo * S::B_ROW + ((sg ^ sw_lo) * 32) + tr * 8;
+      const char* bhi = sb + S::A_STAGE + k_hi * S::B_ROW + ((sg ^ sw_hi) * 32) + tr * 8;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
+      f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mfma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
   // ---- pipeline --------------------------------------------------------------
+  // Step ks: wait until this thread's transfers of stage ks have landed,
+  // barrier (all threads' transfers of stage ks have landed, and every
+  // wavefront is done reading stage ks-1), refill stage ks-1's buffer with
+  // step ks+NS-1, then the MFMAs of stage ks, reading the second half's
+  // fragments while the first half's MFMAs run.
   const int nk = kper / BK;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st);
   for (int ks = 0; ks < nk; ++ks) {
-    // this thread's loads of step ks are done once at most the later issued
-    // stages remain in flight; the barrier then covers every thread's loads
-    // and every wavefront's reads of the stage about to be refilled.
     wait_stages<S::LOADS>(min(NS - 2, nk - 1 - ks));
     // A bare barrier: __syncthreads() adds a release fence that would wait
-    // for every load in flight, the later stages' included.  The LDS reads of
-    // the previous step are complete here (their results fed its MFMAs).
+    // for every transfer in flight, the later stages' included.
     __builtin_amdgcn_s_barrier();
     if (ks + NS - 1 < nk) issue(ks + NS - 1);
-    compute(ks);
+    __builtin_amdgcn_sched_barrier(0);
+    Frags f0;
+    load_frags(f0, ks, 0);
+    if constexpr (S::HALVES == 2) {
+      Frags f1;
+      load_frags(f1, ks, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(f0);
+      mfma(f1);
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(f0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -361,6 +399,16 @@ __global__ __launch_bounds__(64 * NW_, 1) void grouped_bf16_dma_kernel(GroupedGe
     }
   }
 }
+
+// Shapes in use (the host picks one per GEMM through GroupedGemm::shape):
+//   0: 32-row M-tiles for short batches; 4-stage ring, one workgroup per CU.
+//   1: 128 x 256 x 32, 8 wavefronts, 3 stages (72 KB): two workgroups per CU
+//      (4 wavefronts per SIMD); best when experts have many rows.
+//   2: 128 x 256 x 64, 8 wavefronts, 3 stages (144 KB): one workgroup per
+//      CU; best for a few hundred rows per expert (fine-grained experts).
+using ShapeShort = Shape<32, 256, 64, 4, 1, 4>;
+using ShapeLongA = Shape<128, 256, 32, 8, 2, 3>;
+using ShapeLongB = Shape<128, 256, 64, 8, 2, 3>;
 
 }  // namespace dma
 
@@ -473,20 +521,22 @@ hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, 
 
 }  // namespace
 
-#ifndef MOE_GEMM_WAVES_LONG
-#define MOE_GEMM_WAVES_LONG 8
-#endif
+template <bool SWIGLU, class S>
+hipError_t launch_bf16_shape(const GroupedGemm& g, hipStream_t s) {
+  const int cols = SWIGLU ? S::BN / 2 : S::BN;
+  return launch_grid(dma::grouped_bf16_dma_kernel<SWIGLU, S>, g, (g.N + cols - 1) / cols, s, S::NW);
+}
+template <bool SWIGLU>
+hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
+  if (g.bm == 32) return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
+  if (g.shape == 2) return launch_bf16_shape<SWIGLU, dma::ShapeLongB>(g, s);
+  return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
+}
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s) {
-  const int ntn = (g.N + dma::BN / 2 - 1) / (dma::BN / 2);
-  if (g.bm == 32) return launch_grid(dma::grouped_bf16_dma_kernel<true, 32, 4>, g, ntn, s, 4);
-  return launch_grid(dma::grouped_bf16_dma_kernel<true, 128, MOE_GEMM_WAVES_LONG>, g, ntn, s,
-                     MOE_GEMM_WAVES_LONG);
+  return launch_bf16<true>(g, s);
 }
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s) {
-  const int ntn = (g.N + dma::BN - 1) / dma::BN;
-  if (g.bm == 32) return launch_grid(dma::grouped_bf16_dma_kernel<false, 32, 4>, g, ntn, s, 4);
-  return launch_grid(dma::grouped_bf16_dma_kernel<false, 128, MOE_GEMM_WAVES_LONG>, g, ntn, s,
-                     MOE_GEMM_WAVES_LONG);
+  return launch_bf16<false>(g, s);
 }
 hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s) {
   return launch_grid(grouped_f32_kernel<true>, g, (g.N + FBN - 1) / FBN, s);

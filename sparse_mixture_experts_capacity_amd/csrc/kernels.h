@@ -55,6 +55,7 @@ struct GroupedGemm {
   int static_rows;          // rows when tiles == null
   int max_mtiles;           // upper bound of M-tiles
   int bm;                   // M-tile rows (bf16: 128 or 32; fp32: 64); tiles match it
+  int shape;                // bf16 with bm 128: 1 = two workgroups per CU, 2 = one
   int ksplit;               // K is split in this many parts (plain fp32 output only);
   int64_t c_split;          // part p writes C + p * c_split (fp32 partial sums)
 };

@@ -110,6 +110,7 @@ struct Plan {
   int bm = 0;                    // M-tile of the grouped kernels
   int max_mtiles = 0;
   int static_bm = 0;             // M-tile of the GEMMs over all T token rows
+  int routed_shape = 1;          // kernel shape of the routed GEMMs (bm 128)
   bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
@@ -251,6 +252,9 @@ int make_plan(const moe_config_t* c, Plan* p) {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
     const bool short_rows = hit > 0 && p->TK <= 48 * hit;
     p->bm = short_rows ? moe::kGroupedBMShort : moe::kGroupedBM;
+    // Many rows per expert: two workgroups per CU hide barriers and tile
+    // set-up; a few hundred: the deeper one-workgroup pipeline wins.
+    p->routed_shape = (hit > 0 && p->TK >= 384 * hit) ? 1 : 2;
     p->static_bm = p->T <= 64 ? moe::kGroupedBMShort : moe::kGroupedBM;
   } else {
     p->bm = p->static_bm = moe::kF32BM;
@@ -354,7 +358,7 @@ int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
     r.c_group_col = 0; r.tiles = nullptr; r.ntiles = nullptr; r.tstart = nullptr;
     r.n_experts = 1; r.static_rows = static_cast<int>(p.T);
     r.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
-    r.bm = p.static_bm;
+    r.bm = p.static_bm; r.shape = 1;
     r.ksplit = p.router_split; r.c_split = p.T * p.E;
     Timed t("router", s);
     HIP_TRY(moe::launch_grouped_plain_bf16(r, s));
@@ -485,7 +489,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
   g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
-  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm;
+  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm; g1.shape = p.routed_shape;
   // GEMM2 (routed): Y[slot] = H[slot] W2[e]
   moe::GroupedGemm g2 = g1;
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
@@ -501,7 +505,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
     s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);
     s1.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
-    s1.bm = p.static_bm;
+    s1.bm = p.static_bm; s1.shape = 1;
     s2 = s1;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
     s2.b_stride = dF; s2.group_base = p.E; s2.ngroups_n = 1; s2.ldb = p.d;

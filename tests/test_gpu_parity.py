@@ -209,6 +209,9 @@ FORWARD_CASES = {
                               capacity_factor=1.5),
     "bf16_dense_k_eq_E": Workload("bf16_dense", T=64, d=128, F=128, E=4, k=4),
     "bf16_T1": Workload("bf16_T1", T=1, d=256, F=512, E=8, k=2),
+    # >= 384 rows per expert: the two-workgroups-per-CU kernel shape
+    "bf16_long_rows": Workload("bf16_long", T=1600, d=128, F=320, E=4, k=1,
+                               capacity_factor=1.25),
     # short-batch tiles (32 rows): several tiles per expert, drops, ragged N
     "bf16_short_tiles": Workload("bf16_short", T=64, d=128, F=192, E=2, k=1,
                                  capacity_factor=0.9),
@@ -317,7 +320,7 @@ def test_forward_full_size_sampled(name):
 # possible), every output element
 # --------------------------------------------------------------------------
 PATH_CASES = ["bf16_T1", "bf16_multi_tile", "bf16_deepseek_like", "bf16_skew_drops",
-              "bf16_ragged_n", "bf16_short_tiles"]
+              "bf16_ragged_n", "bf16_short_tiles", "bf16_long_rows"]
 
 
 @pytest.mark.parametrize("path", [moe.PATH_GROUPED, moe.PATH_STREAM], ids=["grouped", "stream"])
