@@ -9,14 +9,22 @@
 // M-tiles come from a device-side tile list, so the host never reads the
 // routing back.
 //
-// bf16 path: v_mfma_f32_16x16x32_bf16 on 128 x 256 workgroup tiles, K step 64,
-// 4 wavefronts (2 x 2), each a 64 x 128 sub-tile (4 x 8 MFMA tiles, fp32
-// accumulators).  Weights are stored [K, N] with N contiguous, while the MFMA
-// B operand wants 8 consecutive k per lane; each thread therefore loads an
-// 8 (k) x 8 (n) block with 16-byte loads and transposes it in registers before
-// writing k-contiguous rows to LDS.  Token rows are gathered through the
-// dispatch permutation as 16-byte chunks.  LDS is double buffered and the
-// next K step is prefetched into registers while the MFMAs run.
+// bf16 path: v_mfma_f32_16x16x32_bf16 with fp32 accumulators in VGPRs.  Both
+// operands go from global memory straight into LDS with global_load_lds_dwordx4
+// (no staging registers, no LDS store instructions) through a ring of NS
+// K-steps, NS - 1 of them in flight while the current one is multiplied.
+// Token rows are gathered through the dispatch permutation as 16-byte chunks.
+// Weights stay in LDS as stored, [K][N] with N contiguous; the B fragments
+// (8 consecutive k of one column per lane) are read with ds_read_b64_tr_b16,
+// which transposes 4 x 4 blocks of 16-bit values across each 16-lane group.
+// Both tiles use XOR swizzles instead of padding so the DMA rows stay dense
+// and the fragment reads are free of bank conflicts.  Tile shapes:
+//   128 x 256, K step 32, 8 wavefronts, 3 stages, 72 KB: two workgroups per
+//     CU, for experts with many rows (prefill);
+//   128 x 256, K step 64, 8 wavefronts, 3 stages, 144 KB: one workgroup per
+//     CU, for a few hundred rows per expert;
+//   32 x 256, K step 64, 4 wavefronts, 4 stages: short batches (decode), where
+//     the weights stream once and K may be split over several workgroups.
 //
 // SwiGLU epilogue: a tile's 256 B columns are 128 W1 columns followed by the
 // same 128 W3 columns, and each wavefront owns matching halves, so u and v of

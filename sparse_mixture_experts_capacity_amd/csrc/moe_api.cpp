@@ -480,7 +480,6 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   rc = run_route(p, ws, sc, nullptr, idx, w, s);
   if (rc != MOE_OK) return rc;
 
-  const size_t es = p.bf16 ? 2 : 4;
   const int64_t dF = static_cast<int64_t>(p.d) * p.F;
   // GEMM1 (routed): H[slot] = silu(x[token] W1[e]) * (x[token] W3[e])
   moe::GroupedGemm g1{};
@@ -512,7 +511,6 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s2.K = p.S * p.F; s2.N = p.d; s2.C = at<void>(ws, p.Ys); s2.ldc = p.d; s2.c_group_col = 0;
     s2.ksplit = p.shared2_split; s2.c_split = p.T * p.d;
   }
-  (void)es;
   if (p.bf16) {
     {
       Timed t("ffn1_swiglu", s);
