@@ -24,6 +24,28 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
+# HBM-side bytes per launch of the dominant kernel, from two rocprofv3 --pmc
+# runs (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for
+# a 1 GiB device copy in the same run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 on
+# MI355X).  Keyed by workload and by a digest of the library's kernel sources:
+# once a source changes, the figure no longer describes the kernel and the
+# bench reports null.
+MEASURED_TRAFFIC = {
+    # workload: (source digest, fetch bytes, write bytes)
+}
+SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "combine.hip", "moe_api.cpp", "common.h",
+                "kernels.h")
+
+
+def source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "sparse_mixture_experts_capacity_amd", "csrc")
+    for f in SOURCE_FILES:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -52,8 +74,10 @@ def algorithmic_work(w, kept: int, hit_experts: int):
     io_bytes = es * (2 * w.T * w.d + w.d * w.E)
     gemm1_flops = 2 * w.d * 2 * w.F * kept
     gemm1_bytes = es * 2 * w.d * w.F * hit_experts
+    # token rows read (each kept assignment once) and hidden rows written
+    gemm1_io_bytes = es * kept * (w.d + w.F)
     return dict(flops=flops, bytes=weight_bytes + io_bytes, gemm1_flops=gemm1_flops,
-                gemm1_bytes=gemm1_bytes)
+                gemm1_bytes=gemm1_bytes, gemm1_io_bytes=gemm1_io_bytes)
 
 
 def cpu_baseline(w, inp, n_tokens: int):
@@ -153,22 +177,28 @@ def main():
     per_kernel = {name: dict(launches=n, avg_ms=tot / max(n, 1) if n else 0.0)
                   for name, (n, tot) in kern.items()}
     decode = w.T <= 64
-    if decode:
-        dom = "ffn1_swiglu_stream" if "ffn1_swiglu_stream" in per_kernel else "ffn1_swiglu"
-    else:
-        dom = "ffn1_swiglu" if w.dtype == "bf16" else "ffn1_swiglu_f32"
+    # the routed SwiGLU GEMM (W1 and W3 of every hit expert) dominates every workload
+    dom = "ffn1_swiglu"
     dom_ms = per_kernel.get(dom, {}).get("avg_ms", float("nan"))
+    digest = source_digest()
+    meas = MEASURED_TRAFFIC.get(w.name)
+    traffic = None
+    if meas is not None and meas[0] == digest:
+        traffic = meas[1] + meas[2]
     if decode:
         achieved = work["gemm1_bytes"] / (dom_ms * 1e-3) / 1e9
         roof = dict(kernel=dom, bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS,
-                    unit="GB/s", frac=achieved / PEAK_HBM_GBS, traffic=None,
+                    unit="GB/s", frac=achieved / PEAK_HBM_GBS, traffic=traffic,
                     per_launch=f"{work['gemm1_bytes']} bytes (W1+W3 of {hit} hit experts)")
     else:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = work["gemm1_flops"] / (dom_ms * 1e-3) / 1e12
         roof = dict(kernel=dom, bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
-                    frac=achieved / peak, traffic=None,
+                    frac=achieved / peak, traffic=traffic,
                     per_launch=f"{work['gemm1_flops']} flops (2*d*2F per kept row, {kept} rows)")
+    roof["algorithmic_bytes"] = work["gemm1_bytes"] + work["gemm1_io_bytes"]
+    roof["traffic_unit"] = "bytes per launch (HBM side, counters)"
+    roof["source_digest"] = digest
     layer_tflops = work["flops"] / (ms * 1e-3) / 1e12
     layer_gbs = work["bytes"] / (ms * 1e-3) / 1e9
     res = {

@@ -277,8 +277,11 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   // (wave-uniform: M0 takes it).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
-  const int kper = p.K / p.ksplit;           // this block's share of K
-  const int kbase = tc.kpart * kper;
+  // This block's share of K: part kpart of ksplit near-equal runs of BK steps.
+  const int nk_all = p.K / BK;
+  const int kb0 = static_cast<int>(static_cast<int64_t>(tc.kpart) * nk_all / p.ksplit);
+  const int kb1 = static_cast<int>(static_cast<int64_t>(tc.kpart + 1) * nk_all / p.ksplit);
+  const int kbase = kb0 * BK;
   auto issue = [&](int step) __attribute__((always_inline)) {
     const uint32_t sb = lds0 + (step % NS) * S::STAGE;
     const int k0 = kbase + step * BK;
@@ -343,7 +346,12 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   // wavefront is done reading stage ks-1), refill stage ks-1's buffer with
   // step ks+NS-1, then the MFMAs of stage ks, reading the second half's
   // fragments while the first half's MFMAs run.
-  const int nk = kper / BK;
+  // A wavefront whose rows all lie past the tile's end (the last, short
+  // M-tile of an expert) keeps loading and meeting the barriers but skips
+  // its fragment reads and MFMAs.
+  const bool wactive =
+      (S::WM == 1) || (__builtin_amdgcn_readfirstlane(wm) * S::WROWS < tc.nrows);
+  const int nk = kb1 - kb0;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) issue(st);
@@ -354,17 +362,19 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     __builtin_amdgcn_s_barrier();
     if (ks + NS - 1 < nk) issue(ks + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
-    Frags f0;
-    load_frags(f0, ks, 0);
-    if constexpr (S::HALVES == 2) {
-      Frags f1;
-      load_frags(f1, ks, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma(f0);
-      mfma(f1);
-    } else {
-      __builtin_amdgcn_sched_barrier(0);
-      mfma(f0);
+    if (wactive) {
+      Frags f0;
+      load_frags(f0, ks, 0);
+      if constexpr (S::HALVES == 2) {
+        Frags f1;
+        load_frags(f1, ks, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(f0);
+        mfma(f1);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(f0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -201,7 +201,8 @@ int check(const moe_config_t* c) {
 
 // K parts for a GEMM with `tiles` output tiles and `ksteps` 64-deep K
 // steps: enough for ~512 workgroups (more than 1 only when the tiles alone
-// give fewer than 256), a divisor of ksteps.
+// give fewer than 256).  The kernels split K into near-equal runs of steps,
+// so the count need not divide ksteps.
 int split_for(int64_t tiles, int ksteps, bool force) {
   if (tiles <= 0) return 1;
   if (!force && tiles >= 256) return 1;
@@ -209,7 +210,6 @@ int split_for(int64_t tiles, int ksteps, bool force) {
   if (ks > ksteps) ks = ksteps;
   if (ks > 64) ks = 64;
   if (ks < 1) ks = 1;
-  while (ksteps % ks) --ks;
   return static_cast<int>(ks);
 }
 
