@@ -34,6 +34,8 @@
 // The XCD-aware block order keeps consecutive logical tiles on one XCD; the
 // logical order runs M-tiles fastest, so the M-tiles sharing a weight tile
 // run together on one XCD and read it from HBM once.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -238,16 +240,26 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   // ---- DMA sources ---------------------------------------------------------
   // A: load i of this wavefront fills rows (wave*A_LOADS + i)*A_ROWS_PER_LOAD
   // onward; lane -> row + lane/CA, stored chunk lane%CA.  Rows past the
-  // tile's end repeat its first row (their results are not stored).
+  // tile's end repeat its first row (their results are not stored).  In the
+  // K-blocked layout (a_block_rows = R > 0) element (row, k) sits at
+  // ((k / 32) * R + row) * 32 + k % 32, so one K step of a tile's rows is a
+  // contiguous run of memory.
   const uint16_t* A = static_cast<const uint16_t*>(p.A);
   const uint16_t* asrc[S::A_LOADS];
 #pragma unroll
   for (int i = 0; i < S::A_LOADS; ++i) {
     const int r = (wave * S::A_LOADS + i) * S::A_ROWS_PER_LOAD + lane / S::CA;
     const int rr = tc.row0 + (r < tc.nrows ? r : 0);
-    const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
-    asrc[i] = A + src * p.lda + a_chunk<S::CA>(r, lane % S::CA) * 8;
+    const int sc = a_chunk<S::CA>(r, lane % S::CA) * 8;   // source column in the step
+    if (p.a_block_rows > 0) {
+      asrc[i] = A + ((sc >> 5) * p.a_block_rows + rr) * 32 + (sc & 31);
+    } else {
+      const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
+      asrc[i] = A + src * p.lda + sc;
+    }
   }
+  // element offset of K step k0 along A (a multiple of 32)
+  const int64_t a_kstride = p.a_block_rows > 0 ? p.a_block_rows : 1;
   // B: load i fills rows (wave*B_LOADS + i)*B_ROWS_PER_LOAD onward; lane ->
   // row + lane/(BN/8), stored 16-byte chunk q = lane%(BN/8), which is half
   // (q&1) of stored segment q/2.  Columns past N read column 0 (their
@@ -287,7 +299,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     const int k0 = kbase + step * BK;
 #pragma unroll
     for (int i = 0; i < S::A_LOADS; ++i)
-      dma16(asrc[i] + k0, sb + (wave_u * S::A_LOADS + i) * 1024);
+      dma16(asrc[i] + k0 * a_kstride, sb + (wave_u * S::A_LOADS + i) * 1024);
     const int64_t kb = static_cast<int64_t>(k0) * p.ldb;
 #pragma unroll
     for (int i = 0; i < S::B_LOADS; ++i)
@@ -390,12 +402,18 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
       for (int r = 0; r < 4; ++r) {
         const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
         if (rl >= tc.nrows) continue;
-        uint16_t* hrow = H + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
+        const int64_t row = tc.row0 + rl;
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
           const int col = n0 + wn * (S::WCOLS / 2) + j * 16 + (lane & 15);
-          if (col < p.N)
-            hrow[col] = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+          if (col < p.N) {
+            const uint16_t h = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+            const int64_t c = cgo + col;
+            if (p.c_block_rows > 0)
+              H[((c >> 5) * p.c_block_rows + row) * 32 + (c & 31)] = h;
+            else
+              H[row * p.ldc + c] = h;
+          }
         }
       }
     }
@@ -528,6 +546,28 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(GroupedGemm p, int ntn
   }
 }
 
+// Token rows of the kept assignments, in slot order and K-blocked:
+// Xb[((k / 32) * R + s) * 32 + k % 32] = x[perm[s] / topk][k] for slots
+// s < offsets[E].  Each thread moves 16 bytes; consecutive threads write
+// consecutive memory.
+__global__ __launch_bounds__(256) void gather_blocked_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const int32_t* __restrict__ perm, int topk,
+    const int32_t* __restrict__ nrows_dev, int64_t R, int d, uint16_t* __restrict__ Xb) {
+  const int64_t n = R * (d / 8);
+  const int64_t total = *nrows_dev;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t kb = t / (R * 4);
+    const int64_t rem = t - kb * R * 4;
+    const int64_t sl = rem >> 2;
+    const int c = static_cast<int>(rem & 3);
+    if (sl >= total) continue;
+    const int64_t tok = perm[sl] / topk;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(x + tok * ldx + kb * 32 + c * 8);
+    *reinterpret_cast<u32x4*>(Xb + (kb * R + sl) * 32 + c * 8) = v;
+  }
+}
+
 template <typename Kern>
 hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, int waves = 4) {
   const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n * g.ksplit;
@@ -549,6 +589,17 @@ hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
   if (g.bm == 32) return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
   if (g.shape == 2) return launch_bf16_shape<SWIGLU, dma::ShapeLongB>(g, s);
   return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
+}
+hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm, int topk,
+                                 const int32_t* nrows_dev, int64_t R, int d, void* Xb,
+                                 hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  const int64_t n = R * (d / 8);
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 32);
+  gather_blocked_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+      static_cast<const uint16_t*>(x), ldx, perm, topk, nrows_dev, R, d,
+      static_cast<uint16_t*>(Xb));
+  return hipGetLastError();
 }
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s) {
   return launch_bf16<true>(g, s);

@@ -58,7 +58,16 @@ struct GroupedGemm {
   int shape;                // bf16 with bm 128: 1 = two workgroups per CU, 2 = one
   int ksplit;               // K is split in this many parts (plain fp32 output only);
   int64_t c_split;          // part p writes C + p * c_split (fp32 partial sums)
+  // K-blocked layouts (bf16 kernels): element (row, k) of a matrix with R
+  // rows at ((k / 32) * R + row) * 32 + k % 32.  0 = row-major.
+  int64_t a_block_rows;     // A (then perm and lda are not used)
+  int64_t c_block_rows;     // SwiGLU output H
 };
+// Xb = kept token rows x[perm[s] / topk] for slots s < *nrows_dev, K-blocked
+// with R rows.
+hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm, int topk,
+                                 const int32_t* nrows_dev, int64_t R, int d, void* Xb,
+                                 hipStream_t s);
 constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels, long batches
 constexpr int kGroupedBMShort = 32;  // M-tile for short batches (few rows per expert)
 constexpr int kF32BM = 64;        // M-tile of the fp32 kernels

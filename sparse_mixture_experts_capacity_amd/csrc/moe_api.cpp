@@ -115,9 +115,11 @@ struct Plan {
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
+  bool blocked = false;          // GEMM1 writes H K-blocked; GEMM2 reads it so
+  bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
   // workspace regions
   Region logits, lpart, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
-      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys;
+      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb;
   size_t total = 0;
 };
 
@@ -260,6 +262,18 @@ int make_plan(const moe_config_t* c, Plan* p) {
     p->bm = p->static_bm = moe::kF32BM;
   }
   p->max_mtiles = static_cast<int>(p->rows_max / p->bm + p->E);
+  // Long batches: GEMM1 writes H K-blocked, so each K step of a GEMM2 tile
+  // reads one contiguous run of memory instead of 64-byte pieces of rows.
+  // With the 32-deep K step and up to ~1.5k rows per expert, the kept token
+  // rows are likewise first gathered into a slot-ordered K-blocked copy for
+  // GEMM1 (with the 64-deep step a row piece is already a whole 128-byte
+  // line; with many more rows the copy costs more than it saves).  Short
+  // batches read the few rows directly.
+  p->blocked = p->bf16 && p->bm != moe::kGroupedBMShort;
+  {
+    const int64_t hit = p->TK < p->E ? p->TK : p->E;
+    p->gather_x = p->blocked && p->routed_shape == 1 && p->TK <= 1536 * hit;
+  }
   // Router scores x W_gate on the MFMA GEMM when the weight rows are 16-byte
   // aligned; K is split so that even short batches give ~512 workgroups, and
   // the top-k pass adds the parts in a fixed order.
@@ -312,6 +326,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->Hs, es * p->T * p->S * p->F, cur);
   add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
   add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
+  add(p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur);
   p->total = cur;
   return MOE_OK;
 }
@@ -489,23 +504,35 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
   g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
   g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm; g1.shape = p.routed_shape;
+  if (p.gather_x) {
+    Timed t("gather", s);
+    HIP_TRY(moe::launch_gather_blocked(x, p.d, at<int32_t>(ws, p.perm), p.k,
+                                       at<int32_t>(ws, p.offsets) + p.E, p.rows_max, p.d,
+                                       at<void>(ws, p.Xb), s));
+    g1.A = at<void>(ws, p.Xb); g1.perm = nullptr; g1.a_block_rows = p.rows_max;
+  }
+  if (p.blocked) g1.c_block_rows = p.rows_max;
   // GEMM2 (routed): Y[slot] = H[slot] W2[e]
   moe::GroupedGemm g2 = g1;
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
   g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
   g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
+  g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
+  g2.c_block_rows = 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
   // the S stacked W2 blocks in one pass (their sum).
   moe::GroupedGemm s1{}, s2{};
   if (p.S > 0) {
     s1 = g1;
+    s1.A = x; s1.a_block_rows = 0; s1.c_block_rows = p.blocked ? p.T : 0;
     s1.perm = nullptr; s1.group_base = p.E; s1.ngroups_n = p.S; s1.C = at<void>(ws, p.Hs);
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
     s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);
     s1.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
     s1.bm = p.static_bm; s1.shape = 1;
     s2 = s1;
+    s2.a_block_rows = s1.c_block_rows; s2.c_block_rows = 0;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
     s2.b_stride = dF; s2.group_base = p.E; s2.ngroups_n = 1; s2.ldb = p.d;
     s2.K = p.S * p.F; s2.N = p.d; s2.C = at<void>(ws, p.Ys); s2.ldc = p.d; s2.c_group_col = 0;

@@ -215,6 +215,17 @@ FORWARD_CASES = {
     # short-batch tiles (32 rows): several tiles per expert, drops, ragged N
     "bf16_short_tiles": Workload("bf16_short", T=64, d=128, F=192, E=2, k=1,
                                  capacity_factor=0.9),
+    # token rows gathered into the K-blocked copy, hidden rows K-blocked, with
+    # a shared expert (its hidden rows K-blocked too) and ragged last M-tiles
+    "bf16_long_rows_shared": Workload("bf16_long_sh", T=1600, d=192, F=320, E=4, k=1,
+                                      S=1, capacity_factor=1.25),
+    # a few hundred rows per expert: 64-deep K steps, token rows read in place,
+    # hidden rows K-blocked; shared experts
+    "bf16_mid_rows_shared": Workload("bf16_mid_sh", T=512, d=128, F=192, E=4, k=2, S=2,
+                                     capacity_factor=1.25),
+    # over 1.5k rows per expert: token rows read in place, hidden rows K-blocked
+    "bf16_many_rows": Workload("bf16_many", T=4096, d=128, F=128, E=2, k=1,
+                               capacity_factor=1.0),
 }
 
 
