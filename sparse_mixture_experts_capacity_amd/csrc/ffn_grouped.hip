@@ -294,8 +294,9 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   const int kb0 = static_cast<int>(static_cast<int64_t>(tc.kpart) * nk_all / p.ksplit);
   const int kb1 = static_cast<int>(static_cast<int64_t>(tc.kpart + 1) * nk_all / p.ksplit);
   const int kbase = kb0 * BK;
-  auto issue = [&](int step) __attribute__((always_inline)) {
-    const uint32_t sb = lds0 + (step % NS) * S::STAGE;
+  // step: K step to load; stage: its ring slot (step % NS).
+  auto issue = [&](int step, int stage) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + stage * S::STAGE;
     const int k0 = kbase + step * BK;
 #pragma unroll
     for (int i = 0; i < S::A_LOADS; ++i)
@@ -323,8 +324,8 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     bf16x8 a[MI];
     bf16x8 b[NJ];
   };
-  auto load_frags = [&](Frags& f, int step, int h) __attribute__((always_inline)) {
-    const char* sb = smem + (step % NS) * S::STAGE;
+  auto load_frags = [&](Frags& f, int stage, int h) __attribute__((always_inline)) {
+    const char* sb = smem + stage * S::STAGE;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = wm * S::WROWS + i * 16 + i16;
@@ -366,20 +367,22 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   const int nk = kb1 - kb0;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) issue(st);
-  for (int ks = 0; ks < nk; ++ks) {
+    if (st < nk) issue(st, st);
+  // One K step held in ring slot `stage` (a constant in the unrolled loop
+  // below, so every LDS address of the step is a fixed offset).
+  auto step_body = [&](int ks, int stage) __attribute__((always_inline)) {
     wait_stages<S::LOADS>(min(NS - 2, nk - 1 - ks));
     // A bare barrier: __syncthreads() adds a release fence that would wait
     // for every transfer in flight, the later stages' included.
     __builtin_amdgcn_s_barrier();
-    if (ks + NS - 1 < nk) issue(ks + NS - 1);
+    if (ks + NS - 1 < nk) issue(ks + NS - 1, stage == 0 ? NS - 1 : stage - 1);
     __builtin_amdgcn_sched_barrier(0);
     if (wactive) {
       Frags f0;
-      load_frags(f0, ks, 0);
+      load_frags(f0, stage, 0);
       if constexpr (S::HALVES == 2) {
         Frags f1;
-        load_frags(f1, ks, 1);
+        load_frags(f1, stage, 1);
         __builtin_amdgcn_sched_barrier(0);
         mfma(f0);
         mfma(f1);
@@ -389,7 +392,15 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  int ks = 0;
+  for (; ks + NS <= nk; ks += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step_body(ks + u, u);
   }
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (ks + u < nk) step_body(ks + u, u);
 
   // ---- epilogue -----------------------------------------------------------
   // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.

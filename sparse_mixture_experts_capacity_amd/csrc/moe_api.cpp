@@ -297,6 +297,9 @@ int make_plan(const moe_config_t* c, Plan* p) {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
     const int64_t mt_est = p->rows_max / p->bm + hit;
     p->ffn2_split = split_for(mt_est * ntn2, p->F / 64, p->path == MOE_PATH_STREAM);
+#ifdef MOE_EXP_SPLIT2
+    if (p->bm != moe::kGroupedBMShort) p->ffn2_split = MOE_EXP_SPLIT2;
+#endif
     if (p->S > 0) {
       const int64_t mts = (p->T + p->static_bm - 1) / p->static_bm;
       p->shared2_split = split_for(mts * ntn2, p->S * p->F / 64, p->path == MOE_PATH_STREAM);
@@ -518,6 +521,9 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
   g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
+#ifdef MOE_EXP_G2SHAPE
+  g2.shape = MOE_EXP_G2SHAPE;
+#endif
   g2.c_block_rows = 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
