@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -89,6 +90,25 @@ class Timed {
 
 // ----------------------------------------------------------------- plan
 constexpr size_t kAlign = 256;
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Region {
@@ -297,9 +317,15 @@ int make_plan(const moe_config_t* c, Plan* p) {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
     const int64_t mt_est = p->rows_max / p->bm + hit;
     p->ffn2_split = split_for(mt_est * ntn2, p->F / 64, p->path == MOE_PATH_STREAM);
-#ifdef MOE_EXP_SPLIT2
-    if (p->bm != moe::kGroupedBMShort) p->ffn2_split = MOE_EXP_SPLIT2;
-#endif
+    // Long batches whose down-projection tiles fill one whole round of
+    // resident workgroups and then a last round less than half full (e.g.
+    // 592 tiles on 512 slots): two K parts turn that into fuller rounds.
+    if (p->path == MOE_PATH_AUTO && p->ffn2_split == 1 && p->bm != moe::kGroupedBMShort) {
+      const int64_t slots = static_cast<int64_t>(device_cus()) * (p->routed_shape == 1 ? 2 : 1);
+      const int64_t t = mt_est * ntn2;
+      if (slots > 0 && t > slots && t < 4 * slots && (t % slots) != 0 && (t % slots) <= slots / 2)
+        p->ffn2_split = 2;
+    }
     if (p->S > 0) {
       const int64_t mts = (p->T + p->static_bm - 1) / p->static_bm;
       p->shared2_split = split_for(mts * ntn2, p->S * p->F / 64, p->path == MOE_PATH_STREAM);
@@ -521,9 +547,6 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
   g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
-#ifdef MOE_EXP_G2SHAPE
-  g2.shape = MOE_EXP_G2SHAPE;
-#endif
   g2.c_block_rows = 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
