@@ -35,6 +35,7 @@
 // logical order runs M-tiles fastest, so the M-tiles sharing a weight tile
 // run together on one XCD and read it from HBM once.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -158,7 +159,7 @@ struct Shape {
   static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "loads");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(BN / 16 <= 16 && BN >= 128, "B segments");
-  static_assert(2 * LOADS < 64, "vmcnt");
+  static_assert(3 * LOADS < 64, "vmcnt");
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -188,6 +189,22 @@ __device__ __forceinline__ void wait_stages(int later) {
   if (later >= 2) wait_vmcnt<2 * LOADS>();
   else if (later == 1) wait_vmcnt<LOADS>();
   else wait_vmcnt<0>();
+}
+
+// s_waitcnt: at most N vector-memory operations and no LDS operation of this
+// wavefront still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+// ... until at most `later` (0..3) stages of LOADS transfers each remain.
+template <int LOADS>
+__device__ __forceinline__ void wait_stages_lgkm0(int later) {
+  if (later >= 3) wait_vmcnt_lgkm0<3 * LOADS>();
+  else if (later == 2) wait_vmcnt_lgkm0<2 * LOADS>();
+  else if (later == 1) wait_vmcnt_lgkm0<LOADS>();
+  else wait_vmcnt_lgkm0<0>();
 }
 
 // First B-tile column of MFMA tile j of wavefront column wn.
@@ -324,41 +341,64 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     bf16x8 a[MI];
     bf16x8 b[NJ];
   };
-  auto load_frags = [&](Frags& f, int stage, int h) __attribute__((always_inline)) {
+  auto rd_a = [&](int stage, int h, int i) __attribute__((always_inline)) -> bf16x8 {
     const char* sb = smem + stage * S::STAGE;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int m = wm * S::WROWS + i * 16 + i16;
-      f.a[i] = *reinterpret_cast<const bf16x8*>(sb + m * S::A_ROW +
-                                                a_chunk<S::CA>(m, h * 4 + g) * 16);
-    }
+    const int m = wm * S::WROWS + i * 16 + i16;
+    return *reinterpret_cast<const bf16x8*>(sb + m * S::A_ROW + a_chunk<S::CA>(m, h * 4 + g) * 16);
+  };
+  auto rd_b = [&](int stage, int h, int j) __attribute__((always_inline)) -> bf16x8 {
+    const char* sb = smem + stage * S::STAGE;
     const int k_lo = h * 32 + g * 8 + tq;   // rows of the two transposing reads
     const int k_hi = k_lo + 4;
-    const int sw_lo = b_swz(k_lo), sw_hi = b_swz(k_hi);
+    const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
+    const char* blo = sb + S::A_STAGE + k_lo * S::B_ROW + ((sg ^ b_swz(k_lo)) * 32) + tr * 8;
+    const char* bhi = sb + S::A_STAGE + k_hi * S::B_ROW + ((sg ^ b_swz(k_hi)) * 32) + tr * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto load_frags = [&](Frags& f, int stage, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) f.a[i] = rd_a(stage, h, i);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) f.b[j] = rd_b(stage, h, j);
+  };
+  // The MFMAs of the fragments in f, column by column.  When `more`, the
+  // fragments of the next 32-deep half (ring slot nstage, half nh) are read
+  // into the same registers as they fall free: each B fragment after its
+  // column, the A fragments during the last column.  So the next half's
+  // reads overlap this half's MFMAs and no extra registers are held.
+  auto mfma_reload = [&](Frags& f, int nstage, int nh, bool more) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
-      const char* blo = sb + S::A_STAGE + k_lo * S::B_ROW + ((sg ^ sw_lo) * 32) + tr * 8;
-      const char* bhi = sb + S::A_STAGE + k_hi * S::B_ROW + ((sg ^ sw_hi) * 32) + tr * 8;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
-      f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (j < NJ - 1) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) f.b[j] = rd_b(nstage, nh, j);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) f.a[i] = rd_a(nstage, nh, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) f.b[j] = rd_b(nstage, nh, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  };
-  auto mfma = [&](const Frags& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   };
 
   // ---- pipeline --------------------------------------------------------------
-  // Step ks: wait until this thread's transfers of stage ks have landed,
-  // barrier (all threads' transfers of stage ks have landed, and every
-  // wavefront is done reading stage ks-1), refill stage ks-1's buffer with
-  // step ks+NS-1, then the MFMAs of stage ks, reading the second half's
-  // fragments while the first half's MFMAs run.
+  // NS ring slots of K steps.  The wavefront always holds in registers the
+  // fragments of the 32-deep half it multiplies next, read while the previous
+  // half's MFMAs ran.  Before the last half of step ks, once this thread's
+  // transfers of step ks+1 have landed and its reads of step ks are done, a
+  // barrier makes step ks+1 readable by all (its fragments are read during
+  // that half) and frees step ks's slot, which is refilled with step ks+NS.
   // A wavefront whose rows all lie past the tile's end (the last, short
   // M-tile of an expert) keeps loading and meeting the barriers but skips
   // its fragment reads and MFMAs.
@@ -366,41 +406,54 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
       (S::WM == 1) || (__builtin_amdgcn_readfirstlane(wm) * S::WROWS < tc.nrows);
   const int nk = kb1 - kb0;
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
+  for (int st = 0; st < NS; ++st)
     if (st < nk) issue(st, st);
-  // One K step held in ring slot `stage` (a constant in the unrolled loop
-  // below, so every LDS address of the step is a fixed offset).
-  auto step_body = [&](int ks, int stage) __attribute__((always_inline)) {
-    wait_stages<S::LOADS>(min(NS - 2, nk - 1 - ks));
+  Frags f;
+  if (nk > 0) {
+    wait_stages_lgkm0<S::LOADS>(min(NS - 1, nk - 1));
     // A bare barrier: __syncthreads() adds a release fence that would wait
     // for every transfer in flight, the later stages' included.
     __builtin_amdgcn_s_barrier();
-    if (ks + NS - 1 < nk) issue(ks + NS - 1, stage == 0 ? NS - 1 : stage - 1);
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (wactive) {
-      Frags f0;
-      load_frags(f0, stage, 0);
-      if constexpr (S::HALVES == 2) {
-        Frags f1;
-        load_frags(f1, stage, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma(f0);
-        mfma(f1);
-      } else {
-        __builtin_amdgcn_sched_barrier(0);
-        mfma(f0);
-      }
-    }
+    if (wactive) load_frags(f, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  int ks = 0;
-  for (; ks + NS <= nk; ks += NS) {
+  }
+  // One K step held in ring slot `stage` (a constant in the unrolled loop
+  // below, so every LDS address of the step is a fixed offset).  HAS_NEXT:
+  // a step ks+1 follows (every step but the last), so its stage is waited
+  // for, the slot of step ks is refilled, and its fragments are read ahead.
+  auto step_body = [&](int ks, int stage, auto has_next_c) __attribute__((always_inline)) {
+    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+    const int next_slot = stage == NS - 1 ? 0 : stage + 1;
 #pragma unroll
-    for (int u = 0; u < NS; ++u) step_body(ks + u, u);
+    for (int h = 0; h < S::HALVES; ++h) {
+      if (HAS_NEXT && h == S::HALVES - 1) {
+        wait_stages_lgkm0<S::LOADS>(min(NS - 2, nk - ks - 2));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (ks + NS < nk) issue(ks + NS, stage);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (wactive) {
+        if (h + 1 < S::HALVES) mfma_reload(f, stage, h + 1, true);
+        else mfma_reload(f, next_slot, 0, HAS_NEXT);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  int ks = 0;
+  // steps 0 .. nk-2 (each followed by another), NS at a time, then the last
+  for (; ks + NS <= nk - 1; ks += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step_body(ks + u, u, yes{});
   }
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
-    if (ks + u < nk) step_body(ks + u, u);
+    if (ks + u < nk - 1) step_body(ks + u, u, yes{});
+  if (nk > 0) step_body(nk - 1, (nk - 1) % NS, no{});
 
   // ---- epilogue -----------------------------------------------------------
   // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
