@@ -176,27 +176,32 @@ def main():
     work = algorithmic_work(w, kept, hit)
     per_kernel = {name: dict(launches=n, avg_ms=tot / max(n, 1) if n else 0.0)
                   for name, (n, tot) in kern.items()}
-    decode = w.T <= 64
-    # the routed SwiGLU GEMM (W1 and W3 of every hit expert) dominates every workload
-    dom = "ffn1_swiglu"
+    # The routed SwiGLU GEMM (W1 and W3 of every hit expert) dominates every
+    # workload.  Its bound is whichever floor is higher: the weight and row
+    # bytes at peak HBM bandwidth, or its flops at peak MFMA rate (few rows per
+    # expert, as in decode or with many fine-grained experts: HBM).
+    dom = "ffn1_swiglu" if w.dtype == "bf16" else "ffn1_swiglu_f32"
     dom_ms = per_kernel.get(dom, {}).get("avg_ms", float("nan"))
     digest = source_digest()
     meas = MEASURED_TRAFFIC.get(w.name)
     traffic = None
     if meas is not None and meas[0] == digest:
         traffic = meas[1] + meas[2]
-    if decode:
-        achieved = work["gemm1_bytes"] / (dom_ms * 1e-3) / 1e9
+    peak_flops = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    g1_bytes = work["gemm1_bytes"] + work["gemm1_io_bytes"]
+    hbm_bound = g1_bytes / (PEAK_HBM_GBS * 1e9) > work["gemm1_flops"] / (peak_flops * 1e12)
+    if hbm_bound:
+        achieved = g1_bytes / (dom_ms * 1e-3) / 1e9
         roof = dict(kernel=dom, bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS,
                     unit="GB/s", frac=achieved / PEAK_HBM_GBS, traffic=traffic,
-                    per_launch=f"{work['gemm1_bytes']} bytes (W1+W3 of {hit} hit experts)")
+                    per_launch=(f"{g1_bytes} bytes (W1+W3 of {hit} hit experts, {kept} token "
+                                f"rows read, {kept} hidden rows written)"))
     else:
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = work["gemm1_flops"] / (dom_ms * 1e-3) / 1e12
-        roof = dict(kernel=dom, bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s",
-                    frac=achieved / peak, traffic=traffic,
+        roof = dict(kernel=dom, bound="mfma", achieved=achieved, peak=peak_flops,
+                    unit="TFLOP/s", frac=achieved / peak_flops, traffic=traffic,
                     per_launch=f"{work['gemm1_flops']} flops (2*d*2F per kept row, {kept} rows)")
-    roof["algorithmic_bytes"] = work["gemm1_bytes"] + work["gemm1_io_bytes"]
+    roof["algorithmic_bytes"] = g1_bytes
     roof["traffic_unit"] = "bytes per launch (HBM side, counters)"
     roof["source_digest"] = digest
     layer_tflops = work["flops"] / (ms * 1e-3) / 1e12

@@ -504,11 +504,14 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
 //   0: 32-row M-tiles for short batches; 4-stage ring, one workgroup per CU.
 //   1: 128 x 256 x 32, 8 wavefronts, 3 stages (72 KB): two workgroups per CU
 //      (4 wavefronts per SIMD); best when experts have many rows.
-//   2: 128 x 256 x 64, 8 wavefronts, 3 stages (144 KB): one workgroup per
-//      CU; best for a few hundred rows per expert (fine-grained experts).
+//   2: 256 x 256 x 32, 8 wavefronts (4 x 2) of 64 x 128, 4 stages (128 KB):
+//      one workgroup per CU.  For a few hundred rows per expert (fine-grained
+//      experts, where the weights' HBM traffic is the bound): one M-tile per
+//      expert reads each weight tile once, and on an expert's short tile the
+//      64-row wavefront rows with no rows skip their MFMAs.
 using ShapeShort = Shape<32, 256, 64, 4, 1, 4>;
 using ShapeLongA = Shape<128, 256, 32, 8, 2, 3>;
-using ShapeLongB = Shape<128, 256, 64, 8, 2, 3>;
+using ShapeWide = Shape<256, 256, 32, 8, 4, 4>;
 
 }  // namespace dma
 
@@ -650,8 +653,8 @@ hipError_t launch_bf16_shape(const GroupedGemm& g, hipStream_t s) {
 }
 template <bool SWIGLU>
 hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
-  if (g.bm == 32) return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
-  if (g.shape == 2) return launch_bf16_shape<SWIGLU, dma::ShapeLongB>(g, s);
+  if (g.bm == kGroupedBMShort) return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
+  if (g.bm == kGroupedBMWide) return launch_bf16_shape<SWIGLU, dma::ShapeWide>(g, s);
   return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
 }
 hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm, int topk,

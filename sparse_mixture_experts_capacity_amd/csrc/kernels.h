@@ -54,8 +54,7 @@ struct GroupedGemm {
   int n_experts;
   int static_rows;          // rows when tiles == null
   int max_mtiles;           // upper bound of M-tiles
-  int bm;                   // M-tile rows (bf16: 128 or 32; fp32: 64); tiles match it
-  int shape;                // bf16 with bm 128: 1 = two workgroups per CU, 2 = one
+  int bm;                   // M-tile rows (bf16: 32, 128 or 256; fp32: 64); tiles match it
   int ksplit;               // K is split in this many parts (plain fp32 output only);
   int64_t c_split;          // part p writes C + p * c_split (fp32 partial sums)
   // K-blocked layouts (bf16 kernels): element (row, k) of a matrix with R
@@ -70,6 +69,7 @@ hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm
                                  hipStream_t s);
 constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels, long batches
 constexpr int kGroupedBMShort = 32;  // M-tile for short batches (few rows per expert)
+constexpr int kGroupedBMWide = 256;  // M-tile for a few hundred rows per expert
 constexpr int kF32BM = 64;        // M-tile of the fp32 kernels
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s);

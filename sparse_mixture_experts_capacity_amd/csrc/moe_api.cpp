@@ -130,7 +130,6 @@ struct Plan {
   int bm = 0;                    // M-tile of the grouped kernels
   int max_mtiles = 0;
   int static_bm = 0;             // M-tile of the GEMMs over all T token rows
-  int routed_shape = 1;          // kernel shape of the routed GEMMs (bm 128)
   bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
@@ -268,15 +267,19 @@ int make_plan(const moe_config_t* c, Plan* p) {
   if (tpb < groups) tpb = groups;
   p->topk_tpb = static_cast<int>(tpb);
   p->topk_blocks = static_cast<int>((p->T + tpb - 1) / tpb);
-  // M-tile: 32 rows when the hit experts average at most 48 rows each (short
-  // batches), else 128; the tile list is built for it.
+  // M-tile of the routed GEMMs, from the average rows per hit expert (the
+  // tile list is built for it; the M-tile picks the kernel shape):
+  //   <= 48   32 rows (short batches: the weights stream once);
+  //   < 384  256 rows, one workgroup per CU (a few hundred rows, as with many
+  //          fine-grained experts: one M-tile per expert reads each weight
+  //          tile once);
+  //   more   128 rows, two workgroups per CU (barriers and tile set-up of one
+  //          overlap the other's MFMAs).
   if (p->bf16) {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
-    const bool short_rows = hit > 0 && p->TK <= 48 * hit;
-    p->bm = short_rows ? moe::kGroupedBMShort : moe::kGroupedBM;
-    // Many rows per expert: two workgroups per CU hide barriers and tile
-    // set-up; a few hundred: the deeper one-workgroup pipeline wins.
-    p->routed_shape = (hit > 0 && p->TK >= 384 * hit) ? 1 : 2;
+    if (hit > 0 && p->TK <= 48 * hit) p->bm = moe::kGroupedBMShort;
+    else if (hit > 0 && p->TK < 384 * hit) p->bm = moe::kGroupedBMWide;
+    else p->bm = moe::kGroupedBM;
     p->static_bm = p->T <= 64 ? moe::kGroupedBMShort : moe::kGroupedBM;
   } else {
     p->bm = p->static_bm = moe::kF32BM;
@@ -284,15 +287,14 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->max_mtiles = static_cast<int>(p->rows_max / p->bm + p->E);
   // Long batches: GEMM1 writes H K-blocked, so each K step of a GEMM2 tile
   // reads one contiguous run of memory instead of 64-byte pieces of rows.
-  // With the 32-deep K step and up to ~1.5k rows per expert, the kept token
-  // rows are likewise first gathered into a slot-ordered K-blocked copy for
-  // GEMM1 (with the 64-deep step a row piece is already a whole 128-byte
-  // line; with many more rows the copy costs more than it saves).  Short
-  // batches read the few rows directly.
+  // With 128-row tiles and up to ~1.5k rows per expert, the kept token rows
+  // are likewise first gathered into a slot-ordered K-blocked copy for GEMM1
+  // (with many more rows, or with the weight-bound 256-row tiles, the copy
+  // costs more than it saves).  Short batches read the few rows directly.
   p->blocked = p->bf16 && p->bm != moe::kGroupedBMShort;
   {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
-    p->gather_x = p->blocked && p->routed_shape == 1 && p->TK <= 1536 * hit;
+    p->gather_x = p->blocked && p->bm == moe::kGroupedBM && p->TK <= 1536 * hit;
   }
   // Router scores x W_gate on the MFMA GEMM when the weight rows are 16-byte
   // aligned; K is split so that even short batches give ~512 workgroups, and
@@ -321,7 +323,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
     // resident workgroups and then a last round less than half full (e.g.
     // 592 tiles on 512 slots): two K parts turn that into fuller rounds.
     if (p->path == MOE_PATH_AUTO && p->ffn2_split == 1 && p->bm != moe::kGroupedBMShort) {
-      const int64_t slots = static_cast<int64_t>(device_cus()) * (p->routed_shape == 1 ? 2 : 1);
+      const int64_t slots = static_cast<int64_t>(device_cus()) * (p->bm == moe::kGroupedBM ? 2 : 1);
       const int64_t t = mt_est * ntn2;
       if (slots > 0 && t > slots && t < 4 * slots && (t % slots) != 0 && (t % slots) <= slots / 2)
         p->ffn2_split = 2;
@@ -402,7 +404,7 @@ int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
     r.c_group_col = 0; r.tiles = nullptr; r.ntiles = nullptr; r.tstart = nullptr;
     r.n_experts = 1; r.static_rows = static_cast<int>(p.T);
     r.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
-    r.bm = p.static_bm; r.shape = 1;
+    r.bm = p.static_bm;
     r.ksplit = p.router_split; r.c_split = p.T * p.E;
     Timed t("router", s);
     HIP_TRY(moe::launch_grouped_plain_bf16(r, s));
@@ -532,7 +534,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
   g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
-  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm; g1.shape = p.routed_shape;
+  g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm;
   if (p.gather_x) {
     Timed t("gather", s);
     HIP_TRY(moe::launch_gather_blocked(x, p.d, at<int32_t>(ws, p.perm), p.k,
@@ -559,7 +561,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
     s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);
     s1.max_mtiles = static_cast<int>((p.T + p.static_bm - 1) / p.static_bm);
-    s1.bm = p.static_bm; s1.shape = 1;
+    s1.bm = p.static_bm;
     s2 = s1;
     s2.a_block_rows = s1.c_block_rows; s2.c_block_rows = 0;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
