@@ -24,6 +24,18 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* kcount, int32_t* offsets, int32_t* slot,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
                            int32_t* tstart, hipStream_t s);
+// Short batches: top-k, gates and the whole dispatch in one workgroup
+// (T <= kSmallT, T * k <= kSmallTK); results equal launch_topk_gate with one
+// block followed by launch_dispatch.
+constexpr int kSmallT = 128;
+constexpr int kSmallTK = 2048;
+hipError_t launch_route_small(const float* lpart, int nsplit, int64_t split_stride,
+                              const float* bias, float* logits_out, int T, int E, int k,
+                              int gating, int renorm, int32_t* topk_idx, float* topk_w,
+                              float* Ppart, float* Hpart, int C, int32_t* counts,
+                              int32_t* kcount, int32_t* offsets, int32_t* slot,
+                              int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
+                              int32_t* tstart, hipStream_t s);
 hipError_t launch_stats(const float* Ppart, const float* Hpart, int nblk,
                         const int32_t* counts, const int32_t* kcount, int64_t T,
                         int k, int E, double* out, hipStream_t s);

@@ -134,6 +134,7 @@ struct Plan {
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
+  bool small_route = false;      // top-k and dispatch in one workgroup
   bool blocked = false;          // GEMM1 writes H K-blocked; GEMM2 reads it so
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
   // workspace regions
@@ -267,6 +268,13 @@ int make_plan(const moe_config_t* c, Plan* p) {
   if (tpb < groups) tpb = groups;
   p->topk_tpb = static_cast<int>(tpb);
   p->topk_blocks = static_cast<int>((p->T + tpb - 1) / tpb);
+  // Short batches: top-k, gates and dispatch run as one kernel in one
+  // workgroup (its softmax statistics come as a single partial row).
+  p->small_route = p->T > 0 && p->T <= moe::kSmallT && p->TK <= moe::kSmallTK;
+  if (p->small_route) {
+    p->topk_blocks = 1;
+    p->topk_tpb = static_cast<int>(p->T);
+  }
   // M-tile of the routed GEMMs, from the average rows per hit expert (the
   // tile list is built for it; the M-tile picks the kernel shape):
   //   <= 48   32 rows (short batches: the weights stream once);
@@ -422,6 +430,16 @@ int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
 // scores are also written to logits_out when it is given.
 int run_route(const Plan& p, void* ws, const Scores& sc, float* logits_out, int32_t* idx,
               float* w, hipStream_t s) {
+  if (p.small_route) {
+    Timed t("route_small", s);
+    HIP_TRY(moe::launch_route_small(
+        sc.lsrc, sc.nsplit, sc.split_stride, sc.bias, logits_out, static_cast<int>(p.T), p.E,
+        p.k, p.gating, p.renorm, idx, w, at<float>(ws, p.ppart), at<float>(ws, p.hpart),
+        p.Ceff, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount), at<int32_t>(ws, p.offsets),
+        at<int32_t>(ws, p.slot), at<int32_t>(ws, p.perm), p.bm, at<moe::Tile>(ws, p.tiles),
+        at<int32_t>(ws, p.ntiles), at<int32_t>(ws, p.tstart), s));
+    return MOE_OK;
+  }
   {
     Timed t("topk_gate", s);
     HIP_TRY(moe::launch_topk_gate(sc.lsrc, sc.nsplit, sc.split_stride, sc.bias, logits_out,

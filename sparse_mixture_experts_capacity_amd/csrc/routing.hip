@@ -137,6 +137,99 @@ __device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
   return (a > b) || (a == b && ia < ib);
 }
 
+// Top-k selection and gates of token t by a group of G lanes (lane gl of the
+// group): the router score of expert i is the sum of the nsplit partial
+// arrays (split_stride apart) plus bias[i]; lane gl holds experts gl + v*G.
+// Lane 0 writes the chosen experts (best first) and their gates; every lane
+// adds its experts' full-softmax probabilities to pacc and lane 0 the
+// token's router entropy to hacc.  When sidx is given, lane 0 also stores the
+// chosen experts there.
+template <int V>
+__device__ __forceinline__ void topk_token(
+    int64_t t, const float* __restrict__ lpart, int nsplit, int64_t split_stride,
+    const float* __restrict__ bias, float* __restrict__ logits_out, int E, int k, int G,
+    int gl, int gating, int renorm, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int* sidx, float (&pacc)[V], float& hacc) {
+  float val[V];
+  bool taken[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int i = gl + v * G;
+    float l = -INFINITY;
+    if (i < E) {
+      l = lpart[t * E + i];
+      // fixed order q = 0, 1, ...; unrolled so the loads are in flight together
+#pragma unroll 8
+      for (int q = 1; q < nsplit; ++q) l += lpart[q * split_stride + t * E + i];
+      if (bias) l += bias[i];
+      if (logits_out) logits_out[t * E + i] = l;
+      // A NaN score ranks as -infinity: never ahead of a number, ties by
+      // index, so a valid expert index is always chosen.
+      if (l != l) l = -INFINITY;
+    }
+    val[v] = l;
+    taken[v] = !(i < E);
+  }
+  float m = 0.f;
+  float esum = 0.f;  // sum of e^(l_j - m) over the chosen experts (lane 0)
+  for (int j = 0; j < k; ++j) {
+    // sentinel loses to every real expert, -infinity scores included
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i = gl + v * G;
+      if (!taken[v] && better(val[v], i, bv, bi)) { bv = val[v]; bi = i; }
+    }
+    for (int off = G >> 1; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, G);
+      const int oi = __shfl_xor(bi, off, G);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (j == 0) m = bv;
+    if ((bi % G) == gl) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (gl + v * G == bi) taken[v] = true;
+    }
+    if (gl == 0 && topk_idx) topk_idx[t * k + j] = bi;
+    if (gl == 0 && sidx) sidx[t * k + j] = bi;
+    if (gl == 0 && topk_w) {
+      // un-normalised gate e^(l_j - m); scaled below once Z is known
+      const float ej = bv > -INFINITY ? expf(bv - m) : 0.f;
+      topk_w[t * k + j] = ej;
+      esum += ej;
+    }
+  }
+  // Full softmax over all E experts, shifted by the top score m.
+  float ex[V];
+  float z = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    ex[v] = (gl + v * G < E && val[v] > -INFINITY) ? expf(val[v] - m) : 0.f;
+    z += ex[v];
+  }
+  for (int off = G >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off, G);
+  const float inv_z = 1.0f / z;
+  float plogp = 0.f;  // sum_i p_i (l_i - m)
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const float p = ex[v] * inv_z;
+    pacc[v] += p;
+    if (p > 0.f) plogp += p * (val[v] - m);
+  }
+  for (int off = G >> 1; off >= 1; off >>= 1) plogp += __shfl_xor(plogp, off, G);
+  if (gl == 0) hacc += logf(z) - plogp;
+
+  // Gate weights: Mixtral order w_j = e_j / sum_j' e_j; DeepSeek order
+  // w_j = e_j / Z (the full softmax at the chosen expert), or e_j / sum e
+  // when renormalised.  Lane 0 rescales the values it wrote above.
+  if (gl == 0 && topk_w) {
+    const float scale = (gating == 0 || renorm) ? 1.0f / esum : inv_z;
+    for (int j = 0; j < k; ++j) topk_w[t * k + j] *= scale;
+  }
+}
+
 template <int V>
 __global__ __launch_bounds__(256) void topk_gate_kernel(
     const float* __restrict__ lpart, int nsplit, int64_t split_stride,
@@ -157,83 +250,9 @@ __global__ __launch_bounds__(256) void topk_gate_kernel(
 
   const int64_t tb = static_cast<int64_t>(blockIdx.x) * tokens_per_block;
   const int64_t te = min(T, tb + tokens_per_block);
-  for (int64_t t = tb + grp; t < te; t += ngroups) {
-    float val[V];
-    bool taken[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int i = gl + v * G;
-      float l = -INFINITY;
-      if (i < E) {
-        l = lpart[t * E + i];
-        for (int q = 1; q < nsplit; ++q) l += lpart[q * split_stride + t * E + i];
-        if (bias) l += bias[i];
-        if (logits_out) logits_out[t * E + i] = l;
-        // A NaN score ranks as -infinity: never ahead of a number, ties by
-        // index, so a valid expert index is always chosen.
-        if (l != l) l = -INFINITY;
-      }
-      val[v] = l;
-      taken[v] = !(i < E);
-    }
-    float m = 0.f;
-    float esum = 0.f;  // sum of e^(l_j - m) over the chosen experts (lane 0)
-    for (int j = 0; j < k; ++j) {
-      // sentinel loses to every real expert, -infinity scores included
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int i = gl + v * G;
-        if (!taken[v] && better(val[v], i, bv, bi)) { bv = val[v]; bi = i; }
-      }
-      for (int off = G >> 1; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, G);
-        const int oi = __shfl_xor(bi, off, G);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (j == 0) m = bv;
-      if ((bi % G) == gl) {
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          if (gl + v * G == bi) taken[v] = true;
-      }
-      if (gl == 0 && topk_idx) topk_idx[t * k + j] = bi;
-      if (gl == 0 && topk_w) {
-        // un-normalised gate e^(l_j - m); scaled below once Z is known
-        const float ej = bv > -INFINITY ? expf(bv - m) : 0.f;
-        topk_w[t * k + j] = ej;
-        esum += ej;
-      }
-    }
-    // Full softmax over all E experts, shifted by the top score m.
-    float ex[V];
-    float z = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      ex[v] = (gl + v * G < E && val[v] > -INFINITY) ? expf(val[v] - m) : 0.f;
-      z += ex[v];
-    }
-    for (int off = G >> 1; off >= 1; off >>= 1) z += __shfl_xor(z, off, G);
-    const float inv_z = 1.0f / z;
-    float plogp = 0.f;  // sum_i p_i (l_i - m)
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const float p = ex[v] * inv_z;
-      pacc[v] += p;
-      if (p > 0.f) plogp += p * (val[v] - m);
-    }
-    for (int off = G >> 1; off >= 1; off >>= 1) plogp += __shfl_xor(plogp, off, G);
-    if (gl == 0) hacc += logf(z) - plogp;
-
-    // Gate weights: Mixtral order w_j = e_j / sum_j' e_j; DeepSeek order
-    // w_j = e_j / Z (the full softmax at the chosen expert), or e_j / sum e
-    // when renormalised.  Lane 0 rescales the values it wrote above.
-    if (gl == 0 && topk_w) {
-      const float scale = (gating == 0 || renorm) ? 1.0f / esum : inv_z;
-      for (int j = 0; j < k; ++j) topk_w[t * k + j] *= scale;
-    }
-  }
+  for (int64_t t = tb + grp; t < te; t += ngroups)
+    topk_token<V>(t, lpart, nsplit, split_stride, bias, logits_out, E, k, G, gl, gating,
+                  renorm, topk_idx, topk_w, nullptr, pacc, hacc);
   // Workgroup reduction of the softmax statistics in a fixed order.
   if (Ppart) {
 #pragma unroll
@@ -418,6 +437,182 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                                          offsets, bm, tiles, ntiles, tstart);
   dispatch_scatter_kernel<<<(TK + 255) / 256, 256, 0, s>>>(
       topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Short batches (T <= kSmallT, T*k <= kSmallTK): top-k gating and the whole
+// dispatch in one workgroup of 1024 threads, with the same results as the
+// top-k pass and the three dispatch passes above.
+//   1. top-k and gates per token (topk_token), chosen experts kept in LDS,
+//      softmax statistics reduced into Ppart[0..E) and Hpart[0];
+//   2. each of the 16 wavefronts ranks a contiguous chunk of the T*k
+//      assignments (ballot matching as in pass 1, per-wavefront counters);
+//   3. per expert, chunk bases in chunk order, counts, capacity; offsets and
+//      the M-tile list as in pass 2;
+//   4. slot / perm as in pass 3.
+// ---------------------------------------------------------------------------
+constexpr int kSmallWaves = 16;
+template <int V>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ lpart, int nsplit, int64_t split_stride,
+    const float* __restrict__ bias, float* __restrict__ logits_out, int T, int E, int k,
+    int G, int gating, int renorm, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ Ppart, float* __restrict__ Hpart, int C,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kcount,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ slot, int32_t* __restrict__ perm,
+    int bm, Tile* __restrict__ tiles, int32_t* __restrict__ ntiles,
+    int32_t* __restrict__ tstart) {
+  __shared__ int sidx[kSmallTK];
+  __shared__ int srank[kSmallTK];
+  __shared__ int ccnt[kSmallWaves][kMaxExperts];
+  __shared__ float pbuf[1024 * 4];   // [groups][E], groups*E <= 1024*V
+  __shared__ float hbuf[1024];
+  __shared__ int kc[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int toff[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int TK = T * k;
+
+  // 1. top-k and gates
+  {
+    const int gl = tid % G;
+    const int grp = tid / G;
+    const int ngroups = blockDim.x / G;
+    float pacc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) pacc[v] = 0.f;
+    float hacc = 0.f;
+    for (int t = grp; t < T; t += ngroups)
+      topk_token<V>(t, lpart, nsplit, split_stride, bias, logits_out, E, k, G, gl, gating,
+                    renorm, topk_idx, topk_w, sidx, pacc, hacc);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i = gl + v * G;
+      if (i < E) pbuf[grp * E + i] = pacc[v];
+    }
+    if (gl == 0) hbuf[grp] = hacc;
+    for (int i = tid; i < kSmallWaves * E; i += blockDim.x) ccnt[i / E][i % E] = 0;
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+      float sp = 0.f;
+      for (int g = 0; g < ngroups; ++g) sp += pbuf[g * E + e];
+      Ppart[e] = sp;
+    }
+    if (tid == 0) {
+      float sh = 0.f;
+      for (int g = 0; g < ngroups; ++g) sh += hbuf[g];
+      Hpart[0] = sh;
+    }
+  }
+
+  // 2. stable ranks within each wavefront's chunk of assignments
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int chunk = ((TK + kSmallWaves - 1) / kSmallWaves + kWave - 1) / kWave * kWave;
+  {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int* cnt = ccnt[wave];
+    for (int it = 0; it < chunk; it += kWave) {
+      const int a = wave * chunk + it + lane;
+      const int ein = a < TK ? sidx[a] : -1;
+      const bool valid = ein >= 0 && ein < E;
+      const int e = valid ? ein : 0;
+      uint64_t match = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      const int before = valid ? cnt[e] : 0;
+      __builtin_amdgcn_wave_barrier();
+      const bool leader = valid && (__ffsll(static_cast<unsigned long long>(match)) - 1 == lane);
+      if (leader) cnt[e] = before + __popcll(match);
+      __builtin_amdgcn_wave_barrier();
+      if (valid) srank[a] = before + __popcll(match & lt);
+    }
+  }
+  __syncthreads();
+
+  // 3. chunk bases, counts, capacity, offsets, M-tiles
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int c = ccnt[w][e];
+      ccnt[w][e] = run;
+      run += c;
+    }
+    counts[e] = run;
+    kc[e] = min(run, C);
+    kcount[e] = kc[e];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int so = 0, ts = 0;
+    for (int i = 0; i < E; ++i) {
+      off[i] = so;
+      toff[i] = ts;
+      so += kc[i];
+      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+    }
+    off[E] = so;
+    toff[E] = ts;
+    if (ntiles) *ntiles = ts;
+  }
+  __syncthreads();
+  for (int i = tid; i <= E; i += blockDim.x) {
+    offsets[i] = off[i];
+    if (tstart) tstart[i] = toff[i];
+  }
+  if (tiles && bm > 0) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      int n = 0;
+      for (int r = 0; r < kc[e]; r += bm, ++n)
+        tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
+    }
+  }
+
+  // 4. slots and the permutation (unused entries -1)
+  const int total = off[E];
+  for (int a = tid; a < TK; a += blockDim.x) {
+    if (a >= total) perm[a] = -1;
+    const int e = sidx[a];
+    if (e < 0 || e >= E) {
+      slot[a] = -1;
+      continue;
+    }
+    const int rank = ccnt[a / chunk][e] + srank[a];
+    if (rank < C) {
+      const int sl = off[e] + rank;
+      slot[a] = sl;
+      perm[sl] = a;
+    } else {
+      slot[a] = -1;
+    }
+  }
+}
+
+hipError_t launch_route_small(const float* lpart, int nsplit, int64_t split_stride,
+                              const float* bias, float* logits_out, int T, int E, int k,
+                              int gating, int renorm, int32_t* topk_idx, float* topk_w,
+                              float* Ppart, float* Hpart, int C, int32_t* counts,
+                              int32_t* kcount, int32_t* offsets, int32_t* slot,
+                              int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
+                              int32_t* tstart, hipStream_t s) {
+  if (T <= 0 || T > kSmallT || T * k > kSmallTK) return hipErrorInvalidValue;
+  const int G = topk_group_size(E);
+  const int V = (E + G - 1) / G;
+#define MOE_SMALL_ARGS                                                                 \
+  lpart, nsplit, split_stride, bias, logits_out, T, E, k, G, gating, renorm, topk_idx, \
+      topk_w, Ppart, Hpart, C, counts, kcount, offsets, slot, perm, bm, tiles, ntiles, tstart
+  if (V <= 1)
+    route_small_kernel<1><<<1, 1024, 0, s>>>(MOE_SMALL_ARGS);
+  else if (V <= 2)
+    route_small_kernel<2><<<1, 1024, 0, s>>>(MOE_SMALL_ARGS);
+  else
+    route_small_kernel<4><<<1, 1024, 0, s>>>(MOE_SMALL_ARGS);
+#undef MOE_SMALL_ARGS
   return hipGetLastError();
 }
 
