@@ -501,7 +501,9 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
 }
 
 // Shapes in use (the host picks one per GEMM through GroupedGemm::shape):
-//   0: 32-row M-tiles for short batches; 4-stage ring, one workgroup per CU.
+//   0: 32-row M-tiles for short batches; 4-stage ring, one workgroup per CU;
+//      with narrow_n, 128-wide B tiles (80 KB, two workgroups per CU): twice
+//      the tiles, so the weights of several hit experts stream from more CUs.
 //   1: 128 x 256 x 32, 8 wavefronts, 3 stages (72 KB): two workgroups per CU
 //      (4 wavefronts per SIMD); best when experts have many rows.
 //   2: 256 x 256 x 32, 8 wavefronts (4 x 2) of 64 x 128, 4 stages (128 KB):
@@ -510,6 +512,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
 //      expert reads each weight tile once, and on an expert's short tile the
 //      64-row wavefront rows with no rows skip their MFMAs.
 using ShapeShort = Shape<32, 256, 64, 4, 1, 4>;
+using ShapeShortN = Shape<32, 128, 64, 4, 1, 4>;
 using ShapeLongA = Shape<128, 256, 32, 8, 2, 3>;
 using ShapeWide = Shape<256, 256, 32, 8, 4, 4>;
 
@@ -653,7 +656,10 @@ hipError_t launch_bf16_shape(const GroupedGemm& g, hipStream_t s) {
 }
 template <bool SWIGLU>
 hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
-  if (g.bm == kGroupedBMShort) return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
+  if (g.bm == kGroupedBMShort) {
+    if (g.narrow_n) return launch_bf16_shape<SWIGLU, dma::ShapeShortN>(g, s);
+    return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
+  }
   if (g.bm == kGroupedBMWide) return launch_bf16_shape<SWIGLU, dma::ShapeWide>(g, s);
   return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
 }

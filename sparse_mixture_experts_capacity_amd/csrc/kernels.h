@@ -67,6 +67,7 @@ struct GroupedGemm {
   int static_rows;          // rows when tiles == null
   int max_mtiles;           // upper bound of M-tiles
   int bm;                   // M-tile rows (bf16: 32, 128 or 256; fp32: 64); tiles match it
+  int narrow_n;             // bm 32: 128-wide B tiles instead of 256
   int ksplit;               // K is split in this many parts (plain fp32 output only);
   int64_t c_split;          // part p writes C + p * c_split (fp32 partial sums)
   // K-blocked layouts (bf16 kernels): element (row, k) of a matrix with R

@@ -553,6 +553,9 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
   g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
   g1.static_rows = 0; g1.max_mtiles = p.max_mtiles; g1.bm = p.bm;
+  // Short batches hitting several experts: the SwiGLU GEMM takes 128-wide B
+  // tiles (two workgroups per CU), so more CUs stream the weights at once.
+  g1.narrow_n = p.bm == moe::kGroupedBMShort && (p.TK < p.E ? p.TK : p.E) >= 4;
   if (p.gather_x) {
     Timed t("gather", s);
     HIP_TRY(moe::launch_gather_blocked(x, p.d, at<int32_t>(ws, p.perm), p.k,
@@ -565,7 +568,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   moe::GroupedGemm g2 = g1;
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
   g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
-  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
+  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d; g2.narrow_n = 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
@@ -574,7 +577,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   moe::GroupedGemm s1{}, s2{};
   if (p.S > 0) {
     s1 = g1;
-    s1.A = x; s1.a_block_rows = 0; s1.c_block_rows = p.blocked ? p.T : 0;
+    s1.A = x; s1.a_block_rows = 0; s1.c_block_rows = p.blocked ? p.T : 0; s1.narrow_n = 0;
     s1.perm = nullptr; s1.group_base = p.E; s1.ngroups_n = p.S; s1.C = at<void>(ws, p.Hs);
     s1.ldc = static_cast<int64_t>(p.S) * p.F; s1.c_group_col = p.F; s1.tiles = nullptr;
     s1.ntiles = nullptr; s1.tstart = nullptr; s1.static_rows = static_cast<int>(p.T);

@@ -223,6 +223,8 @@ FORWARD_CASES = {
     # hidden rows K-blocked; shared experts
     "bf16_mid_rows_shared": Workload("bf16_mid_sh", T=512, d=128, F=192, E=4, k=2, S=2,
                                      capacity_factor=1.25),
+    # a few rows for each of several experts: short tiles with narrow weight tiles
+    "bf16_decode_narrow": Workload("bf16_dec_nar", T=16, d=256, F=384, E=8, k=2),
     # over 1.5k rows per expert: token rows read in place, hidden rows K-blocked
     "bf16_many_rows": Workload("bf16_many", T=4096, d=128, F=128, E=2, k=1,
                                capacity_factor=1.0),
