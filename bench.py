@@ -31,7 +31,11 @@ PEAK_HBM_GBS = 8000.0
 # once a source changes, the figure no longer describes the kernel and the
 # bench reports null.
 MEASURED_TRAFFIC = {
-    # workload: (source digest, fetch bytes, write bytes)
+    # workload: (source digest, fetch bytes, write bytes) per launch of the
+    # routed SwiGLU GEMM; the counter summaries are kept beside the profiles
+    "mixtral_prefill": ("5111429808994724", 4519.13e6, 121.79e6),
+    "deepseek": ("5111429808994724", 5372.37e6, 75.86e6),
+    "mixtral_decode_t64": ("5111429808994724", 1892.92e6, 3.67e6),
 }
 SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "combine.hip", "moe_api.cpp", "common.h",
                 "kernels.h")
