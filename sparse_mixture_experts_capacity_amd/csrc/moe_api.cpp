@@ -277,17 +277,19 @@ int make_plan(const moe_config_t* c, Plan* p) {
   }
   // M-tile of the routed GEMMs, from the average rows per hit expert (the
   // tile list is built for it; the M-tile picks the kernel shape):
-  //   <= 48   32 rows (short batches: the weights stream once);
-  //   < 384  256 rows, one workgroup per CU (a few hundred rows, as with many
-  //          fine-grained experts: one M-tile per expert reads each weight
-  //          tile once);
-  //   more   128 rows, two workgroups per CU (barriers and tile set-up of one
-  //          overlap the other's MFMAs).
+  //   <= 48        32 rows (short batches: the weights stream once);
+  //   384 .. 1536 128 rows, two workgroups per CU (barriers and tile set-up
+  //               of one overlap the other's MFMAs), token rows gathered into
+  //               a K-blocked copy first;
+  //   otherwise   256 rows, one workgroup per CU: with a few hundred rows (as
+  //               with many fine-grained experts) one M-tile per expert reads
+  //               each weight tile once; with thousands, each weight tile is
+  //               fetched for half as many M-tiles.
   if (p->bf16) {
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
     if (hit > 0 && p->TK <= 48 * hit) p->bm = moe::kGroupedBMShort;
-    else if (hit > 0 && p->TK < 384 * hit) p->bm = moe::kGroupedBMWide;
-    else p->bm = moe::kGroupedBM;
+    else if (hit > 0 && p->TK >= 384 * hit && p->TK <= 1536 * hit) p->bm = moe::kGroupedBM;
+    else p->bm = moe::kGroupedBMWide;
     p->static_bm = p->T <= 64 ? moe::kGroupedBMShort : moe::kGroupedBM;
   } else {
     p->bm = p->static_bm = moe::kF32BM;
@@ -295,15 +297,11 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->max_mtiles = static_cast<int>(p->rows_max / p->bm + p->E);
   // Long batches: GEMM1 writes H K-blocked, so each K step of a GEMM2 tile
   // reads one contiguous run of memory instead of 64-byte pieces of rows.
-  // With 128-row tiles and up to ~1.5k rows per expert, the kept token rows
-  // are likewise first gathered into a slot-ordered K-blocked copy for GEMM1
-  // (with many more rows, or with the weight-bound 256-row tiles, the copy
-  // costs more than it saves).  Short batches read the few rows directly.
+  // With 128-row tiles, the kept token rows are likewise first gathered into
+  // a slot-ordered K-blocked copy for GEMM1.  Short batches read the few rows
+  // directly.
   p->blocked = p->bf16 && p->bm != moe::kGroupedBMShort;
-  {
-    const int64_t hit = p->TK < p->E ? p->TK : p->E;
-    p->gather_x = p->blocked && p->bm == moe::kGroupedBM && p->TK <= 1536 * hit;
-  }
+  p->gather_x = p->blocked && p->bm == moe::kGroupedBM;
   // Router scores x W_gate on the MFMA GEMM when the weight rows are 16-byte
   // aligned; K is split so that even short batches give ~512 workgroups, and
   // the top-k pass adds the parts in a fixed order.
