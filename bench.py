@@ -54,17 +54,31 @@ def source_digest() -> str:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="after the timed steps, this many more with L2 and the 256 MB "
+                         "Infinity Cache flushed before each (reported separately)")
+    ap.add_argument("--flush-mib", type=int, default=512)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps "
                          "(a kernel of known traffic for scaling HBM counters)")
     return ap.parse_args()
+
+
+def percentile(sorted_vals, q):
+    """q-th percentile (0..100) of a sorted list, linear interpolation."""
+    if not sorted_vals:
+        return float("nan")
+    pos = (len(sorted_vals) - 1) * q / 100.0
+    lo = int(pos)
+    hi = min(lo + 1, len(sorted_vals) - 1)
+    return sorted_vals[lo] + (sorted_vals[hi] - sorted_vals[lo]) * (pos - lo)
 
 
 def algorithmic_work(w, kept: int, hit_experts: int):
@@ -162,17 +176,49 @@ def main():
         for _ in range(args.warmup):
             step()
         stream.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
         moe.moe_timing_reset()
         moe.moe_timing_enable(True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for i in range(args.steps):
+            ev[i][0].record(stream)
             step()
+            ev[i][1].record(stream)
         stream.synchronize()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         moe.moe_timing_enable(False)
         kern = moe.moe_timing_read()
+        step_ms = sorted(a.elapsed_time(b) for a, b in ev)
+
+        # Cold steps (not part of the timed region above): a buffer larger than
+        # L2 and the Infinity Cache is read before each step, so no weight
+        # bytes survive from the previous step.  It is read, not written, so
+        # the caches hold clean lines and the step pays no write-back.
+        cold = None
+        if args.cold_steps > 0:
+            flush = torch.ones(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+            sink = torch.zeros((), dtype=torch.float32, device=dev)
+            sink += flush.sum()
+            stream.synchronize()
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.cold_steps)]
+            moe.moe_timing_reset()
+            moe.moe_timing_enable(True)
+            for i in range(args.cold_steps):
+                sink += flush.sum()
+                cev[i][0].record(stream)
+                step()
+                cev[i][1].record(stream)
+            stream.synchronize()
+            moe.moe_timing_enable(False)
+            ckern = moe.moe_timing_read()
+            cold = dict(steps=args.cold_steps, flush_mib=args.flush_mib,
+                        step_ms_median=percentile(sorted(a.elapsed_time(b) for a, b in cev), 50),
+                        kernels={n: (t / c if c else 0.0) for n, (c, t) in ckern.items()})
+            del flush, sink
 
     ms = (t1 - t0) * 1e3 / args.steps
     kept = int(sum(st["kept"]))
@@ -208,6 +254,13 @@ def main():
     roof["algorithmic_bytes"] = g1_bytes
     roof["traffic_unit"] = "bytes per launch (HBM side, counters)"
     roof["source_digest"] = digest
+    if cold is not None:
+        cold_dom = cold["kernels"].get(dom, float("nan"))
+        cold_ach = (g1_bytes / (cold_dom * 1e-3) / 1e9 if hbm_bound
+                    else work["gemm1_flops"] / (cold_dom * 1e-3) / 1e12)
+        roof["cold"] = dict(kernel_ms=cold_dom, achieved=cold_ach, frac=cold_ach / roof["peak"],
+                            note=f"L2 and Infinity Cache flushed ({cold['flush_mib']} MiB "
+                                 f"read) before each of {cold['steps']} extra steps")
     layer_tflops = work["flops"] / (ms * 1e-3) / 1e12
     layer_gbs = work["bytes"] / (ms * 1e-3) / 1e9
     res = {
@@ -239,6 +292,9 @@ def main():
                   "entropy_load": st["entropy_load"], "entropy_token": st["entropy_token"],
                   "counts": [int(c) for c in st["counts"]]},
         "kernels": per_kernel,
+        "step_ms": {"median": percentile(step_ms, 50), "p10": percentile(step_ms, 10),
+                    "p90": percentile(step_ms, 90), "source": "HIP events around each timed step"},
+        "cold": cold,
     }
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or (64 if w.T > 64 else w.T)
