@@ -40,7 +40,13 @@ design notes):
 * load-balance statistics use pre-drop fractions f_i = count_i/(T*k) and the
   mean full softmax P_i over all E experts in both gating modes;
 * "routing entropy" is reported two ways: entropy of the expert-load
-  distribution and the mean per-token router entropy, both in nats.
+  distribution and the mean per-token router entropy, both in nats;
+* overflow policies other than dropping: a rerouted assignment goes, after
+  every first choice has taken its slot and in flat assignment order, to the
+  best-scoring expert (ties to the lower index) that the token did not choose
+  and that still has a free slot, and keeps its gate weight; with sequential
+  processing nothing is dropped, the output equals the unlimited layer's, and
+  the number of capacity-sized rounds of the busiest expert is reported.
 
 Nothing here is "parity unpinned": every function is checked by
 ``tests/test_oracle_pins.py`` against page values, closed forms, library
@@ -60,6 +66,16 @@ TOPK_THEN_SOFTMAX = 0  # Mixtral-style gating
 SOFTMAX_THEN_TOPK = 1  # DeepSeek-style gating
 
 
+# Overflow policies.  [Routing guide] "Plain explanation" paragraph 3: an
+# expert takes a fixed number of tokens per batch, and what exceeds it can
+# only be dropped (fast, costs quality), sent to spare experts (blurs
+# specialisation, costs coordination) or processed in full, round after round
+# (costs latency).
+OVERFLOW_DROP = 0
+OVERFLOW_REROUTE = 1
+OVERFLOW_SEQUENTIAL = 2
+
+
 @dataclass(frozen=True)
 class LayerShape:
     """Shape and routing options of one MoE layer call."""
@@ -73,6 +89,7 @@ class LayerShape:
     gating: int = TOPK_THEN_SOFTMAX
     renormalize: bool = True
     capacity_factor: float = 0.0   # <= 0: no limit
+    overflow: int = OVERFLOW_DROP
 
 
 # ---------------------------------------------------------------------------
@@ -223,6 +240,82 @@ def dispatch(sel: np.ndarray, E: int, C: int) -> dict:
                 dropped=int(np.sum(counts - kcount)), capacity=int(C))
 
 
+def dispatch_policy(sel: np.ndarray, logits: np.ndarray, E: int, C: int,
+                    policy: int = OVERFLOW_DROP) -> dict:
+    """Slots under one of the overflow policies of [Routing guide] "Plain
+    explanation" paragraph 3.  Returns what ``dispatch`` returns, plus
+    ``expert`` (the expert that processes each assignment, -1 if dropped),
+    ``overflowed`` (assignments that found their chosen expert full),
+    ``rerouted`` (of those, the ones a spare expert took) and ``rounds`` (the
+    capacity-sized rounds the busiest chosen expert needs; 0 for no tokens).
+
+    * drop: ``dispatch`` as it is;
+    * sequential: every assignment is processed by its chosen expert, in
+      rounds of C rows, so nothing is dropped;
+    * reroute: first choices take slots as in ``dispatch``; then every
+      assignment that found its expert full, in flat order a = t*k + j, goes
+      to the best-scoring expert of token t (ties to the lower index) among
+      those t did not choose that still have a free slot, after the rows
+      already there; with no such expert it is dropped.
+    """
+    T, k = sel.shape
+    d = dispatch(sel, E, C)
+    flat = [int(v) for v in sel.reshape(-1)]
+    rank = [int(r) for r in d["rank"]]
+    overflowed = sum(1 for r in rank if r >= C)
+    rounds = max([-(-int(c) // C) for c in d["counts"] if c > 0], default=0)
+    if policy == OVERFLOW_SEQUENTIAL:
+        full = dispatch(sel, E, max(T, 1))    # no token picks an expert twice
+        full.update(capacity=int(C), expert=np.asarray(flat, dtype=np.int64),
+                    overflowed=overflowed, rerouted=0, rounds=rounds)
+        return full
+    expert = np.array([e if r < C else -1 for e, r in zip(flat, rank)],
+                      dtype=np.int64)
+    d.update(expert=expert, overflowed=overflowed, rerouted=0, rounds=rounds)
+    if policy == OVERFLOW_DROP or overflowed == 0:
+        return d
+    if policy != OVERFLOW_REROUTE:
+        raise ValueError(f"unknown overflow policy {policy}")
+
+    scores = np.asarray(logits, dtype=np.float64)
+    fill = [int(v) for v in d["kept"]]        # rows per expert so far
+    extra = [[] for _ in range(E)]            # rerouted assignments, in order
+    for a in range(len(flat)):
+        if expert[a] >= 0:
+            continue
+        t = a // k
+        chosen = set(flat[t * k:(t + 1) * k])
+        best = -1
+        for c in range(E):
+            if c in chosen or fill[c] >= C:
+                continue
+            if best < 0 or scores[t, c] > scores[t, best]:
+                best = c                      # strict >: a tie keeps the lower index
+        if best >= 0:
+            expert[a] = best
+            extra[best].append(a)
+            fill[best] += 1
+
+    kept = np.array(fill, dtype=np.int64)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + kept[e]
+    slot = np.full(len(flat), -1, dtype=np.int64)
+    perm = np.full(int(offsets[E]), -1, dtype=np.int64)
+    for a, e in enumerate(flat):              # first choices keep their places
+        if rank[a] < C:
+            slot[a] = offsets[e] + rank[a]
+            perm[slot[a]] = a
+    for e in range(E):                        # rerouted rows follow them
+        for i, a in enumerate(extra[e]):
+            slot[a] = offsets[e] + int(d["kept"][e]) + i
+            perm[slot[a]] = a
+    rerouted = sum(len(x) for x in extra)
+    d.update(kept=kept, offsets=offsets, slot=slot, perm=perm,
+             rerouted=rerouted, dropped=overflowed - rerouted)
+    return d
+
+
 # ---------------------------------------------------------------------------
 # Expert FFN.  [Mixtral explainer] "Plain explanation" paragraph 2: the
 # feed-forward block widens the token vector (about 4k) to a hidden width
@@ -317,7 +410,7 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
     w = gate_weights(logits, sel, shape.gating, shape.renormalize)
     p = softmax_all(logits) if T > 0 else np.zeros((0, E))
     C = capacity(T, k, E, shape.capacity_factor)
-    disp = dispatch(sel, E, C)
+    disp = dispatch_policy(sel, logits, E, C, shape.overflow)
     stats = routing_stats(disp["counts"], disp["kept"], p, T, k, E)
 
     want = np.zeros(T, dtype=bool)

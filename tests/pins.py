@@ -242,10 +242,12 @@ def pin_ffn_library(O):
     assert np.allclose(O.silu(u), ref.numpy(), rtol=1e-15, atol=0)
 
 
-def _shape(O, T, d, F, E, k, S=0, gating=None, renorm=True, cf=0.0):
+def _shape(O, T, d, F, E, k, S=0, gating=None, renorm=True, cf=0.0,
+           overflow=None):
     return O.LayerShape(T=T, d=d, F=F, E=E, k=k, S=S,
                         gating=O.TOPK_THEN_SOFTMAX if gating is None else gating,
-                        renormalize=renorm, capacity_factor=cf)
+                        renormalize=renorm, capacity_factor=cf,
+                        overflow=O.OVERFLOW_DROP if overflow is None else overflow)
 
 
 def pin_dense_equivalence(O):
@@ -344,6 +346,200 @@ def pin_drop_semantics(O):
         assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
     assert res["stats"]["dropped"] == 2
     assert list(res["dispatch"]["counts"]) == [5, 3, 2]
+
+
+# ---------------------------------------------------------------- overflow
+# [Routing guide] "Plain explanation" paragraph 3 names three ways to handle
+# assignments beyond an expert's capacity: drop them, send them to spare
+# experts, or process everything in rounds.
+def pin_reroute_hand_example(O):
+    # Two tokens, four experts, top-2, one slot each (2 x 2 x 0.5 / 4 = 1).
+    # Token 0 takes experts 0 and 1.  Token 1 also wants 0 and 1, finds both
+    # full, and its spare experts are 2 and 3 with equal scores: its first
+    # overflow (a=2) goes to the lower index, 2; its second (a=3) finds 2 full
+    # and goes to 3.  Both keep their own gate weights.
+    L = np.array([[4.0, 3.0, 1.0, 1.0],
+                  [4.0, 3.0, 2.0, 2.0]])
+    assert O.capacity(2, 2, 4, 0.5) == 1
+    sel, _ = O.topk_select(L, 2)
+    D = O.dispatch_policy(sel, L, 4, 1, O.OVERFLOW_REROUTE)
+    assert list(D["expert"]) == [0, 1, 2, 3]
+    assert list(D["slot"]) == [0, 1, 2, 3]
+    assert list(D["kept"]) == [1, 1, 1, 1]
+    assert (D["overflowed"], D["rerouted"], D["dropped"], D["rounds"]) == (2, 2, 0, 2)
+    assert list(D["counts"]) == [2, 2, 0, 0]
+    # First choices are placed before any rerouted row: expert 2 is token 2's
+    # own choice, so token 1's overflow (a=1) must skip it and take expert 1,
+    # and token 3's overflow finds nothing free and is dropped.
+    L = np.array([[5.0, 1.0, 1.0],
+                  [5.0, 2.0, 3.0],
+                  [0.0, 0.0, 6.0],
+                  [5.0, 1.0, 0.0]])
+    sel, _ = O.topk_select(L, 1)
+    D = O.dispatch_policy(sel, L, 3, 1, O.OVERFLOW_REROUTE)
+    assert list(D["expert"]) == [0, 1, 2, -1]
+    assert list(D["slot"]) == [0, 1, 2, -1]
+    assert list(D["perm"]) == [0, 1, 2]
+    assert (D["overflowed"], D["rerouted"], D["dropped"], D["rounds"]) == (2, 1, 1, 3)
+    # The same call under the other policies.
+    D = O.dispatch_policy(sel, L, 3, 1, O.OVERFLOW_DROP)
+    assert list(D["expert"]) == [0, -1, 2, -1] and D["dropped"] == 2
+    D = O.dispatch_policy(sel, L, 3, 1, O.OVERFLOW_SEQUENTIAL)
+    assert list(D["expert"]) == [0, 0, 2, 0] and D["dropped"] == 0
+    assert list(D["perm"]) == [0, 1, 3, 2] and D["rounds"] == 3
+
+
+def _check_reroute(O, sel, L, E, C, D):
+    """Checks a rerouted dispatch against the rules it must follow, without
+    recomputing it: capacity, first choices untouched, one row per token and
+    expert, spare experts only, greedy best choice, drops only when full."""
+    T, k = sel.shape
+    flat = [int(v) for v in sel.reshape(-1)]
+    base = O.dispatch(sel, E, C)
+    ex = [int(v) for v in D["expert"]]
+    assert np.all(D["kept"] <= C)
+    assert np.array_equal(np.diff(D["offsets"]), D["kept"])
+    assert int(D["kept"].sum()) + D["dropped"] == T * k
+    assert D["rerouted"] + D["dropped"] == base["dropped"] == D["overflowed"]
+    for a in range(T * k):
+        if base["slot"][a] >= 0:                      # first choice kept
+            e = flat[a]
+            assert ex[a] == e
+            assert D["slot"][a] - D["offsets"][e] == base["slot"][a] - base["offsets"][e]
+    for e in range(E):                                # primaries lead each expert
+        lo = int(D["offsets"][e])
+        mine = [int(a) for a in D["perm"][lo:int(D["offsets"][e + 1])]]
+        assert mine[:int(base["kept"][e])] == [int(a) for a in base["perm"][int(base["offsets"][e]):int(base["offsets"][e + 1])]]
+        assert mine == sorted(mine[:int(base["kept"][e])]) + sorted(mine[int(base["kept"][e]):])
+        assert all(ex[a] == e for a in mine)
+    for t in range(T):                                # one row per token/expert
+        placed = [ex[a] for a in range(t * k, t * k + k) if ex[a] >= 0]
+        assert len(placed) == len(set(placed))
+    # Occupancy of each expert just before overflow assignment a is handled:
+    # its first choices plus the rerouted rows of earlier assignments.
+    for a in range(T * k):
+        if base["slot"][a] >= 0:
+            continue
+        t = a // k
+        chosen = set(flat[t * k:t * k + k])
+        occ = [int(base["kept"][c]) + sum(1 for b in range(a) if base["slot"][b] < 0 and ex[b] == c)
+               for c in range(E)]
+        free = [c for c in range(E) if c not in chosen and occ[c] < C]
+        if ex[a] < 0:
+            assert not free
+        else:
+            c = ex[a]
+            assert c in free
+            for c2 in free:                           # nothing free was better
+                assert (L[t, c2], -c2) <= (L[t, c], -c)
+
+
+def pin_reroute_rules(O):
+    r = _rng(13)
+    for (T, E, k, C) in [(40, 4, 2, 12), (33, 6, 2, 5), (64, 8, 2, 10), (25, 5, 3, 9),
+                         (30, 8, 1, 2), (16, 4, 1, 1), (20, 3, 2, 7)]:
+        for rep in range(3):
+            L = r.standard_normal((T, E))
+            L[:, 0] += 1.5
+            if rep == 1:
+                L = np.round(L)                      # many exact ties
+            sel, _ = O.topk_select(L, k)
+            D = O.dispatch_policy(sel, L, E, C, O.OVERFLOW_REROUTE)
+            _check_reroute(O, sel, L, E, C, D)
+
+
+def pin_reroute_degenerate(O):
+    r = _rng(14)
+    L = r.standard_normal((30, 4))
+    L[:, 1] += 2.0
+    # k = E: no token has a spare expert, so rerouting is dropping.
+    sel, _ = O.topk_select(L, 4)
+    a = O.dispatch_policy(sel, L, 4, 20, O.OVERFLOW_REROUTE)
+    b = O.dispatch(sel, 4, 20)
+    assert a["rerouted"] == 0 and a["dropped"] == b["dropped"] == 40
+    assert list(a["perm"]) == list(b["perm"])
+    # Room for everything: all three policies place every assignment alike.
+    sel, _ = O.topk_select(L, 2)
+    for pol in (O.OVERFLOW_DROP, O.OVERFLOW_REROUTE, O.OVERFLOW_SEQUENTIAL):
+        D = O.dispatch_policy(sel, L, 4, 30, pol)
+        assert D["dropped"] == 0 and D["overflowed"] == 0 and D["rounds"] == 1
+        assert list(D["perm"]) == list(O.dispatch(sel, 4, 30)["perm"])
+    # Total capacity E x C covers all T x k assignments and every token has a
+    # spare expert for each overflow: nothing is dropped (T=8, k=1, C=2).
+    L = np.zeros((8, 4))
+    L[:, 0] = 1.0
+    sel, _ = O.topk_select(L, 1)
+    D = O.dispatch_policy(sel, L, 4, 2, O.OVERFLOW_REROUTE)
+    assert D["dropped"] == 0 and list(D["kept"]) == [2, 2, 2, 2]
+    assert list(D["expert"]) == [0, 0, 1, 1, 2, 2, 3, 3]   # ties: lowest index
+    # No tokens.
+    D = O.dispatch_policy(np.zeros((0, 2), np.int64), np.zeros((0, 4)), 4, 0,
+                          O.OVERFLOW_REROUTE)
+    assert D["rounds"] == 0 and D["dropped"] == 0 and len(D["perm"]) == 0
+
+
+def pin_sequential_rounds(O):
+    # Every token on expert 0 (k=1): C = ceil(T cf / E) slots, so the busiest
+    # expert needs ceil(T / C) rounds; 2048 tokens, 8 experts, factor 1.25
+    # give 320 slots and 7 rounds.
+    for (T, E, cf, C, R) in [(2048, 8, 1.25, 320, 7), (10, 4, 1.0, 3, 4),
+                             (5, 5, 1.0, 1, 5), (7, 2, 2.0, 7, 1)]:
+        sel = np.zeros((T, 1), dtype=np.int64)
+        L = np.zeros((T, E))
+        L[:, 0] = 1.0
+        assert O.capacity(T, 1, E, cf) == C
+        D = O.dispatch_policy(sel, L, E, C, O.OVERFLOW_SEQUENTIAL)
+        assert D["rounds"] == R and D["dropped"] == 0
+        assert D["overflowed"] == T - C
+        assert list(D["kept"]) == [T] + [0] * (E - 1)
+        assert list(D["perm"]) == list(range(T))
+
+
+def pin_overflow_forward(O):
+    r = _rng(15)
+    T, d, F, E, k = 24, 8, 12, 6, 2
+    x = r.standard_normal((T, d))
+    ex = _experts(E, d, F, 150)
+    Wg = r.standard_normal((d, E))
+    bias = np.array([2.0, 1.0, 0.0, 0.0, -1.0, -2.0])
+    free = O.forward(x, _shape(O, T, d, F, E, k), lambda e: ex[e], W_gate=Wg,
+                     bias=bias)
+    # Sequential processing drops nothing: the unlimited layer, exactly.
+    seq = O.forward(x, _shape(O, T, d, F, E, k, cf=0.5,
+                              overflow=O.OVERFLOW_SEQUENTIAL),
+                    lambda e: ex[e], W_gate=Wg, bias=bias)
+    assert seq["capacity"] == 4 and seq["dispatch"]["rounds"] == 4
+    assert np.array_equal(seq["out"], free["out"])
+    assert seq["stats"]["dropped"] == 0
+    # With identical experts the expert that runs a row does not matter: a
+    # rerouted row keeps its gate weight, so a reroute that drops nothing
+    # gives the unlimited layer.
+    one = _experts(1, d, F, 151)[0]
+    ref = O.forward(x, _shape(O, T, d, F, E, k), lambda e: one, W_gate=Wg,
+                    bias=bias)
+    rr = O.forward(x, _shape(O, T, d, F, E, k, cf=1.0,
+                             overflow=O.OVERFLOW_REROUTE),
+                   lambda e: one, W_gate=Wg, bias=bias)
+    D = rr["dispatch"]
+    assert D["rerouted"] > 0 and D["dropped"] == 0
+    assert np.allclose(rr["out"], ref["out"], rtol=1e-12, atol=1e-12)
+    # Distinct experts: each token's output is the gate-weighted sum over the
+    # experts that actually ran its rows.
+    rr = O.forward(x, _shape(O, T, d, F, E, k, cf=0.75,
+                             overflow=O.OVERFLOW_REROUTE),
+                   lambda e: ex[e], W_gate=Wg, bias=bias)
+    D = rr["dispatch"]
+    assert D["rerouted"] > 0 and D["dropped"] > 0
+    y = [_torch_ffn(x, *ex[e]) for e in range(E)]
+    for t in range(T):
+        want = np.zeros(d)
+        for j in range(k):
+            e = int(D["expert"][t * k + j])
+            if e >= 0:
+                want += rr["w"][t, j] * y[e][t]
+        assert np.allclose(rr["out"][t], want, rtol=1e-12, atol=1e-12)
+    assert rr["stats"]["dropped"] == D["dropped"]
+    assert np.isclose(rr["stats"]["overflow_rate"], D["dropped"] / (T * k))
 
 
 # ---------------------------------------------------------------- stats

@@ -143,7 +143,92 @@ def _ffn_relu(X, W1, W3, W2):
     return h @ np.asarray(W2, np.float64)
 
 
+def _reroute_variant(mode):
+    """A rerouting dispatch built on the drop dispatch with one planted
+    mistake: 'high' breaks score ties to the higher index, 'own' lets an
+    overflow land on another of the token's own choices, 'worst' takes the
+    lowest-scoring spare expert, 'onepass' handles assignments strictly in
+    flat order so a later first choice can find its slot taken, 'weightless'
+    runs rerouted rows but leaves them out of the combine."""
+    def fn(sel, logits, E, C, policy=O.OVERFLOW_DROP):
+        if policy != O.OVERFLOW_REROUTE:
+            return _orig["dispatch_policy"](sel, logits, E, C, policy)
+        T, k = sel.shape
+        flat = [int(v) for v in sel.reshape(-1)]
+        D = _orig["dispatch"](sel, E, C)
+        fill = [0] * E
+        expert = [-1] * len(flat)
+        primary = [r < C for r in D["rank"]]
+        if mode == "onepass":
+            primary = [False] * len(flat)
+        for a, e in enumerate(flat):
+            if primary[a]:
+                expert[a] = e
+                fill[e] += 1
+        for a, e in enumerate(flat):
+            if primary[a]:
+                continue
+            if mode == "onepass" and fill[e] < C:
+                expert[a] = e
+                fill[e] += 1
+                continue
+            t = a // k
+            chosen = set(flat[t * k:(t + 1) * k])
+            cand = [c for c in range(E) if fill[c] < C and (mode == "own" or c not in chosen)]
+            if mode == "own":
+                cand = [c for c in cand if c != e]
+            if not cand:
+                continue
+            key = {"high": lambda c: (logits[t, c], c),
+                   "worst": lambda c: (-logits[t, c], -c)}.get(mode, lambda c: (logits[t, c], -c))
+            best = max(cand, key=key)
+            expert[a] = best
+            fill[best] += 1
+        offsets = np.concatenate([[0], np.cumsum(fill)]).astype(np.int64)
+        slot = np.full(len(flat), -1, dtype=np.int64)
+        perm = []
+        for e in range(E):
+            first = [a for a in range(len(flat)) if expert[a] == e and flat[a] == e and (primary[a] or mode == "onepass")]
+            rest = [a for a in range(len(flat)) if expert[a] == e and a not in first]
+            for a in first + rest:
+                slot[a] = len(perm)
+                perm.append(a)
+        moved = sum(1 for a in range(len(flat)) if expert[a] >= 0 and expert[a] != flat[a])
+        over = int(D["dropped"])
+        out = dict(D)
+        out.update(kept=np.array(fill, dtype=np.int64), offsets=offsets, slot=slot,
+                   perm=np.array(perm, dtype=np.int64), expert=np.array(expert, dtype=np.int64),
+                   overflowed=over, rerouted=moved, dropped=len(flat) - sum(fill),
+                   rounds=_orig["dispatch_policy"](sel, logits, E, C, O.OVERFLOW_DROP)["rounds"])
+        if mode == "weightless":
+            keep = [a for a in perm if expert[a] == flat[a]]
+            out["perm"] = np.array(keep, dtype=np.int64)
+            out["offsets"] = np.concatenate([[0], np.cumsum(
+                [sum(1 for a in keep if expert[a] == e) for e in range(E)])]).astype(np.int64)
+        return out
+    return fn
+
+
+def _sequential_as_drop(sel, logits, E, C, policy=O.OVERFLOW_DROP):
+    if policy == O.OVERFLOW_SEQUENTIAL:
+        policy = O.OVERFLOW_DROP
+    return _orig["dispatch_policy"](sel, logits, E, C, policy)
+
+
+def _rounds_floor(sel, logits, E, C, policy=O.OVERFLOW_DROP):
+    D = _orig["dispatch_policy"](sel, logits, E, C, policy)
+    D["rounds"] = max([int(c) // max(C, 1) for c in D["counts"]], default=0)
+    return D
+
+
 MUTATIONS = {
+    "reroute_ties_to_high_index": ("dispatch_policy", _reroute_variant("high")),
+    "reroute_onto_own_choice": ("dispatch_policy", _reroute_variant("own")),
+    "reroute_to_worst_spare": ("dispatch_policy", _reroute_variant("worst")),
+    "reroute_single_pass": ("dispatch_policy", _reroute_variant("onepass")),
+    "reroute_rows_not_combined": ("dispatch_policy", _reroute_variant("weightless")),
+    "sequential_drops": ("dispatch_policy", _sequential_as_drop),
+    "rounds_rounded_down": ("dispatch_policy", _rounds_floor),
     "dispatch_drops_earliest": ("dispatch", _drop_earliest),
     "silu_on_w3_branch": ("expert_ffn", _silu_on_w3),
     "w2_transposed": ("expert_ffn", _w2_transposed),
