@@ -17,9 +17,10 @@
  *      softmax over the k chosen scores (Mixtral) or the full softmax over all
  *      E experts read at the chosen ones (DeepSeek), optionally renormalised
  *      [Mixtral explainer] para 3; [Routing guide] paras 2 and 4
- *   3. dispatch with capacity C = ceil(T*k*cf/E) slots per expert; excess
- *      assignments, latest first in flat order a = t*k + j, are dropped
- *      [Routing guide] "Plain explanation" paras 3 and 5
+ *   3. dispatch with capacity C = ceil(T*k*cf/E) slots per expert; the
+ *      assignments beyond C (the latest in flat order a = t*k + j) are
+ *      dropped, sent to spare experts or kept for later rounds
+ *      (moe_overflow_t)   [Routing guide] "Plain explanation" paras 3 and 5
  *   4. expert FFN, SwiGLU: y = (silu(x W1[e]) * (x W3[e])) W2[e]
  *      [Mixtral explainer] "Plain explanation" para 2
  *   5. out = sum over kept j of w[t,j] * y[t,j]  +  sum of S shared experts
@@ -90,6 +91,26 @@ typedef enum {
                             each expert's weights through many CUs */
 } moe_ffn_path_t;
 
+/* What happens to assignments beyond an expert's C slots.  [Routing guide]
+ * "Plain explanation" para 3 names the three choices.  In every policy an
+ * expert first takes its own assignments in flat order a = t*k + j, up to C.
+ *   DROP        the rest contribute nothing.
+ *   REROUTE     then the rest, in flat order, each go to the highest-scoring
+ *               expert (ties: lower index) that token t did not choose and
+ *               that still has a free slot, placed after the rows already
+ *               there, with their own gate weight; dropped if none has room.
+ *               Runs a one-workgroup pass; short batches lose the fused
+ *               single-kernel routing.
+ *   SEQUENTIAL  nothing is dropped: every assignment is processed by its
+ *               expert, as if in rounds of C rows (one launch runs all the
+ *               rounds' rows, so the output equals the unlimited layer and
+ *               the workspace holds T*k rows); stats report the rounds. */
+typedef enum {
+  MOE_OVERFLOW_DROP = 0,
+  MOE_OVERFLOW_REROUTE = 1,
+  MOE_OVERFLOW_SEQUENTIAL = 2
+} moe_overflow_t;
+
 typedef struct {
   int64_t T;             /* tokens in this call, >= 0 */
   int32_t d_model;       /* d */
@@ -106,19 +127,26 @@ typedef struct {
   void* workspace;       /* device scratch, see moe_workspace_size */
   size_t workspace_bytes;
   void* stream;          /* hipStream_t */
+  int32_t overflow;      /* moe_overflow_t (0 = drop) */
 } moe_config_t;
 
 typedef struct {
   int64_t capacity;      /* C */
   int64_t assignments;   /* T * k */
-  int64_t dropped;       /* assignments beyond capacity */
+  int64_t dropped;       /* assignments no expert processes */
   int64_t* counts;       /* host [E] per-expert assignments before drops, or NULL */
-  int64_t* kept;         /* host [E] per-expert assignments kept, or NULL */
+  int64_t* kept;         /* host [E] rows each expert processes (rerouted
+                            rows included), or NULL */
   double aux_loss;       /* E * sum f_i P_i, f_i = counts_i / (T k) */
   double aux_loss_kept;  /* same with kept counts */
   double overflow_rate;  /* dropped / (T k) */
   double entropy_load;   /* -sum f_i ln f_i */
   double entropy_token;  /* mean over tokens of -sum_i p_ti ln p_ti */
+  int64_t overflowed;    /* sum_i max(counts_i - C, 0): assignments that found
+                            their chosen expert full */
+  int64_t rerouted;      /* of those, placed on a spare expert (REROUTE) */
+  int64_t rounds;        /* max_i ceil(counts_i / C): C-row rounds the busiest
+                            chosen expert needs (0 when T = 0) */
 } moe_stats_t;
 
 /* Validate cfg without touching the GPU.  Bounds: T >= 0, T*k < 2^31,
@@ -152,7 +180,9 @@ int moe_forward(const void* x, const void* W_gate, const void* W1,
  *   offsets  [E+1]  int32 exclusive prefix sum of kept counts
  *   perm     [T*k]  int32 perm[s] = assignment a = t*k + j held in slot s;
  *                          entries at and after offsets[E] are -1
- *   slot     [T*k]  int32 slot of assignment a, or -1 when dropped
+ *   slot     [T*k]  int32 slot of assignment a, or -1 when dropped; the
+ *                          expert that processes it is the e with
+ *                          offsets[e] <= slot < offsets[e+1]
  * Any output pointer except topk_idx may be NULL to skip it. */
 int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg,
               float* logits, int32_t* topk_idx, float* topk_w,

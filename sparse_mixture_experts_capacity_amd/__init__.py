@@ -17,7 +17,8 @@ import numpy as np
 from ._lib import (LIB, MoeConfig, MoeStats, MoeError, MOE_OK, MOE_EINVAL,  # noqa: F401
                    MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, DTYPE_F32,
                    DTYPE_BF16, TOPK_THEN_SOFTMAX, SOFTMAX_THEN_TOPK, PATH_AUTO,
-                   PATH_GROUPED, PATH_STREAM, EXPORTED_SYMBOLS)
+                   PATH_GROUPED, PATH_STREAM, OVERFLOW_DROP, OVERFLOW_REROUTE,
+                   OVERFLOW_SEQUENTIAL, EXPORTED_SYMBOLS)
 
 __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
@@ -50,7 +51,7 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
                 renormalize: bool = True, capacity_factor: float = 0.0,
                 dtype: str = "bf16", ffn_path: int = PATH_AUTO,
                 logit_bias=None, workspace=None, workspace_bytes: int = 0,
-                stream=0) -> MoeConfig:
+                stream=0, overflow: int = OVERFLOW_DROP) -> MoeConfig:
     """Fill a moe_config_t.  ``stream`` = None means torch's current stream."""
     c = MoeConfig()
     c.T = int(T)
@@ -68,6 +69,7 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
     c.workspace = _ptr(workspace)
     c.workspace_bytes = int(workspace_bytes)
     c.stream = _stream_handle(stream) if stream != 0 else None
+    c.overflow = int(overflow)
     return c
 
 
@@ -126,7 +128,8 @@ def _stats_dict(st, counts, kept) -> dict:
                 dropped=st.dropped, counts=counts.copy(), kept=kept.copy(),
                 aux_loss=st.aux_loss, aux_loss_kept=st.aux_loss_kept,
                 overflow_rate=st.overflow_rate, entropy_load=st.entropy_load,
-                entropy_token=st.entropy_token)
+                entropy_token=st.entropy_token, overflowed=st.overflowed,
+                rerouted=st.rerouted, rounds=st.rounds)
 
 
 def moe_forward(x, W_gate, W1, W3, W2, cfg: MoeConfig, out,

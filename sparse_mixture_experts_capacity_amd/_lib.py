@@ -13,6 +13,7 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 TOPK_THEN_SOFTMAX, SOFTMAX_THEN_TOPK = 0, 1
 PATH_AUTO, PATH_GROUPED, PATH_STREAM = 0, 1, 2
+OVERFLOW_DROP, OVERFLOW_REROUTE, OVERFLOW_SEQUENTIAL = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -38,6 +39,7 @@ class MoeConfig(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("overflow", ctypes.c_int32),
     ]
 
 
@@ -53,6 +55,9 @@ class MoeStats(ctypes.Structure):
         ("overflow_rate", ctypes.c_double),
         ("entropy_load", ctypes.c_double),
         ("entropy_token", ctypes.c_double),
+        ("overflowed", ctypes.c_int64),
+        ("rerouted", ctypes.c_int64),
+        ("rounds", ctypes.c_int64),
     ]
 
 

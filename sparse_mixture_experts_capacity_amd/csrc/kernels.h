@@ -19,11 +19,21 @@ hipError_t launch_topk_gate(const float* lpart, int nsplit, int64_t split_stride
                             int k, int gating, int renorm, int32_t* topk_idx,
                             float* topk_w, float* Ppart, float* Hpart,
                             int nblocks, int tokens_per_block, hipStream_t s);
+// Overflow sent to spare experts: the full router scores [T, E] fp32 (as the
+// top-k pass saw them) and three int32 [T*k] scratch arrays.
+struct Reroute {
+  const float* logits;
+  int k;
+  int32_t* ovf;
+  int32_t* xdest;
+  int32_t* xrel;
+};
+// rr == nullptr: assignments beyond capacity C are dropped.
 hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* lrank, int32_t* blkcnt, int32_t* counts,
                            int32_t* kcount, int32_t* offsets, int32_t* slot,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
-                           int32_t* tstart, hipStream_t s);
+                           int32_t* tstart, const Reroute* rr, hipStream_t s);
 // Short batches: top-k, gates and the whole dispatch in one workgroup
 // (T <= kSmallT, T * k <= kSmallTK); results equal launch_topk_gate with one
 // block followed by launch_dispatch.

@@ -122,7 +122,9 @@ struct Plan {
   bool bf16 = false;
   int path = MOE_PATH_GROUPED;   // resolved
   int64_t capacity = 0;          // exact C
-  int Ceff = 0;                  // min(C, T): the value that can bind
+  int overflow = MOE_OVERFLOW_DROP;
+  int Ceff = 0;                  // rows per expert the dispatch keeps: min(C, T),
+                                 // or T when nothing is dropped (sequential)
   int64_t TK = 0;
   int64_t rows_max = 0;          // most kept rows possible
   int nblk_dispatch = 0;
@@ -139,7 +141,7 @@ struct Plan {
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
   // workspace regions
   Region logits, lpart, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
-      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb;
+      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb, ovf, xdest, xrel;
   size_t total = 0;
 };
 
@@ -204,6 +206,8 @@ int check(const moe_config_t* c) {
     return fail(MOE_EINVAL, "dtype = %d is not a moe_dtype_t", c->dtype);
   if (c->ffn_path < MOE_PATH_AUTO || c->ffn_path > MOE_PATH_STREAM)
     return fail(MOE_EINVAL, "ffn_path = %d is not a moe_ffn_path_t", c->ffn_path);
+  if (c->overflow < MOE_OVERFLOW_DROP || c->overflow > MOE_OVERFLOW_SEQUENTIAL)
+    return fail(MOE_EINVAL, "overflow = %d is not a moe_overflow_t", c->overflow);
   if (isnan(c->capacity_factor) || c->capacity_factor > 1e6)
     return fail(MOE_EINVAL, "capacity_factor must be a number <= 1e6");
   if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
@@ -256,7 +260,11 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->path = c->ffn_path;
   p->capacity = exact_capacity(c->T, c->top_k, c->n_experts, c->capacity_factor);
   if (p->capacity < 0) return fail(MOE_EINVAL, "capacity_factor is not finite");
+  p->overflow = c->overflow;
   p->Ceff = static_cast<int>(p->capacity < p->T ? p->capacity : p->T);
+  // Sequential rounds keep every assignment: one launch runs all the rounds'
+  // rows, so the dispatch sees no limit (the rounds are reported).
+  if (p->overflow == MOE_OVERFLOW_SEQUENTIAL) p->Ceff = static_cast<int>(p->T);
   p->TK = p->T * p->k;
   p->rows_max = p->TK;
   if (static_cast<int64_t>(p->E) * p->Ceff < p->rows_max) p->rows_max = static_cast<int64_t>(p->E) * p->Ceff;
@@ -270,7 +278,8 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->topk_blocks = static_cast<int>((p->T + tpb - 1) / tpb);
   // Short batches: top-k, gates and dispatch run as one kernel in one
   // workgroup (its softmax statistics come as a single partial row).
-  p->small_route = p->T > 0 && p->T <= moe::kSmallT && p->TK <= moe::kSmallTK;
+  p->small_route = p->T > 0 && p->T <= moe::kSmallT && p->TK <= moe::kSmallTK &&
+                   p->overflow != MOE_OVERFLOW_REROUTE;
   if (p->small_route) {
     p->topk_blocks = 1;
     p->topk_tpb = static_cast<int>(p->T);
@@ -364,6 +373,10 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
   add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
   add(p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur);
+  const size_t rr = p->overflow == MOE_OVERFLOW_REROUTE ? sizeof(int32_t) * p->TK : 0;
+  add(p->ovf, rr, cur);
+  add(p->xdest, rr, cur);
+  add(p->xrel, rr, cur);
   p->total = cur;
   return MOE_OK;
 }
@@ -425,9 +438,26 @@ int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
 }
 
 // Steps 2-3 (top-k, gates, dispatch) from router scores `sc`; the summed
-// scores are also written to logits_out when it is given.
+// scores are also written to logits_out when it is given.  Rerouting reads
+// the full scores again: complete ones in place, partial sums as the top-k
+// pass stores them (in logits_out, else in the workspace).
 int run_route(const Plan& p, void* ws, const Scores& sc, float* logits_out, int32_t* idx,
               float* w, hipStream_t s) {
+  moe::Reroute rr{};
+  const moe::Reroute* rrp = nullptr;
+  if (p.overflow == MOE_OVERFLOW_REROUTE) {
+    if (sc.nsplit == 1 && sc.bias == nullptr) {
+      rr.logits = sc.lsrc;
+    } else {
+      if (!logits_out) logits_out = at<float>(ws, p.logits);
+      rr.logits = logits_out;
+    }
+    rr.k = p.k;
+    rr.ovf = at<int32_t>(ws, p.ovf);
+    rr.xdest = at<int32_t>(ws, p.xdest);
+    rr.xrel = at<int32_t>(ws, p.xrel);
+    rrp = &rr;
+  }
   if (p.small_route) {
     Timed t("route_small", s);
     HIP_TRY(moe::launch_route_small(
@@ -452,7 +482,7 @@ int run_route(const Plan& p, void* ws, const Scores& sc, float* logits_out, int3
                                  at<int32_t>(ws, p.kcount), at<int32_t>(ws, p.offsets),
                                  at<int32_t>(ws, p.slot), at<int32_t>(ws, p.perm), p.bm,
                                  at<moe::Tile>(ws, p.tiles), at<int32_t>(ws, p.ntiles),
-                                 at<int32_t>(ws, p.tstart), s));
+                                 at<int32_t>(ws, p.tstart), rrp, s));
   }
   return MOE_OK;
 }
@@ -463,6 +493,9 @@ int fill_stats(const Plan& p, void* ws, hipStream_t s, moe_stats_t* st,
   st->capacity = p.capacity;
   st->assignments = p.TK;
   st->dropped = 0;
+  st->overflowed = 0;
+  st->rerouted = 0;
+  st->rounds = 0;
   if (p.T == 0) {
     if (st->counts) memset(st->counts, 0, sizeof(int64_t) * p.E);
     if (st->kept) memset(st->kept, 0, sizeof(int64_t) * p.E);
@@ -491,6 +524,17 @@ int fill_stats(const Plan& p, void* ws, hipStream_t s, moe_stats_t* st,
     if (st->counts) st->counts[e] = cnt[e];
     if (st->kept) st->kept[e] = kc[e];
   }
+  // Assignments beyond their chosen expert's C slots, and the C-row rounds
+  // the busiest chosen expert needs; what is not dropped of the overflow
+  // went to spare experts or to later rounds.
+  for (int e = 0; e < p.E; ++e) {
+    if (cnt[e] > p.capacity) st->overflowed += cnt[e] - p.capacity;
+    if (cnt[e] > 0 && p.capacity > 0) {
+      const int64_t r = (cnt[e] + p.capacity - 1) / p.capacity;
+      if (r > st->rounds) st->rounds = r;
+    }
+  }
+  if (p.overflow == MOE_OVERFLOW_REROUTE) st->rerouted = st->overflowed - st->dropped;
   return MOE_OK;
 }
 

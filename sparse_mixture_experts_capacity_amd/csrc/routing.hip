@@ -344,6 +344,44 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Slot offsets (exclusive prefix sum of the kept counts kc, in LDS) and the
+// M-tile list of the grouped expert GEMMs: tiles of at most `bm` rows, expert
+// by expert, with tstart[e] the first tile of expert e and tstart[E] their
+// number.  Called by every thread of one workgroup (blockDim.x >= 1); off and
+// toff are LDS arrays of E + 1 entries.
+// ---------------------------------------------------------------------------
+__device__ void slot_offsets_and_tiles(const int* kc, int E, int bm, int* off, int* toff,
+                                       int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
+                                       int32_t* __restrict__ ntiles,
+                                       int32_t* __restrict__ tstart) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int so = 0, ts = 0;
+    for (int i = 0; i < E; ++i) {
+      off[i] = so;
+      toff[i] = ts;
+      so += kc[i];
+      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+    }
+    off[E] = so;
+    toff[E] = ts;
+    if (ntiles) *ntiles = ts;
+  }
+  __syncthreads();
+  for (int i = tid; i <= E; i += blockDim.x) {
+    offsets[i] = off[i];
+    if (tstart) tstart[i] = toff[i];
+  }
+  if (tiles && bm > 0) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      int n = 0;
+      for (int r = 0; r < kc[e]; r += bm, ++n)
+        tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch, pass 2 (one workgroup): per expert, turn chunk totals into
 // exclusive chunk bases (in place) and the total count; apply the capacity;
 // prefix-sum the kept counts into slot offsets; build the M-tile list of the
@@ -372,28 +410,147 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
     kcount[e] = kc[e];
   }
   __syncthreads();
-  if (e == 0) {
-    int s = 0, ts = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = s;
-      toff[i] = ts;
-      s += kc[i];
-      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+  slot_offsets_and_tiles(kc, E, bm, off, toff, offsets, tiles, ntiles, tstart);
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch, pass 2b (one workgroup of 1024 threads), only when overflow is
+// sent to spare experts ([Routing guide] "Plain explanation" para 3).  After
+// pass 2 every expert holds its first min(count, C) assignments.  The
+// overflow assignments (rank >= C) are then handled one after another in flat
+// order a = t*k + j: each goes to the highest-scoring expert of token t (ties:
+// lower index; NaN as -infinity) that t did not choose and that still has a
+// free slot, behind the rows already there, or is dropped when none has.
+//   A. all threads list the overflow assignments in flat order (ovf);
+//   B. wavefront 0 takes them 64 at a time, lane i the i-th: it stages the 64
+//      tokens' scores in LDS (a token's own choices marked NaN), each lane
+//      finds its best expert among those with room, and the lanes are
+//      accepted in order up to the first one whose expert was filled by the
+//      lanes before it; the rest search again with the new fill levels.  Each
+//      repeat means one more expert became full, so there are at most
+//      (overflow / 64) + E rounds.
+//   C. kcount becomes the final rows per expert; offsets and tiles as pass 2.
+// xdest[a] / xrel[a] (overflow assignments only) receive the new expert (or
+// -1) and the row inside its range.
+// ---------------------------------------------------------------------------
+constexpr int kRerouteThreads = 1024;
+constexpr int kRerouteStride = kMaxExperts + 1;   // odd: lanes hit distinct LDS banks
+__global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
+    const int32_t* __restrict__ blkbase, const float* __restrict__ logits, int64_t TK,
+    int k, int E, int C, int32_t* __restrict__ kcount, int32_t* __restrict__ offsets,
+    int bm, Tile* __restrict__ tiles, int32_t* __restrict__ ntiles,
+    int32_t* __restrict__ tstart, int32_t* __restrict__ ovf, int32_t* __restrict__ xdest,
+    int32_t* __restrict__ xrel) {
+  __shared__ float srow[kWave * kRerouteStride];
+  __shared__ int fill[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  __shared__ int toff[kMaxExperts + 1];
+  __shared__ int wsum[kRerouteThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = tid; e < E; e += blockDim.x) fill[e] = kcount[e];
+
+  // A. overflow assignments in flat order
+  int64_t n = 0;
+  for (int64_t base = 0; base < TK; base += blockDim.x) {
+    const int64_t a = base + tid;
+    bool over = false;
+    if (a < TK) {
+      const int e = topk_idx[a];
+      if (e >= 0 && e < E)
+        over = blkbase[(a / kDispatchChunk) * E + e] + lrank[a] >= C;
     }
-    off[E] = s;
-    toff[E] = ts;
-    if (ntiles) *ntiles = ts;
+    const uint64_t b = __ballot(over);
+    if (lane == 0) wsum[wave] = __popcll(b);
+    __syncthreads();
+    int64_t before = 0, total = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int c = wsum[w];
+      if (w < wave) before += c;
+      total += c;
+    }
+    if (over) ovf[n + before + __popcll(b & lt)] = static_cast<int32_t>(a);
+    n += total;
+    __syncthreads();
+  }
+
+  // B. the greedy pass, wavefront 0
+  if (wave == 0) {
+    int64_t room = 0;   // free slots left over all experts
+    for (int e = lane; e < E; e += kWave) room += C - fill[e];
+    for (int sh = kWave / 2; sh >= 1; sh >>= 1) room += __shfl_xor(room, sh);
+    for (int64_t base = 0; base < n; base += kWave) {
+      const int cnt = static_cast<int>(min<int64_t>(kWave, n - base));
+      const bool have = lane < cnt;
+      const int a = have ? ovf[base + lane] : 0;
+      const int64_t t = a / k;
+      float* row = srow + lane * kRerouteStride;
+      if (room > 0) {
+        for (int r = 0; r < cnt; ++r) {
+          const int64_t tr = __shfl(a, r) / k;
+          for (int c = lane; c < E; c += kWave) {
+            const float v = logits[tr * E + c];
+            srow[r * kRerouteStride + c] = (v != v) ? -INFINITY : v;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (have)
+          for (int j = 0; j < k; ++j) {
+            const int c = topk_idx[t * k + j];
+            if (c >= 0 && c < E) row[c] = __builtin_nanf("");
+          }
+        __builtin_amdgcn_wave_barrier();
+      }
+      bool pending = have;
+      while (__ballot(pending)) {
+        int best = -1;
+        if (pending && room > 0) {
+          float bv = -INFINITY;
+          for (int c = 0; c < E; ++c) {
+            const float v = row[c];
+            if (v != v || fill[c] >= C) continue;   // own choice, or full
+            if (best < 0 || v > bv) { best = c; bv = v; }
+          }
+        }
+        // lanes before this one (in this round) that picked the same expert
+        const bool valid = pending && best >= 0;
+        const int e = valid ? best : 0;
+        uint64_t match = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const bool on = (e >> bit) & 1;
+          const uint64_t m = __ballot(on);
+          match &= on ? m : ~m;
+        }
+        const int fb = valid ? fill[e] : 0;
+        const int ahead = __popcll(match & lt);
+        const uint64_t clash = __ballot(valid && fb + ahead >= C);
+        const int first = clash ? __ffsll(static_cast<unsigned long long>(clash)) - 1 : kWave;
+        const bool accept = pending && lane < first;
+        if (accept) {
+          xdest[a] = best;
+          xrel[a] = valid ? fb + ahead : -1;
+        }
+        const uint64_t took = __ballot(accept && valid);
+        const uint64_t mine = match & took;
+        __builtin_amdgcn_wave_barrier();
+        if (accept && valid && __ffsll(static_cast<unsigned long long>(mine)) - 1 == lane)
+          fill[e] = fb + __popcll(mine);
+        __builtin_amdgcn_wave_barrier();
+        room -= __popcll(took);
+        pending = pending && !accept;
+      }
+    }
   }
   __syncthreads();
-  for (int i = e; i <= E; i += blockDim.x) {
-    offsets[i] = off[i];
-    if (tstart) tstart[i] = toff[i];
-  }
-  if (e < E && tiles && bm > 0) {
-    int n = 0;
-    for (int r = 0; r < kc[e]; r += bm, ++n)
-      tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
-  }
+
+  // C. final rows per expert, offsets, tiles
+  for (int e = tid; e < E; e += blockDim.x) kcount[e] = fill[e];
+  slot_offsets_and_tiles(fill, E, bm, off, toff, offsets, tiles, ntiles, tstart);
 }
 
 // ---------------------------------------------------------------------------
@@ -405,7 +562,8 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
     const int32_t* __restrict__ blkbase, const int32_t* __restrict__ offsets,
     int64_t TK, int E, int C, int32_t* __restrict__ slot,
-    int32_t* __restrict__ perm) {
+    int32_t* __restrict__ perm, const int32_t* __restrict__ xdest,
+    const int32_t* __restrict__ xrel) {
   const int64_t a = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (a >= TK) return;
   const int e = topk_idx[a];
@@ -421,6 +579,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int s = offsets[e] + rank;
     slot[a] = s;
     perm[s] = static_cast<int32_t>(a);
+  } else if (xdest && xdest[a] >= 0) {   // rerouted to a spare expert
+    const int s = offsets[xdest[a]] + xrel[a];
+    slot[a] = s;
+    perm[s] = static_cast<int32_t>(a);
   } else {
     slot[a] = -1;
   }
@@ -430,13 +592,18 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* lrank, int32_t* blkcnt, int32_t* counts,
                            int32_t* kcount, int32_t* offsets, int32_t* slot,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
-                           int32_t* tstart, hipStream_t s) {
+                           int32_t* tstart, const Reroute* rr, hipStream_t s) {
   const int nblk = static_cast<int>((TK + kDispatchChunk - 1) / kDispatchChunk);
   dispatch_rank_kernel<<<nblk, 64, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
   dispatch_scan_kernel<<<1, 256, 0, s>>>(blkcnt, nblk, E, C, counts, kcount,
                                          offsets, bm, tiles, ntiles, tstart);
+  if (rr)
+    dispatch_reroute_kernel<<<1, kRerouteThreads, 0, s>>>(
+        topk_idx, lrank, blkcnt, rr->logits, TK, rr->k, E, C, kcount, offsets, bm, tiles,
+        ntiles, tstart, rr->ovf, rr->xdest, rr->xrel);
   dispatch_scatter_kernel<<<(TK + 255) / 256, 256, 0, s>>>(
-      topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm);
+      topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm, rr ? rr->xdest : nullptr,
+      rr ? rr->xrel : nullptr);
   return hipGetLastError();
 }
 
@@ -548,30 +715,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     kcount[e] = kc[e];
   }
   __syncthreads();
-  if (tid == 0) {
-    int so = 0, ts = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = so;
-      toff[i] = ts;
-      so += kc[i];
-      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
-    }
-    off[E] = so;
-    toff[E] = ts;
-    if (ntiles) *ntiles = ts;
-  }
-  __syncthreads();
-  for (int i = tid; i <= E; i += blockDim.x) {
-    offsets[i] = off[i];
-    if (tstart) tstart[i] = toff[i];
-  }
-  if (tiles && bm > 0) {
-    for (int e = tid; e < E; e += blockDim.x) {
-      int n = 0;
-      for (int r = 0; r < kc[e]; r += bm, ++n)
-        tiles[toff[e] + n] = Tile{e, off[e] + r, min(bm, kc[e] - r), 0};
-    }
-  }
+  slot_offsets_and_tiles(kc, E, bm, off, toff, offsets, tiles, ntiles, tstart);
 
   // 4. slots and the permutation (unused entries -1)
   const int total = off[E];

@@ -25,13 +25,13 @@ def config_for(w: Workload, T=None, path=moe.PATH_AUTO, bias=None, stream=None):
         T=w.T if T is None else T, d_model=w.d, d_ff=w.F, n_experts=w.E,
         top_k=w.k, n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
         capacity_factor=w.capacity_factor, dtype=w.dtype, ffn_path=path,
-        logit_bias=bias, stream=stream)
+        logit_bias=bias, stream=stream, overflow=w.overflow)
 
 
 def shape_of(w: Workload, T=None) -> O.LayerShape:
     return O.LayerShape(T=w.T if T is None else T, d=w.d, F=w.F, E=w.E, k=w.k,
                         S=w.S, gating=w.gating, renormalize=w.renormalize,
-                        capacity_factor=w.capacity_factor)
+                        capacity_factor=w.capacity_factor, overflow=w.overflow)
 
 
 def to64(t: torch.Tensor) -> np.ndarray:
@@ -114,21 +114,31 @@ def route_buffers(T, E, k):
     )
 
 
-def near_tie_tokens(gpu_logits: np.ndarray, ref: dict, floor=1e-6):
-    """Tokens whose top-k decision margin is within the fp32-vs-fp64 logit
-    error (or 1e-6): their selection is allowed to differ."""
+def full_order_margin(logits: np.ndarray) -> np.ndarray:
+    """Per token, the smallest gap between neighbours of all its sorted
+    scores: rerouting reads the whole order, not only the top k + 1."""
+    if logits.shape[0] == 0 or logits.shape[1] < 2:
+        return np.full(logits.shape[0], np.inf)
+    return np.min(np.diff(np.sort(logits, axis=1), axis=1), axis=1)
+
+
+def near_tie_tokens(gpu_logits: np.ndarray, ref: dict, floor=1e-6, full_order=False):
+    """Tokens whose routing decision margin is within the fp32-vs-fp64 logit
+    error (or 1e-6): their selection is allowed to differ.  With full_order
+    the margin covers every score of the token (rerouting)."""
     err = float(np.max(np.abs(gpu_logits - ref["logits"]))) if gpu_logits.size else 0.0
     thr = max(floor, 4.0 * err)
-    return np.nonzero(ref["margin"] < thr)[0], err, thr
+    margin = full_order_margin(ref["logits"]) if full_order else ref["margin"]
+    return np.nonzero(margin < thr)[0], err, thr
 
 
 def comparable_tokens(w: Workload, ref: dict, ties: np.ndarray, T: int):
     """Tokens whose output is comparable: all but the near ties, and, when
-    some assignments were dropped, only tokens before the first near tie
+    some assignments overflowed, only tokens before the first near tie
     (a flipped choice shifts every later rank of that expert)."""
     ok = np.ones(T, dtype=bool)
     ok[ties] = False
-    if len(ties) and ref["dispatch"]["dropped"] > 0:
+    if len(ties) and ref["dispatch"]["overflowed"] > 0:
         ok[int(ties.min()):] = False
     return ok
 

@@ -65,6 +65,10 @@ def cfg(**kw):
     (dict(d_ff=100), moe.MOE_EUNSUPPORTED),
     (dict(dtype="f32", d_model=5, d_ff=7), moe.MOE_OK),
     (dict(dtype="f32", ffn_path=moe.PATH_STREAM), moe.MOE_EUNSUPPORTED),
+    (dict(overflow=moe.OVERFLOW_REROUTE), moe.MOE_OK),
+    (dict(overflow=moe.OVERFLOW_SEQUENTIAL), moe.MOE_OK),
+    (dict(overflow=3), moe.MOE_EINVAL),
+    (dict(overflow=-1), moe.MOE_EINVAL),
 ])
 def test_check_config(kw, code):
     c = cfg(**kw)
@@ -99,3 +103,25 @@ def test_workspace_grows_with_tokens():
     assert all(s > 0 for s in sizes)
     assert sizes == sorted(sizes)
     assert moe.moe_workspace_size(cfg(T=0)) >= 0
+
+
+def test_struct_layouts_match_the_header():
+    # moe_config_t ends with the overflow policy; moe_stats_t with the
+    # overflow counters (offsets as the C compiler lays them out on x86-64)
+    assert _lib.MoeConfig.overflow.offset == 88 and ctypes.sizeof(_lib.MoeConfig) == 96
+    assert _lib.MoeStats.rounds.offset == 96 and ctypes.sizeof(_lib.MoeStats) == 104
+
+
+def test_overflow_policies_size_the_workspace():
+    # rerouting needs three T*k index arrays; sequential rounds keep every
+    # assignment, so the row buffers hold T*k rows instead of E*C
+    drop = moe.moe_workspace_size(cfg(T=4096, capacity_factor=1.0))
+    rr = moe.moe_workspace_size(cfg(T=4096, capacity_factor=1.0, overflow=moe.OVERFLOW_REROUTE))
+    seq = moe.moe_workspace_size(cfg(T=4096, capacity_factor=0.5,
+                                     overflow=moe.OVERFLOW_SEQUENTIAL))
+    half = moe.moe_workspace_size(cfg(T=4096, capacity_factor=0.5))
+    assert rr >= drop + 3 * 4 * 4096 * 2
+    assert seq > half
+    # the reported capacity is the policy-independent C
+    for pol in (moe.OVERFLOW_DROP, moe.OVERFLOW_REROUTE, moe.OVERFLOW_SEQUENTIAL):
+        assert moe.moe_capacity(cfg(T=4096, capacity_factor=0.5, overflow=pol)) == 512

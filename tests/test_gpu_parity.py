@@ -82,6 +82,14 @@ def _logits_case(name):
         mask[::7, 1:] = True      # rows with a single number
         L[mask] = float("nan")
         return w, L
+    if name == "deepseek_cf1.0":
+        # 160 fine-grained experts at capacity factor 1: spare experts abound
+        w = PRESETS["deepseek"].with_(capacity_factor=1.0)
+        return w, random_logits(w.T, w.E, seed=16) * 2
+    if name == "short_batch_skew":
+        # T <= 128: the fused one-workgroup routing, unless overflow is rerouted
+        w = Workload("short_skew", T=100, d=64, F=64, E=8, k=2, capacity_factor=0.75)
+        return w, random_logits(w.T, w.E, seed=15) + torch.tensor(SKEW_BIAS)
     if name == "deepseek_renorm_k1":
         w = Workload("dsr", T=777, d=64, F=64, E=64, k=1, gating=SOFTMAX_THEN_TOPK,
                      renormalize=True, capacity_factor=1.25)
@@ -94,10 +102,31 @@ LOGIT_CASES = ["tiny", "prefill", "skew_cf1.0", "skew_cf1.5", "deepseek",
                "tiny_capacity", "deepseek_renorm_k1", "nan_scores"]
 
 
-@pytest.mark.parametrize("case", LOGIT_CASES)
+REROUTE_CASES = ["tiny", "prefill", "skew_cf1.0", "deepseek", "ties_signed_zero", "all_equal",
+                 "E256_k8", "k_equals_E", "E1", "T1", "tiny_capacity", "nan_scores",
+                 "short_batch_skew", "deepseek_cf1.0"]
+SEQUENTIAL_CASES = ["skew_cf1.0", "deepseek", "tiny_capacity", "short_batch_skew", "T1"]
+
+
+@pytest.mark.parametrize("case", LOGIT_CASES + ["short_batch_skew"])
 def test_route_logits_bit_exact(case):
-    say(f"[route_logits] {case}")
+    _route_logits_case(case, O.OVERFLOW_DROP)
+
+
+@pytest.mark.parametrize("case", REROUTE_CASES)
+def test_route_logits_reroute_bit_exact(case):
+    _route_logits_case(case, O.OVERFLOW_REROUTE)
+
+
+@pytest.mark.parametrize("case", SEQUENTIAL_CASES)
+def test_route_logits_sequential_bit_exact(case):
+    _route_logits_case(case, O.OVERFLOW_SEQUENTIAL)
+
+
+def _route_logits_case(case, policy):
+    say(f"[route_logits] {case} overflow policy {policy}")
     w, L = _logits_case(case)
+    w = w.with_(overflow=policy)
     T, E, k = w.T, w.E, w.k
     # oracle on the same fp32 values, widened exactly (a NaN score ranks as
     # -infinity in the library; the oracle, which takes numbers only, gets -1e30)
@@ -106,7 +135,7 @@ def test_route_logits_bit_exact(case):
     sel, margin = O.topk_select(L64, k)
     gates = O.gate_weights(L64, sel, w.gating, w.renormalize)
     C = O.capacity(T, k, E, w.capacity_factor)
-    D = O.dispatch(sel, E, C)
+    D = O.dispatch_policy(sel, L64, E, C, policy)
     st_ref = O.routing_stats(D["counts"], D["kept"], O.softmax_all(L64), T, k, E)
 
     cfg = config_for(w, stream=None)
@@ -132,11 +161,14 @@ def test_route_logits_bit_exact(case):
     assert st["capacity"] == C and st["dropped"] == D["dropped"]
     assert np.array_equal(st["counts"], D["counts"])
     assert np.array_equal(st["kept"], D["kept"])
+    assert (st["overflowed"], st["rerouted"], st["rounds"]) == \
+        (D["overflowed"], D["rerouted"], D["rounds"])
     for key in ("aux_loss", "aux_loss_kept", "overflow_rate", "entropy_load",
                 "entropy_token"):
         ref = st_ref[key]
         assert abs(st[key] - ref) <= 1e-5 * max(abs(ref), 1e-3), (key, st[key], ref)
-    say(f"  ok: C={C} dropped={D['dropped']} aux={st['aux_loss']:.6f} "
+    say(f"  ok: C={C} overflowed={D['overflowed']} rerouted={D['rerouted']} "
+        f"dropped={D['dropped']} rounds={D['rounds']} aux={st['aux_loss']:.6f} "
         f"min margin={float(margin.min()) if T else 0:.3g}")
 
 
@@ -228,6 +260,18 @@ FORWARD_CASES = {
     # over 1.5k rows per expert: token rows read in place, hidden rows K-blocked
     "bf16_many_rows": Workload("bf16_many", T=4096, d=128, F=128, E=2, k=1,
                                capacity_factor=1.0),
+    # overflow sent to spare experts, or processed in later rounds
+    "bf16_skew_reroute": Workload("bf16_skew_rr", T=1000, d=256, F=384, E=8, k=2,
+                                  capacity_factor=1.0, bias=SKEW_BIAS, overflow=1),
+    "bf16_skew_sequential": Workload("bf16_skew_seq", T=1000, d=256, F=384, E=8, k=2,
+                                     capacity_factor=1.0, bias=SKEW_BIAS, overflow=2),
+    "bf16_deepseek_reroute": Workload("bf16_ds_rr", T=256, d=256, F=128, E=32, k=6, S=2,
+                                      gating=SOFTMAX_THEN_TOPK, renormalize=False,
+                                      capacity_factor=1.0, overflow=1),
+    "bf16_short_reroute": Workload("bf16_short_rr", T=64, d=128, F=192, E=4, k=2,
+                                   capacity_factor=0.75, overflow=1),
+    "f32_reroute_shared": Workload("f32_rr", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
+                                   capacity_factor=0.8, overflow=1),
 }
 
 
@@ -239,7 +283,8 @@ def test_forward_small(case):
     out, st = run.forward()
     g_route, _ = run.route()
     ref = run.oracle()
-    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref)
+    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref,
+                                      full_order=w.overflow == O.OVERFLOW_REROUTE)
     ok = comparable_tokens(w, ref, ties, w.T)
     got = to64(out)
     err, rms = rel_max_err(got[ok], ref["out"][ok])
@@ -248,9 +293,14 @@ def test_forward_small(case):
         f"excess over bound {excess:.2e}, near ties {len(ties)}")
     assert np.all(np.isfinite(got))
     assert good
+    if w.overflow != O.OVERFLOW_DROP:
+        assert ref["dispatch"]["overflowed"] > 0   # the case exercises its policy
     if len(ties) == 0:
         assert np.array_equal(st["counts"], ref["dispatch"]["counts"])
+        assert np.array_equal(st["kept"], ref["dispatch"]["kept"])
         assert st["dropped"] == ref["dispatch"]["dropped"]
+        for key in ("overflowed", "rerouted", "rounds"):
+            assert st[key] == ref["dispatch"][key], key
         for key in ("aux_loss", "overflow_rate", "entropy_load", "entropy_token"):
             r = ref["stats"][key]
             assert abs(st[key] - r) <= 1e-4 * max(abs(r), 1e-3), key
@@ -281,7 +331,9 @@ def test_forward_deterministic():
 # full workload sizes, sampled tokens
 # --------------------------------------------------------------------------
 FULL = ["mixtral_prefill", "mixtral_decode_t1", "mixtral_decode_t8", "mixtral_decode_t64",
-        "skew_cf1.0", "skew_cf1.5", "deepseek"]
+        "skew_cf1.0", "skew_cf1.5", "deepseek", "skew_cf1.0:reroute", "deepseek:reroute",
+        "skew_cf1.0:sequential"]
+_POLICY = {"reroute": O.OVERFLOW_REROUTE, "sequential": O.OVERFLOW_SEQUENTIAL}
 
 
 def _sample(ref, T, n=40, seed=0):
@@ -293,12 +345,20 @@ def _sample(ref, T, n=40, seed=0):
     if len(dropped_tok):
         pick.update(rng.choice(dropped_tok, size=min(8, len(dropped_tok)), replace=False).tolist())
         pick.add(int(dropped_tok[0]))
+    moved = ref["dispatch"]["expert"] != ref["sel"].reshape(-1)
+    moved_tok = np.nonzero((moved & (ref["dispatch"]["expert"] >= 0)).reshape(T, -1).any(1))[0]
+    if len(moved_tok):   # rows run by a spare expert
+        pick.update(rng.choice(moved_tok, size=min(8, len(moved_tok)), replace=False).tolist())
+        pick.add(int(moved_tok[0]))
     return sorted(pick)
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_forward_full_size_sampled(name):
-    w = PRESETS[name]
+    base, _, policy = name.partition(":")
+    w = PRESETS[base]
+    if policy:
+        w = w.with_(overflow=_POLICY[policy])
     say(f"[full] {name}")
     run = Run(w, gen_device=DEV)
     out, st = run.forward()
@@ -306,7 +366,8 @@ def test_forward_full_size_sampled(name):
     routing = run.oracle(tokens=[])
     toks = _sample(routing, w.T)
     ref = run.oracle(tokens=toks)
-    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref)
+    ties, lerr, thr = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref,
+                                      full_order=w.overflow == O.OVERFLOW_REROUTE)
     ok = comparable_tokens(w, ref, ties, w.T)
     sel_ok = [t for t in toks if ok[t]]
     got = to64(out)[sel_ok]
@@ -314,7 +375,8 @@ def test_forward_full_size_sampled(name):
     good, ratio, excess = output_within_tolerance(got, ref["out"][sel_ok], w)
     say(f"  {len(sel_ok)} tokens: max|d| = {err:.3e}, RMS = {rms:.3e}, ratio "
         f"{ratio:.2e}, excess over bound {excess:.2e}; near ties {len(ties)}; dropped "
-        f"{ref['dispatch']['dropped']}; aux {st['aux_loss']:.4f}")
+        f"{ref['dispatch']['dropped']}; rerouted {ref['dispatch']['rerouted']}; rounds "
+        f"{ref['dispatch']['rounds']}; aux {st['aux_loss']:.4f}")
     assert len(sel_ok) >= min(20, w.T)
     assert np.all(np.isfinite(to64(out)))
     assert good
@@ -322,6 +384,8 @@ def test_forward_full_size_sampled(name):
         assert np.array_equal(st["counts"], ref["dispatch"]["counts"])
         assert np.array_equal(st["kept"], ref["dispatch"]["kept"])
         assert st["dropped"] == ref["dispatch"]["dropped"]
+        for key in ("overflowed", "rerouted", "rounds"):
+            assert st[key] == ref["dispatch"][key], key
         for key in ("aux_loss", "aux_loss_kept", "overflow_rate", "entropy_load",
                     "entropy_token"):
             r = ref["stats"][key]

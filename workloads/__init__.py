@@ -49,6 +49,7 @@ class Workload:
     capacity_factor: float = 0.0
     dtype: str = "bf16"           # "bf16" or "f32"
     bias: Optional[Tuple[float, ...]] = None
+    overflow: int = 0             # 0 drop, 1 reroute to spare experts, 2 sequential rounds
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
