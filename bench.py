@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="override the workload's capacity factor")
+    ap.add_argument("--overflow", default="drop", choices=["drop", "reroute", "sequential"],
+                    help="what happens to assignments beyond an expert's capacity")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
@@ -122,7 +126,8 @@ def cpu_baseline(w, inp, n_tokens: int):
     rng = np.random.default_rng(0)
     toks = sorted(rng.choice(w.T, size=min(n_tokens, w.T), replace=False).tolist())
     shape = O.LayerShape(T=w.T, d=w.d, F=w.F, E=w.E, k=w.k, S=w.S, gating=w.gating,
-                         renormalize=w.renormalize, capacity_factor=w.capacity_factor)
+                         renormalize=w.renormalize, capacity_factor=w.capacity_factor,
+                         overflow=w.overflow)
     x64, wg64 = w64(hx), w64(hWg)
     experts = lambda e: (w64(W1[e]), w64(W3[e]), w64(W2[e]))  # noqa: E731
     # routing, dispatch and statistics alone (all T tokens, no expert outputs)
@@ -152,6 +157,11 @@ def main():
     from workloads import PRESETS, make_inputs
 
     w = PRESETS[args.workload]
+    overflow = {"drop": 0, "reroute": 1, "sequential": 2}[args.overflow]
+    if overflow:
+        w = w.with_(overflow=overflow)
+    if args.capacity_factor is not None:
+        w = w.with_(capacity_factor=args.capacity_factor)
     dev = "cuda"
     torch.cuda.init()
     inp = make_inputs(w, seed=args.seed, device=dev)
@@ -161,7 +171,8 @@ def main():
         cfg = moe.make_config(T=w.T, d_model=w.d, d_ff=w.F, n_experts=w.E, top_k=w.k,
                               n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
                               capacity_factor=w.capacity_factor, dtype=w.dtype,
-                              ffn_path=path, logit_bias=inp.bias, stream=stream)
+                              ffn_path=path, logit_bias=inp.bias, stream=stream,
+                              overflow=w.overflow)
         ws = moe.Workspace(moe.moe_workspace_size(cfg))
         ws.bind(cfg)
         out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
@@ -238,7 +249,8 @@ def main():
     dom = "ffn1_swiglu" if w.dtype == "bf16" else "ffn1_swiglu_f32"
     dom_ms = per_kernel.get(dom, {}).get("avg_ms", float("nan"))
     digest = source_digest()
-    meas = MEASURED_TRAFFIC.get(w.name)
+    meas = (MEASURED_TRAFFIC.get(w.name)
+            if w.overflow == 0 and args.capacity_factor is None else None)
     traffic = None
     if meas is not None and meas[0] == digest:
         traffic = meas[1] + meas[2]
@@ -283,7 +295,7 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and weights of the workload's shapes)",
         "config": {"workload": w.name, "T": w.T, "d_model": w.d, "d_ff": w.F,
                    "n_experts": w.E, "top_k": w.k, "n_shared": w.S,
-                   "capacity_factor": w.capacity_factor,
+                   "capacity_factor": w.capacity_factor, "overflow": args.overflow,
                    "gating": "softmax_then_topk" if w.gating else "topk_then_softmax",
                    "parallelism": "single GPU"},
         "roofline": roof,
@@ -293,6 +305,8 @@ def main():
                   "frac_of_hbm_peak": layer_gbs / PEAK_HBM_GBS,
                   "kept_assignments": kept, "experts_hit": hit,
                   "capacity": st["capacity"], "dropped": st["dropped"],
+                  "overflowed": st["overflowed"], "rerouted": st["rerouted"],
+                  "rounds": st["rounds"],
                   "aux_loss": st["aux_loss"], "overflow_rate": st["overflow_rate"],
                   "entropy_load": st["entropy_load"], "entropy_token": st["entropy_token"],
                   "counts": [int(c) for c in st["counts"]]},

@@ -422,19 +422,22 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
 // lower index; NaN as -infinity) that t did not choose and that still has a
 // free slot, behind the rows already there, or is dropped when none has.
 //   A. all threads list the overflow assignments in flat order (ovf);
-//   B. wavefront 0 takes them 64 at a time, lane i the i-th: it stages the 64
-//      tokens' scores in LDS (a token's own choices marked NaN), each lane
-//      finds its best expert among those with room, and the lanes are
+//   B. in chunks of up to kRerouteRows assignments: all threads copy the
+//      chunk's score rows into LDS, writing NaN where an expert is not
+//      available (full, or one of the token's own choices); then wavefront 0
+//      takes the chunk 64 assignments at a time, lane i the i-th: each lane
+//      finds the best available expert of its row, and the lanes are
 //      accepted in order up to the first one whose expert was filled by the
-//      lanes before it; the rest search again with the new fill levels.  Each
-//      repeat means one more expert became full, so there are at most
-//      (overflow / 64) + E rounds.
+//      lanes before it; the rest search again.  Each repeat means one more
+//      expert became full (its column is then set to NaN in every row of the
+//      chunk), so there are at most (overflow / 64) + E rounds;
 //   C. kcount becomes the final rows per expert; offsets and tiles as pass 2.
 // xdest[a] / xrel[a] (overflow assignments only) receive the new expert (or
 // -1) and the row inside its range.
 // ---------------------------------------------------------------------------
 constexpr int kRerouteThreads = 1024;
-constexpr int kRerouteStride = kMaxExperts + 1;   // odd: lanes hit distinct LDS banks
+constexpr int kRerouteLds = kWave * (kMaxExperts + 1);   // floats of staged scores
+constexpr int kRerouteRows = 1792;   // rows staged at most: kRerouteLds / 9, floor to 64
 __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
     const int32_t* __restrict__ blkbase, const float* __restrict__ logits, int64_t TK,
@@ -442,11 +445,13 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
     int bm, Tile* __restrict__ tiles, int32_t* __restrict__ ntiles,
     int32_t* __restrict__ tstart, int32_t* __restrict__ ovf, int32_t* __restrict__ xdest,
     int32_t* __restrict__ xrel) {
-  __shared__ float srow[kWave * kRerouteStride];
+  __shared__ float srow[kRerouteLds];
+  __shared__ int sa[kRerouteRows];
   __shared__ int fill[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
   __shared__ int toff[kMaxExperts + 1];
-  __shared__ int wsum[kRerouteThreads / kWave];
+  constexpr int U = 16;   // assignments per thread per pass of A
+  __shared__ int wsum[U][kRerouteThreads / kWave];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -454,99 +459,175 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int e = tid; e < E; e += blockDim.x) fill[e] = kcount[e];
 
-  // A. overflow assignments in flat order
+  // A. overflow assignments in flat order, U per thread per pass (their
+  // loads in flight together)
   int64_t n = 0;
-  for (int64_t base = 0; base < TK; base += blockDim.x) {
-    const int64_t a = base + tid;
-    bool over = false;
-    if (a < TK) {
-      const int e = topk_idx[a];
-      if (e >= 0 && e < E)
-        over = blkbase[(a / kDispatchChunk) * E + e] + lrank[a] >= C;
+  for (int64_t base = 0; base < TK; base += U * blockDim.x) {
+    bool over[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t a = base + u * blockDim.x + tid;
+      over[u] = false;
+      if (a < TK) {
+        const int e = topk_idx[a];
+        if (e >= 0 && e < E)
+          over[u] = blkbase[(a / kDispatchChunk) * E + e] + lrank[a] >= C;
+      }
+      const uint64_t b = __ballot(over[u]);
+      if (lane == 0) wsum[u][wave] = __popcll(b);
     }
-    const uint64_t b = __ballot(over);
-    if (lane == 0) wsum[wave] = __popcll(b);
     __syncthreads();
-    int64_t before = 0, total = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int c = wsum[w];
-      if (w < wave) before += c;
-      total += c;
+    int64_t before = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t a = base + u * blockDim.x + tid;
+      int64_t mine = before, total = 0;
+      for (int w = 0; w < nwaves; ++w) {
+        const int c = wsum[u][w];
+        if (w < wave) mine += c;
+        total += c;
+      }
+      const uint64_t b = __ballot(over[u]);
+      if (over[u]) ovf[n + mine + __popcll(b & lt)] = static_cast<int32_t>(a);
+      before += total;
     }
-    if (over) ovf[n + before + __popcll(b & lt)] = static_cast<int32_t>(a);
-    n += total;
+    n += before;
     __syncthreads();
   }
 
-  // B. the greedy pass, wavefront 0
+  // B. the greedy pass
+  const int E8 = (E + 7) & ~7;     // scanned columns; those >= E are never available
+  const int stride = E8 + 1;       // odd: the 64 lanes' rows fall in distinct LDS banks
+  const int R = min(kRerouteRows, kRerouteLds / stride / kWave * kWave);
+  const float kNaN = __builtin_nanf("");
+  int64_t room = 0;   // free slots left over all experts (wavefront 0)
   if (wave == 0) {
-    int64_t room = 0;   // free slots left over all experts
     for (int e = lane; e < E; e += kWave) room += C - fill[e];
     for (int sh = kWave / 2; sh >= 1; sh >>= 1) room += __shfl_xor(room, sh);
-    for (int64_t base = 0; base < n; base += kWave) {
-      const int cnt = static_cast<int>(min<int64_t>(kWave, n - base));
-      const bool have = lane < cnt;
-      const int a = have ? ovf[base + lane] : 0;
-      const int64_t t = a / k;
-      float* row = srow + lane * kRerouteStride;
-      if (room > 0) {
-        for (int r = 0; r < cnt; ++r) {
-          const int64_t tr = __shfl(a, r) / k;
-          for (int c = lane; c < E; c += kWave) {
-            const float v = logits[tr * E + c];
-            srow[r * kRerouteStride + c] = (v != v) ? -INFINITY : v;
-          }
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (have)
-          for (int j = 0; j < k; ++j) {
-            const int c = topk_idx[t * k + j];
-            if (c >= 0 && c < E) row[c] = __builtin_nanf("");
-          }
-        __builtin_amdgcn_wave_barrier();
+  }
+  for (int64_t cbase = 0; cbase < n; cbase += R) {
+    const int rows = static_cast<int>(min<int64_t>(R, n - cbase));
+    // the tokens' scores (NaN read as -infinity), NaN where the expert is
+    // full; element-wise over all threads
+    for (int i = tid; i < rows * E8; i += blockDim.x) {
+      const int r = i / E8;
+      const int c = i - r * E8;
+      const int a = ovf[cbase + r];
+      if (c == 0) sa[r] = a;
+      float v = kNaN;
+      if (c < E && fill[c] < C) {
+        v = logits[static_cast<int64_t>(a / k) * E + c];
+        v = (v != v) ? -INFINITY : v;
       }
-      bool pending = have;
-      while (__ballot(pending)) {
-        int best = -1;
-        if (pending && room > 0) {
-          float bv = -INFINITY;
-          for (int c = 0; c < E; ++c) {
-            const float v = row[c];
-            if (v != v || fill[c] >= C) continue;   // own choice, or full
-            if (best < 0 || v > bv) { best = c; bv = v; }
-          }
-        }
-        // lanes before this one (in this round) that picked the same expert
-        const bool valid = pending && best >= 0;
-        const int e = valid ? best : 0;
-        uint64_t match = __ballot(valid);
+      srow[r * stride + c] = v;
+    }
+    __syncthreads();
+    // NaN at the token's own choices
+    for (int i = tid; i < rows * k; i += blockDim.x) {
+      const int r = i / k;
+      const int a = sa[r];
+      const int c = topk_idx[a - a % k + (i - r * k)];
+      if (c >= 0 && c < E) srow[r * stride + c] = kNaN;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;   // bits of an expert index
+      for (int b0 = 0; b0 < rows; b0 += kWave) {
+        const bool have = b0 + lane < rows;
+        const int a = have ? sa[b0 + lane] : 0;
+        const float* row = srow + (b0 + lane) * stride;
+        bool pending = have;
+        // best and second-best available expert of the row (-1: none, -2:
+        // not known).  Availability only shrinks, so when the best fills up
+        // the second becomes the best and the row needs no rescan.
+        int best = -2, second = -2;
+        while (__ballot(pending)) {
+          // a best that is not known, or no longer has room, needs a scan
+          const bool scan = pending && (best == -2 || (best >= 0 && fill[best] >= C));
+          if (__ballot(scan)) {
+            if (scan && room > 0) {
+              // strict > over ascending indices keeps the lower index on
+              // ties; unavailable entries are NaN and never compare greater
+              float bv = -INFINITY, sv = -INFINITY;
+              int b = -1, s2 = -1;
+#pragma unroll 2
+              for (int c0 = 0; c0 < E8; c0 += 8) {
+                float v[8];
 #pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-          const bool on = (e >> bit) & 1;
-          const uint64_t m = __ballot(on);
-          match &= on ? m : ~m;
+                for (int u = 0; u < 8; ++u) v[u] = row[c0 + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                  const bool top = v[u] > bv;
+                  const bool mid = !top && v[u] > sv;
+                  s2 = top ? b : (mid ? c0 + u : s2);
+                  sv = top ? bv : (mid ? v[u] : sv);
+                  b = top ? c0 + u : b;
+                  bv = top ? v[u] : bv;
+                }
+              }
+              // available experts that score -infinity come after the rest,
+              // by index: they fill the best / second places left empty
+              if (s2 < 0) {
+                for (int c = 0; c < E8; ++c) {
+                  if (row[c] != -INFINITY || c == b) continue;
+                  if (b < 0) { b = c; continue; }
+                  s2 = c;
+                  break;
+                }
+              }
+              best = b;
+              second = s2;
+            } else if (scan) {
+              best = second = -1;   // no free slot anywhere
+            }
+          }
+          const int cur = pending ? best : -1;
+          // lanes before this one (in this round) that picked the same expert
+          const bool valid = cur >= 0;
+          const int e = valid ? cur : 0;
+          uint64_t match = __ballot(valid);
+          for (int bit = 0; bit < ebits; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const uint64_t m = __ballot(on);
+            match &= on ? m : ~m;
+          }
+          const int fb = valid ? fill[e] : 0;
+          const int ahead = __popcll(match & lt);
+          const uint64_t clash = __ballot(valid && fb + ahead >= C);
+          const int first = clash ? __ffsll(static_cast<unsigned long long>(clash)) - 1 : kWave;
+          const bool accept = pending && lane < first;
+          if (accept) {
+            xdest[a] = cur;
+            xrel[a] = valid ? fb + ahead : -1;
+          }
+          const uint64_t took = __ballot(accept && valid);
+          const uint64_t mine = match & took;
+          const bool leader = accept && valid &&
+                              __ffsll(static_cast<unsigned long long>(mine)) - 1 == lane;
+          const int nfill = fb + __popcll(mine);
+          __builtin_amdgcn_wave_barrier();
+          if (leader) fill[e] = nfill;
+          room -= __popcll(took);
+          pending = pending && !accept;
+          // experts this round filled up: unavailable in every row of the chunk
+          uint64_t filled = __ballot(leader && nfill >= C);
+          while (filled) {
+            const int l = __ffsll(static_cast<unsigned long long>(filled)) - 1;
+            filled &= filled - 1;
+            const int cf = __shfl(e, l);
+            for (int r = lane; r < rows; r += kWave) srow[r * stride + cf] = kNaN;
+            if (second == cf) second = -2;
+            if (best == cf) {
+              best = second;
+              second = -2;
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
         }
-        const int fb = valid ? fill[e] : 0;
-        const int ahead = __popcll(match & lt);
-        const uint64_t clash = __ballot(valid && fb + ahead >= C);
-        const int first = clash ? __ffsll(static_cast<unsigned long long>(clash)) - 1 : kWave;
-        const bool accept = pending && lane < first;
-        if (accept) {
-          xdest[a] = best;
-          xrel[a] = valid ? fb + ahead : -1;
-        }
-        const uint64_t took = __ballot(accept && valid);
-        const uint64_t mine = match & took;
-        __builtin_amdgcn_wave_barrier();
-        if (accept && valid && __ffsll(static_cast<unsigned long long>(mine)) - 1 == lane)
-          fill[e] = fb + __popcll(mine);
-        __builtin_amdgcn_wave_barrier();
-        room -= __popcll(took);
-        pending = pending && !accept;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // C. final rows per expert, offsets, tiles
   for (int e = tid; e < E; e += blockDim.x) kcount[e] = fill[e];
