@@ -46,7 +46,10 @@ design notes):
   best-scoring expert (ties to the lower index) that the token did not choose
   and that still has a free slot, and keeps its gate weight; with sequential
   processing nothing is dropped, the output equals the unlimited layer's, and
-  the number of capacity-sized rounds of the busiest expert is reported.
+  the number of capacity-sized rounds of the busiest expert is reported;
+* the router backward differentiates the gates, the softmax and the
+  auxiliary product; the top-k selection, the capacity decisions and the
+  load fractions f_i are held fixed (they are piecewise constant).
 
 Nothing here is "parity unpinned": every function is checked by
 ``tests/test_oracle_pins.py`` against page values, closed forms, library
@@ -422,6 +425,7 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
     out[want] = 0.0
 
     # Routed experts: each expert runs once on its kept rows, in slot order.
+    yrows = {}   # assignment a -> the output row of the expert that ran it
     for e in range(E):
         lo, hi = int(disp["offsets"][e]), int(disp["offsets"][e + 1])
         rows = [int(a) for a in disp["perm"][lo:hi] if want[int(a) // k]]
@@ -433,6 +437,7 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
         for r, a in enumerate(rows):
             t, j = divmod(a, k)
             out[t] += w[t, j] * Y[r]
+            yrows[a] = Y[r]
 
     # Shared experts: every token, gate 1.
     shared = None
@@ -446,7 +451,71 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
         out[idx] += shared
 
     return dict(out=out, logits=logits, sel=sel, margin=margin, w=w, p=p,
-                capacity=C, dispatch=disp, stats=stats)
+                capacity=C, dispatch=disp, stats=stats, yrows=yrows)
+
+
+# ---------------------------------------------------------------------------
+# Router backward.  [Routing guide] "Plain explanation" paragraph 2: the
+# router is trained together with the experts through the softmax, so a
+# token's gradient reaches the scores of experts it did not pick (in the
+# softmax-over-all order); paragraph 4: the auxiliary product E sum f_i P_i
+# pushes the load back towards balance through P_i.  The selection, the
+# capacity decisions and the counts f_i are piecewise constant and carry no
+# gradient.
+# ---------------------------------------------------------------------------
+def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
+                    shape: LayerShape, dout: np.ndarray,
+                    aux_coef: float = 0.0) -> dict:
+    """Gradients of  L = sum(dout * out) + aux_coef * aux  with respect to the
+    gate weights (dw [T, k]), the router scores (dlogits [T, E]), W_gate
+    (dW_gate [d, E]), the bias (dbias [E]) and the router's share of dx
+    ([T, d]; the experts' share is not part of this).  ``fwd`` is the result
+    of ``forward`` for all T tokens.
+
+      dw[t, j]   = dout[t] . y_{t,j} for an assignment some expert ran, else 0
+      top-k then softmax (and renormalised softmax then top-k): the gates are a
+      softmax over the k chosen scores, so for chosen c_i
+          dl[t, c_i] = w_i (dw_i - sum_j w_j dw_j),   0 elsewhere;
+      softmax over all experts, read at the chosen ones: w_j = p[t, c_j], so
+          dl[t, i]  = p_i (G_i - sum_j w_j dw_j),   G_i = dw_j if i = c_j else 0,
+      which is non-zero for every expert the token did not choose;
+      aux = E sum_i f_i P_i with P_i = mean_t p[t, i] and f fixed:
+          dl[t, m] += aux_coef (E / T) p[t, m] (f_m - sum_i f_i p[t, i]);
+      scores l = x W_gate + b:  dW_gate = x^T dl, dbias = sum_t dl[t],
+      dx = dl W_gate^T.
+    """
+    T, E, k = shape.T, shape.E, shape.k
+    x64 = np.asarray(x, dtype=np.float64)
+    W64 = np.asarray(W_gate, dtype=np.float64)
+    g = np.asarray(dout, dtype=np.float64)
+    sel, w, p = fwd["sel"], fwd["w"], fwd["p"]
+    yrows = fwd["yrows"]
+    dw = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            a = t * k + j
+            if a in yrows:
+                dw[t, j] = float(np.dot(g[t], yrows[a]))
+            elif fwd["dispatch"]["slot"][a] >= 0:
+                raise ValueError("forward did not compute every kept row")
+    dl = np.zeros((T, E))
+    softmax_over_chosen = (shape.gating == TOPK_THEN_SOFTMAX or shape.renormalize)
+    for t in range(T):
+        s = float(np.dot(w[t], dw[t]))
+        if softmax_over_chosen:
+            for j in range(k):
+                dl[t, sel[t, j]] = w[t, j] * (dw[t, j] - s)
+        else:
+            G = np.zeros(E)
+            for j in range(k):
+                G[sel[t, j]] = dw[t, j]
+            dl[t] = p[t] * (G - s)
+    if aux_coef != 0.0 and T > 0:
+        f = fwd["dispatch"]["counts"].astype(np.float64) / (T * k)
+        for t in range(T):
+            dl[t] += aux_coef * (E / T) * p[t] * (f - float(np.dot(f, p[t])))
+    return dict(dw=dw, dlogits=dl, dW_gate=x64.T @ dl, dbias=dl.sum(axis=0),
+                dx=dl @ W64.T)
 
 
 # ---------------------------------------------------------------------------

@@ -542,6 +542,135 @@ def pin_overflow_forward(O):
     assert np.isclose(rr["stats"]["overflow_rate"], D["dropped"] / (T * k))
 
 
+# ---------------------------------------------------------------- backward
+# [Routing guide] "Plain explanation" paragraphs 2 and 4: the router learns
+# through the softmax, and the auxiliary product pushes the load to balance.
+def _bwd_case(O, gating, renorm, cf, overflow=None, T=14, d=6, F=8, E=5, k=2, S=1,
+              seed=16):
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    ex = _experts(E + S, d, F, seed + 100)
+    Wg = r.standard_normal((d, E)) * 0.8
+    b = r.standard_normal(E) * 0.5
+    b[0] += 1.0                                   # some overflow at small cf
+    dout = r.standard_normal((T, d))
+    shape = _shape(O, T, d, F, E, k, S=S, gating=gating, renorm=renorm, cf=cf,
+                   overflow=overflow)
+    return x, ex, Wg, b, dout, shape
+
+
+def _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=None):
+    """sum(dout * out) + alpha * aux, with the router reading x_router."""
+    xr = x if x_router is None else x_router
+    res = O.forward(x, shape, lambda e: ex[e], logits=O.router_logits(xr, Wg, b))
+    return float(np.sum(dout * res["out"])) + alpha * res["stats"]["aux_loss"], res
+
+
+def pin_router_backward_finite_differences(O):
+    # Central differences of the layer's own forward (selection and capacity
+    # decisions stay fixed: every decision margin is far above the step).
+    h, alpha = 1e-6, 0.7
+    for gating, renorm, cf, ovf, d in [(O.TOPK_THEN_SOFTMAX, True, 0.8, None, 6),
+                                       (O.SOFTMAX_THEN_TOPK, False, 0.8, None, 6),
+                                       (O.SOFTMAX_THEN_TOPK, True, 0.0, None, 6),
+                                       (O.SOFTMAX_THEN_TOPK, False, 0.7, O.OVERFLOW_REROUTE, 6),
+                                       (O.TOPK_THEN_SOFTMAX, True, 0.8, None, 5)]:  # d == E
+        x, ex, Wg, b, dout, shape = _bwd_case(O, gating, renorm, cf, ovf, d=d)
+        L0, res = _loss(O, x, ex, Wg, b, dout, shape, alpha)
+        assert float(np.min(_full_gaps(res["logits"]))) > 5e-5   # steps move scores by ~1e-5
+        if cf > 0:
+            assert res["dispatch"]["overflowed"] > 0
+        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha)
+        for name, arr, get in (("dW_gate", Wg, lambda v: (x, ex, v, b)),
+                               ("dbias", b, lambda v: (x, ex, Wg, v))):
+            num = np.zeros_like(arr)
+            for idx in np.ndindex(arr.shape):
+                up, dn = arr.copy(), arr.copy()
+                up[idx] += h
+                dn[idx] -= h
+                num[idx] = (_loss(O, *get(up), dout, shape, alpha)[0]
+                            - _loss(O, *get(dn), dout, shape, alpha)[0]) / (2 * h)
+            assert np.allclose(g[name], num, rtol=1e-6, atol=1e-7), (name, gating, renorm)
+        # dx: the router's share only (experts keep reading the unperturbed x)
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            up, dn = x.copy(), x.copy()
+            up[idx] += h
+            dn[idx] -= h
+            num[idx] = (_loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=up)[0]
+                        - _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=dn)[0]) / (2 * h)
+        assert np.allclose(g["dx"], num, rtol=1e-6, atol=1e-7), ("dx", gating, renorm)
+
+
+def _full_gaps(L):
+    return np.min(np.diff(np.sort(L, axis=1), axis=1), axis=1)
+
+
+def pin_router_backward_autograd(O):
+    # torch fp64 autograd of the gating with the selection held fixed.
+    alpha = 0.3
+    for gating, renorm in [(O.TOPK_THEN_SOFTMAX, True), (O.SOFTMAX_THEN_TOPK, False),
+                           (O.SOFTMAX_THEN_TOPK, True)]:
+        x, ex, Wg, b, dout, shape = _bwd_case(O, gating, renorm, 0.9, seed=17)
+        _, res = _loss(O, x, ex, Wg, b, dout, shape, alpha)
+        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha)
+        T, E, k = shape.T, shape.E, shape.k
+        sel = torch.as_tensor(res["sel"])
+        Y = torch.zeros(T, k, shape.d, dtype=torch.float64)
+        for a, y in res["yrows"].items():
+            Y[a // k, a % k] = torch.as_tensor(y)
+        L = torch.tensor(res["logits"], dtype=torch.float64, requires_grad=True)
+        if gating == O.TOPK_THEN_SOFTMAX or renorm:
+            w = torch.softmax(torch.gather(L, 1, sel), dim=1)
+        else:
+            w = torch.gather(torch.softmax(L, dim=1), 1, sel)
+        out = (w[:, :, None] * Y).sum(1)
+        f = torch.as_tensor(res["dispatch"]["counts"], dtype=torch.float64) / (T * k)
+        aux = E * (f * torch.softmax(L, dim=1).mean(0)).sum()
+        loss = (torch.as_tensor(dout) * out).sum() + alpha * aux
+        loss.backward()
+        assert np.allclose(g["dlogits"], L.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def pin_router_backward_closed_forms(O):
+    # Softmax gradients are orthogonal to a constant shift of a token's scores.
+    for gating, renorm in [(O.TOPK_THEN_SOFTMAX, True), (O.SOFTMAX_THEN_TOPK, False)]:
+        x, ex, Wg, b, dout, shape = _bwd_case(O, gating, renorm, 0.8, seed=18)
+        _, res = _loss(O, x, ex, Wg, b, dout, shape, 0.5)
+        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=0.5)
+        assert np.allclose(g["dlogits"].sum(axis=1), 0.0, atol=1e-12)
+        dropped = [t for t in range(shape.T)
+                   if all(res["dispatch"]["slot"][t * shape.k + j] < 0 for j in range(shape.k))]
+        g0 = O.router_backward(x, Wg, res, shape, dout, aux_coef=0.0)
+        for t in dropped:                                 # nothing ran: no gate signal
+            assert np.all(g0["dlogits"][t] == 0.0)
+        if gating == O.SOFTMAX_THEN_TOPK:
+            # experts the token did not choose get -p_i * sum_j w_j dw_j
+            for t in range(shape.T):
+                s = float(np.dot(g0["dw"][t], res["w"][t]))
+                for i in set(range(shape.E)) - set(int(c) for c in res["sel"][t]):
+                    assert np.isclose(g0["dlogits"][t, i], -res["p"][t, i] * s, rtol=0, atol=1e-14)
+    # Identical experts and Mixtral gates: the output does not depend on the
+    # gates (they sum to 1), so neither does the loss.
+    x, ex, Wg, b, dout, shape = _bwd_case(O, O.TOPK_THEN_SOFTMAX, True, 0.0, S=0, seed=19)
+    same = [ex[0]] * shape.E
+    _, res = _loss(O, x, same, Wg, b, dout, shape, 0.0)
+    g = O.router_backward(x, Wg, res, shape, dout, aux_coef=0.0)
+    assert np.allclose(g["dlogits"], 0.0, atol=1e-12)
+    # Balanced load: each of E experts gets T/E tokens (k = 1), so f = 1/E and
+    # the auxiliary gradient (E/T) p (f - <f, p>) vanishes.
+    T, E = 12, 4
+    L = np.full((T, E), -1.0)
+    for t in range(T):
+        L[t, t % E] = 2.0 + 0.1 * t
+    shape = _shape(O, T, 3, 4, E, 1)
+    ex = _experts(E, 3, 4, 190)
+    res = O.forward(np.ones((T, 3)), shape, lambda e: ex[e], logits=L)
+    g = O.router_backward(np.ones((T, 3)), np.zeros((3, E)), res, shape, np.zeros((T, 3)),
+                          aux_coef=1.0)
+    assert np.allclose(g["dlogits"], 0.0, atol=1e-15)
+
+
 # ---------------------------------------------------------------- stats
 def pin_stats_closed_forms(O):
     E, k, T = 8, 2, 64

@@ -221,7 +221,59 @@ def _rounds_floor(sel, logits, E, C, policy=O.OVERFLOW_DROP):
     return D
 
 
+def _bwd_variant(mode):
+    """The router backward with one planted mistake: 'dropped' gives dropped
+    assignments their expert's dot product anyway, 'selected_only' drops the
+    softmax signal to unchosen experts, 'aux_no_E' loses the factor E,
+    'aux_sign' flips the auxiliary term, 'dx_untransposed' multiplies by
+    W_gate instead of its transpose (shapes allowing), 'dw_unweighted' leaves
+    out the gate weight in the chosen-softmax Jacobian."""
+    def fn(x, W_gate, fwd, shape, dout, aux_coef=0.0):
+        T, E, k = shape.T, shape.E, shape.k
+        g = _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef)
+        if mode == "dropped":
+            fwd2 = dict(fwd)
+            yr = dict(fwd["yrows"])
+            for a in range(T * k):
+                if a not in yr:
+                    yr[a] = np.ones(shape.d)
+            fwd2["yrows"] = yr
+            return _orig["router_backward"](x, W_gate, fwd2, shape, dout, aux_coef)
+        if mode == "selected_only":
+            dl = g["dlogits"].copy()
+            for t in range(T):
+                keep = set(int(c) for c in fwd["sel"][t])
+                for i in range(E):
+                    if i not in keep:
+                        dl[t, i] = 0.0
+        elif mode in ("aux_no_E", "aux_sign"):
+            g0 = _orig["router_backward"](x, W_gate, fwd, shape, dout, 0.0)
+            aux_part = g["dlogits"] - g0["dlogits"]
+            dl = g0["dlogits"] + (aux_part / E if mode == "aux_no_E" else -aux_part)
+        elif mode == "dx_untransposed":
+            W = np.asarray(W_gate, np.float64)
+            g["dx"] = g["dlogits"] @ (W if W.shape[0] == W.shape[1] else W.T)
+            return g
+        elif mode == "dw_unweighted":
+            dl = g["dlogits"].copy()
+            w = fwd["w"]
+            for t in range(T):
+                s = float(np.dot(w[t], g["dw"][t]))
+                for j in range(k):
+                    dl[t, fwd["sel"][t, j]] = g["dw"][t, j] - s
+        x64 = np.asarray(x, np.float64)
+        return dict(dw=g["dw"], dlogits=dl, dW_gate=x64.T @ dl, dbias=dl.sum(0),
+                    dx=dl @ np.asarray(W_gate, np.float64).T)
+    return fn
+
+
 MUTATIONS = {
+    "bwd_dropped_rows_counted": ("router_backward", _bwd_variant("dropped")),
+    "bwd_no_signal_to_unchosen": ("router_backward", _bwd_variant("selected_only")),
+    "bwd_aux_without_E": ("router_backward", _bwd_variant("aux_no_E")),
+    "bwd_aux_sign": ("router_backward", _bwd_variant("aux_sign")),
+    "bwd_dx_untransposed": ("router_backward", _bwd_variant("dx_untransposed")),
+    "bwd_jacobian_unweighted": ("router_backward", _bwd_variant("dw_unweighted")),
     "reroute_ties_to_high_index": ("dispatch_policy", _reroute_variant("high")),
     "reroute_onto_own_choice": ("dispatch_policy", _reroute_variant("own")),
     "reroute_to_worst_spare": ("dispatch_policy", _reroute_variant("worst")),
