@@ -465,7 +465,8 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
 # ---------------------------------------------------------------------------
 def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
                     shape: LayerShape, dout: np.ndarray,
-                    aux_coef: float = 0.0) -> dict:
+                    aux_coef: float = 0.0,
+                    tokens: Optional[Sequence[int]] = None) -> dict:
     """Gradients of  L = sum(dout * out) + aux_coef * aux  with respect to the
     gate weights (dw [T, k]), the router scores (dlogits [T, E]), W_gate
     (dW_gate [d, E]), the bias (dbias [E]) and the router's share of dx
@@ -483,6 +484,9 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
           dl[t, m] += aux_coef (E / T) p[t, m] (f_m - sum_i f_i p[t, i]);
       scores l = x W_gate + b:  dW_gate = x^T dl, dbias = sum_t dl[t],
       dx = dl W_gate^T.
+    ``tokens`` limits dw, dlogits and dx to those tokens (the others are NaN;
+    ``forward`` must have computed their rows) and leaves out dW_gate and
+    dbias, which need every token.
     """
     T, E, k = shape.T, shape.E, shape.k
     x64 = np.asarray(x, dtype=np.float64)
@@ -490,17 +494,19 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
     g = np.asarray(dout, dtype=np.float64)
     sel, w, p = fwd["sel"], fwd["w"], fwd["p"]
     yrows = fwd["yrows"]
-    dw = np.zeros((T, k))
-    for t in range(T):
+    todo = range(T) if tokens is None else sorted(set(int(t) for t in tokens))
+    dw = np.zeros((T, k)) if tokens is None else np.full((T, k), np.nan)
+    for t in todo:
         for j in range(k):
             a = t * k + j
             if a in yrows:
                 dw[t, j] = float(np.dot(g[t], yrows[a]))
             elif fwd["dispatch"]["slot"][a] >= 0:
                 raise ValueError("forward did not compute every kept row")
-    dl = np.zeros((T, E))
+    dl = np.zeros((T, E)) if tokens is None else np.full((T, E), np.nan)
     softmax_over_chosen = (shape.gating == TOPK_THEN_SOFTMAX or shape.renormalize)
-    for t in range(T):
+    for t in todo:
+        dl[t] = 0.0
         s = float(np.dot(w[t], dw[t]))
         if softmax_over_chosen:
             for j in range(k):
@@ -512,8 +518,13 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
             dl[t] = p[t] * (G - s)
     if aux_coef != 0.0 and T > 0:
         f = fwd["dispatch"]["counts"].astype(np.float64) / (T * k)
-        for t in range(T):
+        for t in todo:
             dl[t] += aux_coef * (E / T) * p[t] * (f - float(np.dot(f, p[t])))
+    if tokens is not None:
+        dx = np.full((T, x64.shape[1]), np.nan)
+        for t in todo:
+            dx[t] = dl[t] @ W64.T
+        return dict(dw=dw, dlogits=dl, dW_gate=None, dbias=None, dx=dx)
     return dict(dw=dw, dlogits=dl, dW_gate=x64.T @ dl, dbias=dl.sum(axis=0),
                 dx=dl @ W64.T)
 

@@ -671,6 +671,20 @@ def pin_router_backward_closed_forms(O):
     assert np.allclose(g["dlogits"], 0.0, atol=1e-15)
 
 
+def pin_router_backward_token_subset(O):
+    # Rows computed for a subset of tokens equal the full computation's rows.
+    x, ex, Wg, b, dout, shape = _bwd_case(O, O.SOFTMAX_THEN_TOPK, False, 0.8, seed=20)
+    _, full = _loss(O, x, ex, Wg, b, dout, shape, 0.4)
+    g = O.router_backward(x, Wg, full, shape, dout, aux_coef=0.4)
+    toks = [0, 3, 7, shape.T - 1]
+    part = O.forward(x, shape, lambda e: ex[e], logits=O.router_logits(x, Wg, b), tokens=toks)
+    h = O.router_backward(x, Wg, part, shape, dout, aux_coef=0.4, tokens=toks)
+    for key in ("dw", "dlogits", "dx"):
+        assert np.allclose(h[key][toks], g[key][toks], rtol=1e-13, atol=1e-15), key
+        rest = [t for t in range(shape.T) if t not in toks]
+        assert np.all(np.isnan(h[key][rest]))
+
+
 # ---------------------------------------------------------------- stats
 def pin_stats_closed_forms(O):
     E, k, T = 8, 2, 64
