@@ -497,6 +497,7 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
     todo = range(T) if tokens is None else sorted(set(int(t) for t in tokens))
     dw = np.zeros((T, k)) if tokens is None else np.full((T, k), np.nan)
     for t in todo:
+        dw[t] = 0.0
         for j in range(k):
             a = t * k + j
             if a in yrows:
