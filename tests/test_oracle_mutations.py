@@ -228,7 +228,9 @@ def _bwd_variant(mode):
     'aux_sign' flips the auxiliary term, 'dx_untransposed' multiplies by
     W_gate instead of its transpose (shapes allowing), 'dw_unweighted' leaves
     out the gate weight in the chosen-softmax Jacobian."""
-    def fn(x, W_gate, fwd, shape, dout, aux_coef=0.0):
+    def fn(x, W_gate, fwd, shape, dout, aux_coef=0.0, tokens=None):
+        if tokens is not None:   # the planted mistakes live in the full computation
+            return _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef, tokens)
         T, E, k = shape.T, shape.E, shape.k
         g = _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef)
         if mode == "dropped":
