@@ -205,6 +205,38 @@ int moe_route_logits(const float* logits, const moe_config_t* cfg,
 int moe_aux_loss(const float* logits, const int32_t* counts,
                  const moe_config_t* cfg, double* aux_out);
 
+/* Router backward, after moe_forward.  Gradients of
+ *   L = sum(dout * out) + aux_coef * aux
+ * with respect to the router: the gate weights move through their softmax,
+ * so in the softmax-over-all order (DeepSeek, not renormalised) every
+ * expert's score receives gradient, chosen or not; aux = E sum f_i P_i moves
+ * through P_i with the load fractions f_i held fixed, as are the top-k
+ * choices and the capacity decisions.  [Routing guide] "Plain explanation"
+ * paras 2 and 4.
+ *   dw[t,j]       = dout[t] . y[t,j] for an assignment an expert ran, else 0
+ *   softmax over the k chosen (Mixtral, or DeepSeek renormalised):
+ *       dlogits[t, c_j] = w_j (dw_j - sum_i w_i dw_i), 0 at other experts
+ *   softmax over all E read at the chosen ones:
+ *       dlogits[t, i]   = p_i (G_i - sum_j w_j dw_j), G_i = dw_j at i = c_j
+ *   + aux_coef (E/T) p_i (f_i - sum_m f_m p_m),  f_i = counts_i / (T k)
+ *   dW_gate = x^T dlogits, dbias = sum_t dlogits[t], dx = dlogits W_gate^T
+ * Must follow moe_forward on the same stream with the same cfg, inputs and
+ * workspace, with no other call using that workspace in between: the
+ * forward leaves its scores, choices, gates, slots, counts and expert output
+ * rows there.  Arguments (device):
+ *   x [T, d], W_gate [d, E]  the forward's inputs (x needed for dW_gate,
+ *                            W_gate for dx; otherwise may be NULL)
+ *   dout     [T, d]  cfg->dtype, gradient of L with respect to out
+ *   dlogits  [T, E]  fp32 out (required)
+ *   dW_gate  [d, E]  fp32 out, or NULL
+ *   dbias    [E]     fp32 out, or NULL (gradient of the score bias)
+ *   dx       [T, d]  fp32 out, or NULL: the router's share of dL/dx only
+ * Enqueued on cfg->stream; sums run in a fixed order (bitwise reproducible). */
+int moe_router_backward(const void* x, const void* W_gate, const void* dout,
+                        double aux_coef, const moe_config_t* cfg,
+                        float* dlogits, float* dW_gate, float* dbias,
+                        float* dx);
+
 /* Reason for the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 

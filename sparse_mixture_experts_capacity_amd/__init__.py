@@ -23,7 +23,8 @@ from ._lib import (LIB, MoeConfig, MoeStats, MoeError, MOE_OK, MOE_EINVAL,  # no
 __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
     "moe_workspace_size", "moe_capacity", "moe_forward", "moe_route",
-    "moe_route_logits", "moe_aux_loss", "moe_last_error", "moe_timing_enable",
+    "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
+    "moe_timing_enable",
     "moe_timing_reset", "moe_timing_read", "Workspace",
 ]
 
@@ -172,6 +173,16 @@ def moe_route_logits(logits, cfg: MoeConfig, topk_idx=None, topk_w=None,
                               ctypes.byref(st) if st is not None else None)
     _check(rc, "moe_route_logits")
     return _stats_dict(st, c, k) if stats else None
+
+
+def moe_router_backward(x, W_gate, dout, cfg: MoeConfig, dlogits, dW_gate=None,
+                        dbias=None, dx=None, aux_coef: float = 0.0) -> None:
+    """Router gradients after ``moe_forward`` with the same cfg and workspace
+    (see include/moe.h)."""
+    rc = LIB.moe_router_backward(_ptr(x), _ptr(W_gate), _ptr(dout), float(aux_coef),
+                                 ctypes.byref(cfg), _ptr(dlogits), _ptr(dW_gate),
+                                 _ptr(dbias), _ptr(dx))
+    _check(rc, "moe_router_backward")
 
 
 def moe_aux_loss(logits, counts, cfg: MoeConfig) -> float:

@@ -1,6 +1,6 @@
 """Build libmoe.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m sparse_mixture_experts_capacity_amd.build     # or build()
+    python sparse_mixture_experts_capacity_amd/build.py     # or __graft_entry__.build()
 
 Objects go to _build/ at the repository root; the shared library is written
 next to this file, where the Python binding loads it.
@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["routing.hip", "ffn_grouped.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["routing.hip", "ffn_grouped.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,272 @@
+// Router backward for libmoe (gfx950): gradients of
+//   L = sum(dout * out) + aux_coef * aux
+// with respect to the router scores, W_gate, the score bias and the router's
+// share of x, from the routing state and expert output rows a forward call
+// left in the workspace.
+//
+// Pages: [Routing guide] "MoE routing, fully explained" (allinfo.ai.kr),
+// "Plain explanation" para 2 (the router learns through its softmax over the
+// experts) and para 4 (the auxiliary load-balancing product E sum f_i P_i).
+// The selection, the capacity decisions and the counts f_i are piecewise
+// constant and carry no gradient.
+//
+// Every sum runs in a fixed order (no atomics): results are bitwise
+// reproducible.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace moe {
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = kWave / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Gate backward, one wavefront per token t:
+//   dw_j = dout[t] . y_j for each assignment some expert ran (y_j: the sum of
+//          the down projection's K parts at the assignment's slot), else 0;
+//   s    = sum_j w_j dw_j;
+//   chosen-softmax gates (top-k then softmax, or renormalised):
+//          dl[c_j] = w_j (dw_j - s), 0 for the other experts;
+//   softmax over all experts read at the chosen ones:
+//          dl[i] = p_i (G_i - s) with G_i = dw_j for i = c_j, else 0;
+//   plus aux_scale p_i (f_i - sum_m f_m p_m), aux_scale = aux_coef E / T,
+//   f_i = counts_i / (T k).
+// p is the full softmax of the stored scores (NaN as -infinity), formed as
+// the forward forms it.  Lane i holds experts i, i + 64, i + 128, i + 192.
+// ---------------------------------------------------------------------------
+template <typename TOut>
+__global__ __launch_bounds__(256) void gate_backward_kernel(
+    const TOut* __restrict__ dout, const float* __restrict__ Y, int ysplit, int64_t ystride,
+    int64_t rows, const int32_t* __restrict__ slot, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, const float* __restrict__ logits,
+    const int32_t* __restrict__ counts, int64_t T, int k, int E, int d, int chosen_softmax,
+    float aux_scale, float inv_tk, float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  constexpr int V = kMaxExperts / kWave;
+  float G[V], Wc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) G[v] = Wc[v] = 0.f;
+  const TOut* g = dout + t * d;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int64_t a = t * k + j;
+    const int sl = slot[a];
+    float dwj = 0.f;
+    if (sl >= 0 && sl < rows) {   // slots outside the row buffer are never read
+      const float* y = Y + static_cast<int64_t>(sl) * d;
+      float acc = 0.f;
+#pragma unroll 4
+      for (int c = lane; c < d; c += kWave) {
+        float yv = y[c];
+        for (int q = 1; q < ysplit; ++q) yv += y[q * ystride + c];
+        acc += load_elem(g, c) * yv;
+      }
+      dwj = wave_sum(acc);
+    }
+    const float wj = w[a];
+    s += wj * dwj;
+    const int cj = idx[a];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (lane + v * kWave == cj) {
+        G[v] = dwj;
+        Wc[v] = wj;
+      }
+  }
+  // full softmax of the token's scores
+  float l[V];
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int i = lane + v * kWave;
+    float x = -INFINITY;
+    if (i < E) {
+      x = logits[t * E + i];
+      if (x != x) x = -INFINITY;
+    }
+    l[v] = x;
+    m = fmaxf(m, x);
+  }
+  m = wave_max(m);
+  float ex[V];
+  float z = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    ex[v] = (l[v] > -INFINITY) ? expf(l[v] - m) : 0.f;
+    z += ex[v];
+  }
+  z = wave_sum(z);
+  const float inv_z = 1.0f / z;
+  float fp = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int i = lane + v * kWave;
+    if (i < E) fp += counts[i] * inv_tk * (ex[v] * inv_z);
+  }
+  fp = wave_sum(fp);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int i = lane + v * kWave;
+    if (i >= E) continue;
+    const float p = ex[v] * inv_z;
+    float dl = chosen_softmax ? Wc[v] * (G[v] - s) : p * (G[v] - s);
+    if (aux_scale != 0.f) dl += aux_scale * p * (counts[i] * inv_tk - fp);
+    dlogits[t * E + i] = dl;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dW_gate partial sums: part[chunk][c][e] = sum over the chunk's tokens of
+// x[t, c] dl[t, e], and bpart[chunk][e] = sum of dl[t, e].  A workgroup
+// covers 64 columns c and 32 experts; lane c of wavefront q keeps experts
+// e0 + 8q .. e0 + 8q + 7.  The scores a wavefront reads are the same for all
+// its lanes.
+// ---------------------------------------------------------------------------
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(
+    const TIn* __restrict__ x, const float* __restrict__ dl, int64_t T, int d, int E,
+    int64_t tokens_per_chunk, float* __restrict__ part, float* __restrict__ bpart) {
+  const int cl = threadIdx.x & (kWave - 1);
+  const int q = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
+  const int c = blockIdx.x * kWave + cl;
+  const int e0 = blockIdx.y * 32 + q * 8;
+  const int64_t chunk = blockIdx.z;
+  const int64_t t0 = chunk * tokens_per_chunk;
+  const int64_t t1 = min(T, t0 + tokens_per_chunk);
+  float acc[8], bs[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = bs[u] = 0.f;
+  if (e0 < E) {
+#pragma unroll 4
+    for (int64_t t = t0; t < t1; ++t) {
+      const float xv = c < d ? load_elem(x, t * d + c) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float g = (e0 + u < E) ? dl[t * E + e0 + u] : 0.f;
+        acc[u] += xv * g;
+        bs[u] += g;
+      }
+    }
+  }
+  if (c < d) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (e0 + u < E) part[(chunk * d + c) * E + e0 + u] = acc[u];
+  }
+  if (blockIdx.x == 0 && cl == 0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (e0 + u < E) bpart[chunk * E + e0 + u] = bs[u];
+  }
+}
+
+// dW_gate[i] = sum of the chunks' partial sums in chunk order, i < d*E;
+// dbias[e] likewise.
+__global__ __launch_bounds__(256) void router_wgrad_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ bpart, int nchunk, int64_t n,
+    int E, float* __restrict__ dW, float* __restrict__ dbias) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (dW && i < n) {
+    float s = 0.f;
+    for (int q = 0; q < nchunk; ++q) s += part[q * n + i];
+    dW[i] = s;
+  }
+  if (dbias && i < E) {
+    float s = 0.f;
+    for (int q = 0; q < nchunk; ++q) s += bpart[q * E + i];
+    dbias[i] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The router's share of dx: dx[t, c] = sum_e dl[t, e] W_gate[c, e].  A
+// workgroup covers 256 columns and kDxTokens tokens; their scores sit in LDS
+// and every thread reads the same entry at a time (a broadcast); thread c
+// reads its own row of W_gate, 8 experts at a time.
+// ---------------------------------------------------------------------------
+constexpr int kDxTokens = 32;
+template <typename TIn>
+__global__ __launch_bounds__(256) void router_dx_kernel(
+    const float* __restrict__ dl, const TIn* __restrict__ Wg, int64_t T, int d, int E,
+    float* __restrict__ dx) {
+  __shared__ float sdl[kDxTokens * kMaxExperts];
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kDxTokens;
+  const int nt = static_cast<int>(min<int64_t>(kDxTokens, T - t0));
+  for (int i = threadIdx.x; i < kDxTokens * E; i += blockDim.x) {
+    const int r = i / E;
+    sdl[i] = r < nt ? dl[(t0 + r) * E + (i - r * E)] : 0.f;
+  }
+  __syncthreads();
+  if (c >= d) return;
+  float acc[kDxTokens];
+#pragma unroll
+  for (int r = 0; r < kDxTokens; ++r) acc[r] = 0.f;
+  const TIn* wrow = Wg + static_cast<int64_t>(c) * E;
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    float wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) wv[u] = (e0 + u < E) ? load_elem(wrow, e0 + u) : 0.f;
+#pragma unroll
+    for (int r = 0; r < kDxTokens; ++r)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (e0 + u < E) acc[r] += sdl[r * E + e0 + u] * wv[u];
+  }
+  for (int r = 0; r < nt; ++r) dx[(t0 + r) * d + c] = acc[r];
+}
+
+hipError_t launch_gate_backward(const RouterBackward& b, hipStream_t s) {
+  const int wpb = 4;   // tokens (wavefronts) per workgroup
+  const unsigned blocks = static_cast<unsigned>((b.T + wpb - 1) / wpb);
+  if (b.bf16)
+    gate_backward_kernel<uint16_t><<<blocks, wpb * kWave, 0, s>>>(
+        static_cast<const uint16_t*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.slot, b.idx, b.w,
+        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.inv_tk,
+        b.dlogits);
+  else
+    gate_backward_kernel<float><<<blocks, wpb * kWave, 0, s>>>(
+        static_cast<const float*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.slot, b.idx, b.w,
+        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.inv_tk,
+        b.dlogits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const RouterBackward& b, hipStream_t s) {
+  const dim3 grid((b.d + kWave - 1) / kWave, (b.E + 31) / 32, b.nchunk);
+  if (b.bf16)
+    router_wgrad_kernel<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(b.x),
+                                                       b.dlogits, b.T, b.d, b.E,
+                                                       b.tokens_per_chunk, b.part, b.bpart);
+  else
+    router_wgrad_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(b.x), b.dlogits,
+                                                    b.T, b.d, b.E, b.tokens_per_chunk, b.part,
+                                                    b.bpart);
+  const int64_t n = static_cast<int64_t>(b.d) * b.E;
+  const int64_t cover = n > b.E ? n : b.E;
+  router_wgrad_reduce_kernel<<<static_cast<unsigned>((cover + 255) / 256), 256, 0, s>>>(
+      b.part, b.bpart, b.nchunk, n, b.E, b.dW, b.dbias);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_dx(const RouterBackward& b, hipStream_t s) {
+  const dim3 grid((b.d + 255) / 256, static_cast<unsigned>((b.T + kDxTokens - 1) / kDxTokens));
+  if (b.bf16)
+    router_dx_kernel<uint16_t><<<grid, 256, 0, s>>>(
+        b.dlogits, static_cast<const uint16_t*>(b.Wg), b.T, b.d, b.E, b.dx);
+  else
+    router_dx_kernel<float><<<grid, 256, 0, s>>>(b.dlogits, static_cast<const float*>(b.Wg),
+                                                 b.T, b.d, b.E, b.dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -99,6 +99,41 @@ hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_plain_f32(const GroupedGemm& g, hipStream_t s);
 
+// ---- backward.hip ------------------------------------------------------------
+// Router backward from the routing state a forward call left behind.
+struct RouterBackward {
+  const void* x;            // [T, d] layer dtype
+  const void* Wg;           // [d, E] layer dtype
+  const void* dout;         // [T, d] layer dtype
+  const float* Y;           // expert output rows, ysplit K parts ystride apart
+  int ysplit;
+  int64_t ystride;
+  int64_t rows;             // rows of each part (slots at or past it are not read)
+  const int32_t* slot;      // [T*k]
+  const int32_t* idx;       // [T*k]
+  const float* w;           // [T*k] gates
+  const float* logits;      // [T, E] summed router scores
+  const int32_t* counts;    // [E] assignments per expert before capacity
+  int64_t T;
+  int k, E, d;
+  bool bf16;
+  int chosen_softmax;       // gates are a softmax over the k chosen scores
+  float aux_scale;          // aux_coef * E / T
+  float inv_tk;             // 1 / (T k)
+  float* dlogits;           // [T, E] out
+  float* dW;                // [d, E] out or null
+  float* dbias;             // [E] out or null
+  float* dx;                // [T, d] out or null
+  float* part;              // [nchunk, d, E] scratch
+  float* bpart;             // [nchunk, E] scratch
+  int nchunk;
+  int64_t tokens_per_chunk;
+};
+// dlogits; dW_gate and dbias (when requested); the router's share of dx.
+hipError_t launch_gate_backward(const RouterBackward& b, hipStream_t s);
+hipError_t launch_router_wgrad(const RouterBackward& b, hipStream_t s);
+hipError_t launch_router_dx(const RouterBackward& b, hipStream_t s);
+
 // ---- combine.hip -------------------------------------------------------------
 // out[t] = sum_j [slot >= 0] w[t,j] * sum_p Y[p][slot] + sum_p Ys[p][t]
 hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,

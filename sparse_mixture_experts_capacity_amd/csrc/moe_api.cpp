@@ -141,7 +141,9 @@ struct Plan {
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
   // workspace regions
   Region logits, lpart, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
-      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb, ovf, xdest, xrel;
+      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb, ovf, xdest, xrel, gpart;
+  int bwd_chunks = 1;            // token chunks of the router weight gradient
+  int64_t bwd_tokens_per_chunk = 0;
   size_t total = 0;
 };
 
@@ -377,6 +379,21 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->ovf, rr, cur);
   add(p->xdest, rr, cur);
   add(p->xrel, rr, cur);
+  // Router backward: the weight gradient sums x^T dlogits over token chunks
+  // of at least 256 tokens, with at most 16 MiB of partial sums.
+  {
+    const int64_t per = static_cast<int64_t>(p->d) * p->E + p->E;
+    int64_t nc = (p->T + 255) / 256;
+    const int64_t cap = (int64_t(16) << 20) / (4 * per);
+    if (nc > cap) nc = cap;
+    if (nc > 64) nc = 64;
+    if (nc < 1) nc = 1;
+    p->bwd_tokens_per_chunk = (p->T + nc - 1) / nc;
+    if (p->bwd_tokens_per_chunk < 1) p->bwd_tokens_per_chunk = 1;
+    p->bwd_chunks = static_cast<int>((p->T + p->bwd_tokens_per_chunk - 1) / p->bwd_tokens_per_chunk);
+    if (p->bwd_chunks < 1) p->bwd_chunks = 1;
+    add(p->gpart, sizeof(float) * per * p->bwd_chunks, cur);
+  }
   p->total = cur;
   return MOE_OK;
 }
@@ -583,7 +600,9 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   Scores sc;
   rc = run_router(p, ws, x, W_gate, cfg->logit_bias, s, &sc);
   if (rc != MOE_OK) return rc;
-  rc = run_route(p, ws, sc, nullptr, idx, w, s);
+  // the summed scores stay in the workspace for the router backward
+  rc = run_route(p, ws, sc, sc.lsrc == at<float>(ws, p.logits) ? nullptr : at<float>(ws, p.logits),
+                 idx, w, s);
   if (rc != MOE_OK) return rc;
 
   const int64_t dF = static_cast<int64_t>(p.d) * p.F;
@@ -677,6 +696,54 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   if (stats) {
     rc = fill_stats(p, ws, s, stats, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount));
     if (rc != MOE_OK) return rc;
+  }
+  g_err.clear();
+  return MOE_OK;
+}
+
+int moe_router_backward(const void* x, const void* W_gate, const void* dout, double aux_coef,
+                        const moe_config_t* cfg, float* dlogits, float* dW_gate, float* dbias,
+                        float* dx) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (!isfinite(aux_coef)) return fail(MOE_EINVAL, "aux_coef must be finite");
+  if (p.T == 0) {
+    g_err.clear();
+    return MOE_OK;
+  }
+  if (!dout || !dlogits) return fail(MOE_EINVAL, "dout and dlogits must be non-NULL");
+  if (dW_gate && !x) return fail(MOE_EINVAL, "x must be non-NULL when dW_gate is requested");
+  if (dx && !W_gate) return fail(MOE_EINVAL, "W_gate must be non-NULL when dx is requested");
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  void* ws = cfg->workspace;
+  moe::RouterBackward b{};
+  b.x = x; b.Wg = W_gate; b.dout = dout;
+  b.Y = at<float>(ws, p.Y); b.ysplit = p.ffn2_split; b.ystride = p.rows_max * p.d;
+  b.rows = p.rows_max;
+  b.slot = at<int32_t>(ws, p.slot); b.idx = at<int32_t>(ws, p.idx); b.w = at<float>(ws, p.w);
+  b.logits = at<float>(ws, p.logits); b.counts = at<int32_t>(ws, p.counts);
+  b.T = p.T; b.k = p.k; b.E = p.E; b.d = p.d; b.bf16 = p.bf16;
+  b.chosen_softmax = (p.gating == MOE_TOPK_THEN_SOFTMAX || p.renorm) ? 1 : 0;
+  b.aux_scale = static_cast<float>(aux_coef * p.E / static_cast<double>(p.T));
+  b.inv_tk = static_cast<float>(1.0 / (static_cast<double>(p.T) * p.k));
+  b.dlogits = dlogits; b.dW = dW_gate; b.dbias = dbias; b.dx = dx;
+  b.part = at<float>(ws, p.gpart);
+  b.bpart = b.part + static_cast<int64_t>(p.bwd_chunks) * p.d * p.E;
+  b.nchunk = p.bwd_chunks; b.tokens_per_chunk = p.bwd_tokens_per_chunk;
+  {
+    Timed t("gate_backward", s);
+    HIP_TRY(moe::launch_gate_backward(b, s));
+  }
+  if (dW_gate || dbias) {
+    Timed t("router_wgrad", s);
+    HIP_TRY(moe::launch_router_wgrad(b, s));
+  }
+  if (dx) {
+    Timed t("router_dx", s);
+    HIP_TRY(moe::launch_router_dx(b, s));
   }
   g_err.clear();
   return MOE_OK;

@@ -125,3 +125,21 @@ def test_overflow_policies_size_the_workspace():
     # the reported capacity is the policy-independent C
     for pol in (moe.OVERFLOW_DROP, moe.OVERFLOW_REROUTE, moe.OVERFLOW_SEQUENTIAL):
         assert moe.moe_capacity(cfg(T=4096, capacity_factor=0.5, overflow=pol)) == 512
+
+
+def test_router_backward_argument_checks():
+    # host-side validation only: nothing is launched
+    c = cfg(T=64)
+    assert moe.LIB.moe_router_backward(None, None, None, 0.0, ctypes.byref(c), None, None,
+                                       None, None) == moe.MOE_EINVAL
+    assert "dout" in moe.moe_last_error()
+    fake = 256   # never dereferenced: the checks fail first
+    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, ctypes.byref(c), fake, fake,
+                                       None, None) == moe.MOE_EINVAL
+    assert "x must be" in moe.moe_last_error()
+    assert moe.LIB.moe_router_backward(None, None, fake, float("inf"), ctypes.byref(c), fake,
+                                       None, None, None) == moe.MOE_EINVAL
+    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, ctypes.byref(c), fake, None,
+                                       None, None) == moe.MOE_EWORKSPACE
+    assert moe.LIB.moe_router_backward(None, None, None, 0.0, ctypes.byref(cfg(T=0)), None,
+                                       None, None, None) == moe.MOE_OK

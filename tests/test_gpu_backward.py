@@ -1,0 +1,195 @@
+"""GPU parity of the router backward (moe_router_backward) against the fp64
+oracle, through the C ABI: dlogits, dW_gate, dbias and the router's share
+of dx after a forward call on the same inputs.
+
+Bounds, element by element, from the arithmetic.  The gate gradient
+dw_j = dout . y_j is a dot product that can cancel, so its error scale is
+D_j = sum_c |dout_c y_jc| times the relative error of the expert rows y
+(tol: 2e-2 for bf16 layers, whose hidden rows are rounded to bf16; 1e-5 for
+fp32 layers).  A score gradient p_i (G_i - s) or w_i (dw_i - s), s = sum_j
+w_j dw_j, then has the bound tol * (p_i or w_i) * (D_i + sum_j w_j D_j)
+(D_i: that of the assignment on expert i), plus tol times the auxiliary
+term's own scale aux_coef (E/T) p_i (f_i + sum_m f_m p_m).  The weight, bias and input
+gradients are linear in the score gradients, so their bounds are that bound
+B carried through the same maps: |x|^T B, sum_t B, B |W_gate|^T.  They are
+also checked, to 1e-5 of their RMS, against the fp64 products of the
+library's own dlogits (x^T dl, sum_t dl, dl W_gate^T): properties that hold
+at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.oracle as O
+import sparse_mixture_experts_capacity_amd as moe
+from gpu_helpers import DEV, Run, config_for, full_order_margin, say, shape_of, to64
+from workloads import PRESETS, SKEW_BIAS, SOFTMAX_THEN_TOPK, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dout(w: Workload, seed=7):
+    g = torch.Generator().manual_seed(1000 + seed)
+    return torch.randn((w.T, w.d), generator=g).to(w.torch_dtype)
+
+
+def _run_backward(run: Run, dout: torch.Tensor, aux_coef: float):
+    w = run.w
+    cfg = config_for(w, bias=run.bias, stream=None)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=DEV)
+    moe.moe_forward(run.x, run.Wg, run.W1, run.W3, run.W2, cfg, out)
+    dd = dout.to(DEV)
+    g = dict(dlogits=torch.full((w.T, w.E), float("nan"), device=DEV),
+             dW_gate=torch.full((w.d, w.E), float("nan"), device=DEV),
+             dbias=torch.full((w.E,), float("nan"), device=DEV),
+             dx=torch.full((w.T, w.d), float("nan"), device=DEV))
+    moe.moe_router_backward(run.x, run.Wg, dd, cfg, g["dlogits"], g["dW_gate"], g["dbias"],
+                            g["dx"], aux_coef=aux_coef)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy().astype(np.float64) for k, v in g.items()}
+
+
+def _within(got, ref, tol):
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return err <= tol * max(rms, 1e-30), err, rms
+
+
+def _dl_bound(fwd, dout64, w: Workload, alpha, tol, tokens=None):
+    """Per-element bound on |dlogits - ref| (rows of ``tokens``, or all)."""
+    T, E, k = w.T, w.E, w.k
+    todo = range(T) if tokens is None else tokens
+    B = np.zeros((T, E))
+    chosen = w.gating != SOFTMAX_THEN_TOPK or w.renormalize
+    f = fwd["dispatch"]["counts"].astype(np.float64) / (T * k)
+    for t in todo:
+        wt, p = fwd["w"][t], fwd["p"][t]
+        D = np.zeros(k)
+        for j in range(k):
+            y = fwd["yrows"].get(t * k + j)
+            if y is not None:
+                D[j] = float(np.sum(np.abs(dout64[t] * y)))
+        s_abs = float(np.sum(wt * D))
+        G = np.zeros(E)
+        for j in range(k):
+            G[fwd["sel"][t, j]] = D[j]
+        if chosen:
+            for j in range(k):
+                c = fwd["sel"][t, j]
+                B[t, c] = wt[j] * (D[j] + s_abs)
+        else:
+            B[t] = p * (G + s_abs)
+        B[t] += abs(alpha) * (E / T) * p * (f + float(np.dot(f, p)))
+    return tol * B
+
+
+def _check_bounded(name, got, ref, bound):
+    diff = np.abs(got - ref)
+    excess = float(np.max(diff - bound)) if diff.size else 0.0
+    ratio = float(np.max(diff / np.maximum(bound, 1e-300))) if diff.size else 0.0
+    say(f"  {name}: max|d| {float(np.max(diff)):.3e}, max |d|/bound {ratio:.3f}")
+    assert excess <= 0.0, (name, excess)
+
+
+def _check_properties(g, x64, W64):
+    """dW_gate, dbias, dx against fp64 products of the library's dlogits."""
+    dl = g["dlogits"]
+    for key, ref in (("dW_gate", x64.T @ dl), ("dbias", dl.sum(axis=0)), ("dx", dl @ W64.T)):
+        ok, err, rms = _within(g[key], ref, 1e-5)
+        assert ok, (key, err, rms)
+
+
+BACKWARD_CASES = {
+    "bf16_mixtral_drops_aux": (Workload("bw_mix", T=300, d=256, F=256, E=8, k=2,
+                                        capacity_factor=1.0, bias=SKEW_BIAS), 0.5),
+    "bf16_deepseek_shared": (Workload("bw_ds", T=256, d=256, F=128, E=32, k=6, S=2,
+                                      gating=SOFTMAX_THEN_TOPK, renormalize=False,
+                                      capacity_factor=1.0), 0.25),
+    "bf16_deepseek_renorm": (Workload("bw_dsr", T=200, d=128, F=128, E=16, k=2,
+                                      gating=SOFTMAX_THEN_TOPK, renormalize=True,
+                                      capacity_factor=1.25), 1.0),
+    # few rows: the down projection is split along K, the rows are summed
+    "bf16_short_split": (Workload("bw_short", T=16, d=256, F=384, E=8, k=2), 0.0),
+    "f32_reroute_shared": (Workload("bw_f32", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
+                                    capacity_factor=0.8, overflow=1), 0.3),
+    "f32_E40_no_aux": (Workload("bw_f32e40", T=77, d=100, F=30, E=40, k=3, dtype="f32",
+                                capacity_factor=1.0), 0.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BACKWARD_CASES))
+def test_router_backward(case):
+    w, alpha = BACKWARD_CASES[case]
+    say(f"[router backward] {case} aux_coef={alpha}")
+    run = Run(w)
+    g_route, _ = run.route()
+    ref_fwd = run.oracle()
+    # no routing decision within the logits' error: the oracle and the
+    # library make the same choices for every token
+    Lg = g_route["logits"].numpy().astype(np.float64)
+    err = float(np.max(np.abs(Lg - ref_fwd["logits"])))
+    margin = (full_order_margin(ref_fwd["logits"]) if w.overflow == O.OVERFLOW_REROUTE
+              else ref_fwd["margin"])
+    assert float(np.min(margin)) > max(1e-6, 4 * err)
+    dout = _dout(w)
+    ref = O.router_backward(to64(run.hx), to64(run.hWg), ref_fwd, shape_of(run.w), to64(dout),
+                            aux_coef=alpha)
+    g = _run_backward(run, dout, alpha)
+    tol = 1e-5 if w.dtype == "f32" else 2e-2
+    for key in ("dlogits", "dW_gate", "dbias", "dx"):
+        assert np.all(np.isfinite(g[key])), key
+    B = _dl_bound(ref_fwd, to64(dout), w, alpha, tol)
+    x64, W64 = to64(run.hx), to64(run.hWg)
+    _check_bounded("dlogits", g["dlogits"], ref["dlogits"], B)
+    _check_bounded("dW_gate", g["dW_gate"], ref["dW_gate"], np.abs(x64).T @ B)
+    _check_bounded("dbias", g["dbias"], ref["dbias"], B.sum(axis=0))
+    _check_bounded("dx", g["dx"], ref["dx"], B @ np.abs(W64).T)
+    if w.gating == SOFTMAX_THEN_TOPK and not w.renormalize:
+        # experts a token did not choose receive gradient too
+        unchosen = np.ones((w.T, w.E), dtype=bool)
+        np.put_along_axis(unchosen, ref_fwd["sel"], False, axis=1)
+        assert np.count_nonzero(g["dlogits"][unchosen]) > 0.9 * unchosen.sum()
+    _check_properties(g, to64(run.hx), to64(run.hWg))
+
+
+def test_router_backward_deterministic():
+    w, alpha = BACKWARD_CASES["bf16_deepseek_shared"]
+    say("[router backward] determinism")
+    run = Run(w)
+    dout = _dout(w, seed=3)
+    a = _run_backward(run, dout, alpha)
+    b = _run_backward(run, dout, alpha)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["mixtral_prefill", "deepseek"])
+def test_router_backward_full_size_sampled(name):
+    w = PRESETS[name]
+    alpha = 0.01
+    say(f"[router backward full] {name}")
+    run = Run(w, gen_device=DEV)
+    g_route, _ = run.route()
+    routing = run.oracle(tokens=[])
+    rng = np.random.default_rng(5)
+    toks = sorted(set(rng.choice(w.T, size=24, replace=False).tolist()) | {0, w.T - 1})
+    ref_fwd = run.oracle(tokens=toks)
+    Lg = g_route["logits"].numpy().astype(np.float64)
+    err = float(np.max(np.abs(Lg - routing["logits"])))
+    thr = max(1e-6, 4 * err)
+    if w.capacity_factor > 0 and routing["dispatch"]["overflowed"] > 0:
+        first_tie = np.nonzero(routing["margin"] < thr)[0]
+        toks = [t for t in toks if len(first_tie) == 0 or t < first_tie.min()]
+    toks = [t for t in toks if routing["margin"][t] >= thr]
+    assert len(toks) >= 20
+    dout = _dout(w, seed=11)
+    ref = O.router_backward(to64(run.hx), to64(run.hWg), ref_fwd, shape_of(run.w),
+                            to64(dout), aux_coef=alpha, tokens=toks)
+    g = _run_backward(run, dout, alpha)
+    B = _dl_bound(ref_fwd, to64(dout), w, alpha, 2e-2, tokens=toks)[toks]
+    say(f"  {len(toks)} sampled tokens")
+    _check_bounded("dlogits", g["dlogits"][toks], ref["dlogits"][toks], B)
+    _check_bounded("dx", g["dx"][toks], ref["dx"][toks], B @ np.abs(to64(run.hWg)).T)
+    _check_properties(g, to64(run.hx), to64(run.hWg))
