@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the router backward (moe_router_backward) after the forward")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="override the workload's capacity factor")
     ap.add_argument("--overflow", default="drop", choices=["drop", "reroute", "sequential"],
@@ -209,6 +211,37 @@ def main():
         kern = moe.moe_timing_read()
         step_ms = sorted(a.elapsed_time(b) for a, b in ev)
 
+        # Router backward (not part of the forward's timed region): after one
+        # forward on this workspace, K timed backward calls with every output.
+        bwd = None
+        if args.backward:
+            step()
+            gen = torch.Generator(device=dev).manual_seed(1234)
+            dout = torch.randn((w.T, w.d), generator=gen, device=dev).to(w.torch_dtype)
+            dl = torch.empty((w.T, w.E), dtype=torch.float32, device=dev)
+            dWg = torch.empty((w.d, w.E), dtype=torch.float32, device=dev)
+            db = torch.empty((w.E,), dtype=torch.float32, device=dev)
+            dx = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+
+            def bstep():
+                moe.moe_router_backward(inp.x, inp.W_gate, dout, cfg, dl, dWg, db, dx,
+                                        aux_coef=0.01)
+
+            for _ in range(args.warmup):
+                bstep()
+            stream.synchronize()
+            moe.moe_timing_reset()
+            moe.moe_timing_enable(True)
+            b0 = time.perf_counter()
+            for _ in range(args.steps):
+                bstep()
+            stream.synchronize()
+            b1 = time.perf_counter()
+            moe.moe_timing_enable(False)
+            bk = moe.moe_timing_read()
+            bwd = dict(ms_per_call=(b1 - b0) * 1e3 / args.steps,
+                       kernels={n: dict(launches=c, avg_ms=t / max(c, 1)) for n, (c, t) in bk.items()})
+
         # Cold steps (not part of the timed region above): a buffer larger than
         # L2 and the Infinity Cache is read before each step, so no weight
         # bytes survive from the previous step.  It is read, not written, so
@@ -315,6 +348,18 @@ def main():
                     "p90": percentile(step_ms, 90), "source": "HIP events around each timed step"},
         "cold": cold,
     }
+    if bwd is not None:
+        # The gate pass streams the kept expert rows (fp32) and dout once:
+        # it is bound by HBM.
+        es = 2 if w.dtype == "bf16" else 4
+        gbytes = kept * w.d * 4 + w.T * w.d * es + 2 * w.T * w.E * 4 + 3 * w.T * w.k * 4
+        gms = bwd["kernels"].get("gate_backward", {}).get("avg_ms", float("nan"))
+        gach = gbytes / (gms * 1e-3) / 1e9
+        bwd["roofline"] = dict(kernel="gate_backward", bound="hbm", achieved=gach,
+                               peak=PEAK_HBM_GBS, unit="GB/s", frac=gach / PEAK_HBM_GBS,
+                               per_launch=(f"{gbytes} bytes ({kept} fp32 expert rows, dout, "
+                                           f"scores and score gradients)"))
+        res["router_backward"] = bwd
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or (64 if w.T > 64 else w.T)
         cb = cpu_baseline(w, inp, n)

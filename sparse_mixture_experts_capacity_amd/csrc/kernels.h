@@ -109,6 +109,7 @@ struct RouterBackward {
   int ysplit;
   int64_t ystride;
   int64_t rows;             // rows of each part (slots at or past it are not read)
+  bool vec4;                // d % 4 == 0 and dout aligned to 4 elements
   const int32_t* slot;      // [T*k]
   const int32_t* idx;       // [T*k]
   const float* w;           // [T*k] gates
@@ -124,13 +125,25 @@ struct RouterBackward {
   float* dW;                // [d, E] out or null
   float* dbias;             // [E] out or null
   float* dx;                // [T, d] out or null
-  float* part;              // [nchunk, d, E] scratch
-  float* bpart;             // [nchunk, E] scratch
+  float* part;              // vector path: [nchunk, d, E] and [nchunk, E];
+                            // MFMA path: [wsplit, E, d], then [d, E] and [E]
+  float* bpart;
   int nchunk;
   int64_t tokens_per_chunk;
+  // bf16 layers: both router products on the MFMA GEMM
+  bool mfma;
+  int Kp;                   // E rounded up to 64
+  int64_t Tp;               // T rounded up to 64
+  int64_t T64;              // T rounded down to 64 (the GEMM's share of dW)
+  int wsplit;               // K parts of the dW GEMM
+  uint16_t* dlb;            // [T, Kp]
+  uint16_t* dlT;            // [E, Tp]
+  uint16_t* Wt;             // [Kp, d]
 };
-// dlogits; dW_gate and dbias (when requested); the router's share of dx.
+// dlogits; the bf16 operands of the MFMA products; dW_gate and dbias (when
+// requested); the router's share of dx.
 hipError_t launch_gate_backward(const RouterBackward& b, hipStream_t s);
+hipError_t launch_router_pack(const RouterBackward& b, hipStream_t s);
 hipError_t launch_router_wgrad(const RouterBackward& b, hipStream_t s);
 hipError_t launch_router_dx(const RouterBackward& b, hipStream_t s);
 

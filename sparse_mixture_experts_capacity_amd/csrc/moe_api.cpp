@@ -141,9 +141,14 @@ struct Plan {
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
   // workspace regions
   Region logits, lpart, idx, w, lrank, blkcnt, counts, kcount, offsets, slot, perm,
-      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb, ovf, xdest, xrel, gpart;
-  int bwd_chunks = 1;            // token chunks of the router weight gradient
+      tiles, ntiles, tstart, ppart, hpart, stats, H, Hs, Y, Ys, Xb, ovf, xdest, xrel, gpart,
+      bdlb, bdlT, bWt;
+  int bwd_chunks = 1;            // token chunks of the router weight gradient (vector path)
   int64_t bwd_tokens_per_chunk = 0;
+  bool bwd_mfma = false;         // router products of the backward on the MFMA GEMM
+  int bwd_Kp = 0;                // E rounded up to 64
+  int64_t bwd_Tp = 0, bwd_T64 = 0;
+  int bwd_wsplit = 1;            // K parts of the weight-gradient GEMM
   size_t total = 0;
 };
 
@@ -379,9 +384,33 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->ovf, rr, cur);
   add(p->xdest, rr, cur);
   add(p->xrel, rr, cur);
-  // Router backward: the weight gradient sums x^T dlogits over token chunks
-  // of at least 256 tokens, with at most 16 MiB of partial sums.
-  {
+  // Router backward.  bf16 layers: both router products run on the MFMA
+  // GEMM with bf16 score gradients; the weight gradient's K (tokens) is
+  // split for ~512 workgroups with at most 16 MiB of partial sums.  fp32
+  // layers: the weight gradient sums x^T dlogits on vector kernels over
+  // token chunks of at least 256 tokens, with at most 16 MiB of partials.
+  p->bwd_mfma = p->bf16;
+  if (p->bwd_mfma) {
+    p->bwd_Kp = (p->E + 63) / 64 * 64;
+    p->bwd_Tp = (p->T + 63) / 64 * 64;
+    p->bwd_T64 = p->T / 64 * 64;
+    const int64_t ed = static_cast<int64_t>(p->E) * p->d;
+    const int bmw = p->E <= 64 ? moe::kGroupedBMShort : moe::kGroupedBM;
+    const int bk = bmw == moe::kGroupedBMShort ? 64 : 32;
+    const int64_t tiles = ((p->E + bmw - 1) / bmw) * ((p->d + 255) / 256);
+    int64_t ks = (512 + tiles - 1) / tiles;
+    const int64_t nk = p->bwd_T64 / bk;
+    if (ks > nk) ks = nk;
+    const int64_t cap = (int64_t(16) << 20) / (4 * ed);
+    if (ks > cap) ks = cap;
+    if (ks > 64) ks = 64;
+    if (ks < 1) ks = 1;
+    p->bwd_wsplit = static_cast<int>(ks);
+    add(p->gpart, sizeof(float) * (ks * ed + ed + p->E), cur);
+    add(p->bdlb, 2 * static_cast<size_t>(p->T) * p->bwd_Kp, cur);
+    add(p->bdlT, 2 * static_cast<size_t>(p->E) * p->bwd_Tp, cur);
+    add(p->bWt, 2 * static_cast<size_t>(p->bwd_Kp) * p->d, cur);
+  } else {
     const int64_t per = static_cast<int64_t>(p->d) * p->E + p->E;
     int64_t nc = (p->T + 255) / 256;
     const int64_t cap = (int64_t(16) << 20) / (4 * per);
@@ -723,6 +752,7 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   b.x = x; b.Wg = W_gate; b.dout = dout;
   b.Y = at<float>(ws, p.Y); b.ysplit = p.ffn2_split; b.ystride = p.rows_max * p.d;
   b.rows = p.rows_max;
+  b.vec4 = p.d % 4 == 0 && reinterpret_cast<uintptr_t>(dout) % (4 * (p.bf16 ? 2 : 4)) == 0;
   b.slot = at<int32_t>(ws, p.slot); b.idx = at<int32_t>(ws, p.idx); b.w = at<float>(ws, p.w);
   b.logits = at<float>(ws, p.logits); b.counts = at<int32_t>(ws, p.counts);
   b.T = p.T; b.k = p.k; b.E = p.E; b.d = p.d; b.bf16 = p.bf16;
@@ -733,9 +763,16 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   b.part = at<float>(ws, p.gpart);
   b.bpart = b.part + static_cast<int64_t>(p.bwd_chunks) * p.d * p.E;
   b.nchunk = p.bwd_chunks; b.tokens_per_chunk = p.bwd_tokens_per_chunk;
+  b.mfma = p.bwd_mfma; b.Kp = p.bwd_Kp; b.Tp = p.bwd_Tp; b.T64 = p.bwd_T64;
+  b.wsplit = p.bwd_wsplit;
+  b.dlb = at<uint16_t>(ws, p.bdlb); b.dlT = at<uint16_t>(ws, p.bdlT); b.Wt = at<uint16_t>(ws, p.bWt);
   {
     Timed t("gate_backward", s);
     HIP_TRY(moe::launch_gate_backward(b, s));
+  }
+  if (p.bwd_mfma && (dW_gate || dx)) {
+    Timed t("router_pack", s);
+    HIP_TRY(moe::launch_router_pack(b, s));
   }
   if (dW_gate || dbias) {
     Timed t("router_wgrad", s);

@@ -93,12 +93,21 @@ def _check_bounded(name, got, ref, bound):
     assert excess <= 0.0, (name, excess)
 
 
-def _check_properties(g, x64, W64):
-    """dW_gate, dbias, dx against fp64 products of the library's dlogits."""
+def _check_properties(g, x64, W64, bf16):
+    """dW_gate, dbias, dx against fp64 products of the library's dlogits.
+    bf16 layers form dW_gate and dx on the MFMA GEMM from dlogits rounded to
+    bf16 (relative error <= 2^-9 per element), so each element may move by
+    2^-8 of the sum of its terms' magnitudes; otherwise the fp32 sums are
+    held to 1e-5 of the RMS."""
     dl = g["dlogits"]
-    for key, ref in (("dW_gate", x64.T @ dl), ("dbias", dl.sum(axis=0)), ("dx", dl @ W64.T)):
-        ok, err, rms = _within(g[key], ref, 1e-5)
-        assert ok, (key, err, rms)
+    adl = np.abs(dl)
+    for key, ref, mag in (("dW_gate", x64.T @ dl, np.abs(x64).T @ adl),
+                          ("dbias", dl.sum(axis=0), None),
+                          ("dx", dl @ W64.T, adl @ np.abs(W64).T)):
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        bound = 1e-5 * rms + (2.0 ** -8 * mag if (bf16 and mag is not None) else 0.0)
+        excess = float(np.max(np.abs(g[key] - ref) - bound))
+        assert excess <= 0.0, (key, excess)
 
 
 BACKWARD_CASES = {
@@ -110,6 +119,10 @@ BACKWARD_CASES = {
     "bf16_deepseek_renorm": (Workload("bw_dsr", T=200, d=128, F=128, E=16, k=2,
                                       gating=SOFTMAX_THEN_TOPK, renormalize=True,
                                       capacity_factor=1.25), 1.0),
+    # more than 64 experts: the weight-gradient GEMM takes 128-row tiles;
+    # T = 130 leaves two tokens for the vector kernel
+    "bf16_E96_tail": (Workload("bw_e96", T=130, d=128, F=64, E=96, k=4,
+                               capacity_factor=1.0), 0.2),
     # few rows: the down projection is split along K, the rows are summed
     "bf16_short_split": (Workload("bw_short", T=16, d=256, F=384, E=8, k=2), 0.0),
     "f32_reroute_shared": (Workload("bw_f32", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
@@ -151,7 +164,7 @@ def test_router_backward(case):
         unchosen = np.ones((w.T, w.E), dtype=bool)
         np.put_along_axis(unchosen, ref_fwd["sel"], False, axis=1)
         assert np.count_nonzero(g["dlogits"][unchosen]) > 0.9 * unchosen.sum()
-    _check_properties(g, to64(run.hx), to64(run.hWg))
+    _check_properties(g, to64(run.hx), to64(run.hWg), w.dtype == "bf16")
 
 
 def test_router_backward_deterministic():
@@ -192,4 +205,4 @@ def test_router_backward_full_size_sampled(name):
     say(f"  {len(toks)} sampled tokens")
     _check_bounded("dlogits", g["dlogits"][toks], ref["dlogits"][toks], B)
     _check_bounded("dx", g["dx"][toks], ref["dx"][toks], B @ np.abs(to64(run.hWg)).T)
-    _check_properties(g, to64(run.hx), to64(run.hWg))
+    _check_properties(g, to64(run.hx), to64(run.hWg), w.dtype == "bf16")
