@@ -33,9 +33,9 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM; the counter summaries are kept beside the profiles
-    "mixtral_prefill": ("5111429808994724", 4519.13e6, 121.79e6),
-    "deepseek": ("5111429808994724", 5372.37e6, 75.86e6),
-    "mixtral_decode_t64": ("5111429808994724", 1892.92e6, 3.67e6),
+    "mixtral_prefill": ("38fc169425b47bd8", 4525.59e6, 121.09e6),
+    "deepseek": ("38fc169425b47bd8", 5370.47e6, 75.88e6),
+    "mixtral_decode_t64": ("38fc169425b47bd8", 1892.93e6, 3.67e6),
 }
 SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "combine.hip", "moe_api.cpp", "common.h",
                 "kernels.h")
