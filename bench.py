@@ -126,7 +126,7 @@ def cpu_baseline(w, inp, n_tokens: int):
         return t.to(torch.float64).numpy()
 
     rng = np.random.default_rng(0)
-    toks = sorted(rng.choice(w.T, size=min(n_tokens, w.T), replace=False).tolist())
+    order = rng.permutation(w.T).tolist()   # the sample is a prefix of one seeded order
     shape = O.LayerShape(T=w.T, d=w.d, F=w.F, E=w.E, k=w.k, S=w.S, gating=w.gating,
                          renormalize=w.renormalize, capacity_factor=w.capacity_factor,
                          overflow=w.overflow)
@@ -136,9 +136,22 @@ def cpu_baseline(w, inp, n_tokens: int):
     t0 = time.perf_counter()
     O.forward(x64, shape, experts, W_gate=wg64, bias=bias, tokens=[])
     dt_route = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.forward(x64, shape, experts, W_gate=wg64, bias=bias, tokens=toks)
-    dt = time.perf_counter() - t0
+    def timed(n):
+        toks = sorted(order[:min(n, w.T)])
+        t0 = time.perf_counter()
+        O.forward(x64, shape, experts, W_gate=wg64, bias=bias, tokens=toks)
+        return toks, time.perf_counter() - t0
+
+    if n_tokens > 0:
+        toks, dt = timed(n_tokens)
+    else:
+        # Size the sample for about 12 s of oracle work: two short runs give
+        # the cost per token beyond the fixed cost of widening the weights.
+        ta = timed(32)[1]
+        tb = timed(64)[1]
+        slope = (tb - ta) / 32
+        n = w.T if slope <= 0 else int(64 + max(0.0, 12.0 - tb) / slope)
+        toks, dt = timed(max(64, min(n, w.T)))
     return dict(value=len(toks) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=(f"{w.name}: routing, capacity dispatch and statistics of all {w.T} "
                         f"tokens plus expert and shared-expert outputs of {len(toks)} "
@@ -361,8 +374,7 @@ def main():
                                            f"scores and score gradients)"))
         res["router_backward"] = bwd
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or (64 if w.T > 64 else w.T)
-        cb = cpu_baseline(w, inp, n)
+        cb = cpu_baseline(w, inp, args.cpu_sample_tokens)
         res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         res["cpu_baseline"]["routing_dispatch_stats_s"] = cb["routing_seconds"]
     print(json.dumps(res), flush=True)
