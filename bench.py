@@ -324,6 +324,13 @@ def main():
         roof["cold"] = dict(kernel_ms=cold_dom, achieved=cold_ach, frac=cold_ach / roof["peak"],
                             note=f"L2 and Infinity Cache flushed ({cold['flush_mib']} MiB "
                                  f"read) before each of {cold['steps']} extra steps")
+    # The pages' "dispatch time share" on one GPU: the time spent routing,
+    # dispatching, gathering and combining rows, as a share of all the
+    # layer's kernel time (the experts' GEMMs are the rest).
+    route_names = ("router", "topk_gate", "route_small", "dispatch", "gather", "combine")
+    kern_total = sum(v["avg_ms"] * v["launches"] for v in per_kernel.values()) / args.steps
+    route_ms = sum(per_kernel[n]["avg_ms"] * per_kernel[n]["launches"]
+                   for n in route_names if n in per_kernel) / args.steps
     layer_tflops = work["flops"] / (ms * 1e-3) / 1e12
     layer_gbs = work["bytes"] / (ms * 1e-3) / 1e9
     res = {
@@ -349,6 +356,8 @@ def main():
                   "active_frac_of_bf16_peak": layer_tflops / PEAK_BF16_TFLOPS,
                   "algorithmic_gbs": layer_gbs,
                   "frac_of_hbm_peak": layer_gbs / PEAK_HBM_GBS,
+                  "routing_ms": route_ms,
+                  "routing_time_share": route_ms / kern_total if kern_total > 0 else None,
                   "kept_assignments": kept, "experts_hit": hit,
                   "capacity": st["capacity"], "dropped": st["dropped"],
                   "overflowed": st["overflowed"], "rerouted": st["rerouted"],
