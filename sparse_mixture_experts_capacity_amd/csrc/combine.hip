@@ -36,14 +36,24 @@ __global__ __launch_bounds__(256) void combine_kernel(
       if (s < 0) continue;
       const float w = topk_w[t * k + j];
       float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-      for (int p = 0; p < ysplit; ++p) {
-        const float* row = Y + p * ysplit_stride + static_cast<int64_t>(s) * d;
-        if (vec) {
-          const float4 v = reinterpret_cast<const float4*>(row)[c];
-          y.x += v.x; y.y += v.y; y.z += v.z; y.w += v.w;
-        } else {
-          y.x += row[c];
+      // the parts are loaded 8 at a time (their loads in flight together)
+      // and added in part order
+      for (int p0 = 0; p0 < ysplit; p0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (p0 + u < ysplit) {
+            const float* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
+            if (vec) v[u] = reinterpret_cast<const float4*>(row)[c];
+            else v[u].x = row[c];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (p0 + u < ysplit) {
+            y.x += v[u].x; y.y += v[u].y; y.z += v[u].z; y.w += v[u].w;
+          }
         }
       }
       acc.x = fmaf(w, y.x, acc.x);
@@ -87,16 +97,18 @@ hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
                           int64_t T, int k, int d, void* out, bool bf16,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  // enough workgroups to cover the GPU even for a handful of tokens
+  // enough workgroups to cover the GPU even for a handful of tokens: short
+  // batches take 64-thread workgroups, each over 64 column groups
   const int ncols = (d & 3) == 0 ? d / 4 : d;
-  int chunks = (ncols + 255) / 256;
+  const int tpb = T < 64 ? 64 : 256;
+  int chunks = (ncols + tpb - 1) / tpb;
   if (T >= 256) chunks = 1;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
   if (bf16)
-    combine_kernel<true><<<grid, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+    combine_kernel<true><<<grid, tpb, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
                                               ys_split, ys_stride, T, k, d, out);
   else
-    combine_kernel<false><<<grid, 256, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
+    combine_kernel<false><<<grid, tpb, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
                                                ys_split, ys_stride, T, k, d, out);
   return hipGetLastError();
 }
