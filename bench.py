@@ -27,18 +27,19 @@ PEAK_HBM_GBS = 8000.0
 # HBM-side bytes per launch of the dominant kernel, from two rocprofv3 --pmc
 # runs (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read for
 # a 1 GiB device copy in the same run (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 on
-# MI355X).  Keyed by workload and by a digest of the library's kernel sources:
-# once a source changes, the figure no longer describes the kernel and the
-# bench reports null.
+# MI355X).  Keyed by workload and by a digest of the sources that define that
+# kernel and its launch: once one of them changes, the figure no longer
+# describes the kernel and the bench reports null.
 MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM; the counter summaries are kept beside the profiles
-    "mixtral_prefill": ("38fc169425b47bd8", 4525.59e6, 121.09e6),
-    "deepseek": ("38fc169425b47bd8", 5370.47e6, 75.88e6),
-    "mixtral_decode_t64": ("38fc169425b47bd8", 1892.93e6, 3.67e6),
+    "mixtral_prefill": ("867e93a264693add", 4525.59e6, 121.09e6),
+    "deepseek": ("867e93a264693add", 5370.47e6, 75.88e6),
+    "mixtral_decode_t64": ("867e93a264693add", 1892.93e6, 3.67e6),
 }
-SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "combine.hip", "moe_api.cpp", "common.h",
-                "kernels.h")
+# The sources that define the routed SwiGLU GEMM and its launch: the kernel,
+# the M-tile list built by the routing passes, the plan and the shared headers.
+SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "moe_api.cpp", "common.h", "kernels.h")
 
 
 def source_digest() -> str:
