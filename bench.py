@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_prefill")
     ap.add_argument("--path", default="auto", choices=["auto", "grouped", "stream"])
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once into a HIP graph and replayed "
+                         "(no per-kernel events; reported beside the eager figures)")
     ap.add_argument("--backward", action="store_true",
                     help="also time the router backward (moe_router_backward) after the forward")
     ap.add_argument("--capacity-factor", type=float, default=None,
@@ -225,6 +228,25 @@ def main():
         kern = moe.moe_timing_read()
         step_ms = sorted(a.elapsed_time(b) for a, b in ev)
 
+        # The same step captured into a graph and replayed: the launches of
+        # one step go to the GPU as one submission.
+        graph = None
+        if args.graph:
+            g = torch.cuda.CUDAGraph()
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                step()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph = dict(ms_per_step=(time.perf_counter() - g0) * 1e3 / args.steps,
+                         steps=args.steps)
+            del g
+
         # Router backward (not part of the forward's timed region): after one
         # forward on this workspace, K timed backward calls with every output.
         bwd = None
@@ -371,6 +393,9 @@ def main():
                     "p90": percentile(step_ms, 90), "source": "HIP events around each timed step"},
         "cold": cold,
     }
+    if graph is not None:
+        graph["tokens_per_s"] = w.T / (graph["ms_per_step"] * 1e-3)
+        res["graph"] = graph
     if bwd is not None:
         # The gate pass streams the kept expert rows (fp32) and dout once:
         # it is bound by HBM.
