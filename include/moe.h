@@ -52,6 +52,11 @@
  *     checked completely before anything is enqueued.  The reason for the
  *     last failure on the calling thread is in moe_last_error().
  *   - T = 0 is a valid, empty call: nothing is launched and stats are zero.
+ *   - With stats == NULL, moe_forward and moe_router_backward only enqueue
+ *     kernels on cfg->stream (no allocation, copy, memset or host wait), so
+ *     a caller may capture them into a HIP graph and replay it; a replay
+ *     reads the inputs' current contents.  Per-kernel timing must be off
+ *     while capturing.
  *   - A NaN router score ranks as -infinity (chosen only after every
  *     number; ties by index) and gets gate weight 0.
  */
