@@ -261,7 +261,7 @@ def main():
 
             def bstep():
                 moe.moe_router_backward(inp.x, inp.W_gate, dout, cfg, dl, dWg, db, dx,
-                                        aux_coef=0.01)
+                                        aux_coef=0.01, entropy_coef=0.001)
 
             for _ in range(args.warmup):
                 bstep()

@@ -211,8 +211,10 @@ int moe_aux_loss(const float* logits, const int32_t* counts,
                  const moe_config_t* cfg, double* aux_out);
 
 /* Router backward, after moe_forward.  Gradients of
- *   L = sum(dout * out) + aux_coef * aux
- * with respect to the router: the gate weights move through their softmax,
+ *   L = sum(dout * out) + aux_coef * aux + entropy_coef * H_tok
+ * with respect to the router (H_tok: the mean router entropy, the quantity a
+ * training schedule raises early and lowers later, [Routing guide] "Plain
+ * explanation" para 4): the gate weights move through their softmax,
  * so in the softmax-over-all order (DeepSeek, not renormalised) every
  * expert's score receives gradient, chosen or not; aux = E sum f_i P_i moves
  * through P_i with the load fractions f_i held fixed, as are the top-k
@@ -224,6 +226,7 @@ int moe_aux_loss(const float* logits, const int32_t* counts,
  *   softmax over all E read at the chosen ones:
  *       dlogits[t, i]   = p_i (G_i - sum_j w_j dw_j), G_i = dw_j at i = c_j
  *   + aux_coef (E/T) p_i (f_i - sum_m f_m p_m),  f_i = counts_i / (T k)
+ *   + entropy_coef (1/T) (-p_i (ln p_i + H_t)),  H_t = -sum_m p_m ln p_m
  *   dW_gate = x^T dlogits, dbias = sum_t dlogits[t], dx = dlogits W_gate^T
  * Must follow moe_forward on the same stream with the same cfg, inputs and
  * workspace, with no other call using that workspace in between: the
@@ -238,9 +241,9 @@ int moe_aux_loss(const float* logits, const int32_t* counts,
  *   dx       [T, d]  fp32 out, or NULL: the router's share of dL/dx only
  * Enqueued on cfg->stream; sums run in a fixed order (bitwise reproducible). */
 int moe_router_backward(const void* x, const void* W_gate, const void* dout,
-                        double aux_coef, const moe_config_t* cfg,
-                        float* dlogits, float* dW_gate, float* dbias,
-                        float* dx);
+                        double aux_coef, double entropy_coef,
+                        const moe_config_t* cfg, float* dlogits,
+                        float* dW_gate, float* dbias, float* dx);
 
 /* Reason for the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);

@@ -466,8 +466,10 @@ def forward(x: np.ndarray, shape: LayerShape, expert_weights: ExpertWeights,
 def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
                     shape: LayerShape, dout: np.ndarray,
                     aux_coef: float = 0.0,
-                    tokens: Optional[Sequence[int]] = None) -> dict:
-    """Gradients of  L = sum(dout * out) + aux_coef * aux  with respect to the
+                    tokens: Optional[Sequence[int]] = None,
+                    entropy_coef: float = 0.0) -> dict:
+    """Gradients of  L = sum(dout * out) + aux_coef * aux
+    + entropy_coef * H_tok  with respect to the
     gate weights (dw [T, k]), the router scores (dlogits [T, E]), W_gate
     (dW_gate [d, E]), the bias (dbias [E]) and the router's share of dx
     ([T, d]; the experts' share is not part of this).  ``fwd`` is the result
@@ -482,6 +484,10 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
       which is non-zero for every expert the token did not choose;
       aux = E sum_i f_i P_i with P_i = mean_t p[t, i] and f fixed:
           dl[t, m] += aux_coef (E / T) p[t, m] (f_m - sum_i f_i p[t, i]);
+      H_tok = mean_t H_t, H_t = -sum_i p_ti ln p_ti (the router entropy that
+      [Routing guide] "Plain explanation" paragraph 4 schedules, high early
+      in training and lower later):
+          dl[t, m] += entropy_coef (1 / T) (-p[t, m] (ln p[t, m] + H_t));
       scores l = x W_gate + b:  dW_gate = x^T dl, dbias = sum_t dl[t],
       dx = dl W_gate^T.
     ``tokens`` limits dw, dlogits and dx to those tokens (the others are NaN;
@@ -521,6 +527,13 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
         f = fwd["dispatch"]["counts"].astype(np.float64) / (T * k)
         for t in todo:
             dl[t] += aux_coef * (E / T) * p[t] * (f - float(np.dot(f, p[t])))
+    if entropy_coef != 0.0 and T > 0:
+        for t in todo:
+            pt = p[t]
+            with np.errstate(divide="ignore", invalid="ignore"):
+                lnp = np.where(pt > 0, np.log(pt), 0.0)
+            H = -float(np.sum(pt * lnp))
+            dl[t] += entropy_coef / T * (-pt * (lnp + H))
     if tokens is not None:
         dx = np.full((T, x64.shape[1]), np.nan)
         for t in todo:

@@ -176,12 +176,13 @@ def moe_route_logits(logits, cfg: MoeConfig, topk_idx=None, topk_w=None,
 
 
 def moe_router_backward(x, W_gate, dout, cfg: MoeConfig, dlogits, dW_gate=None,
-                        dbias=None, dx=None, aux_coef: float = 0.0) -> None:
+                        dbias=None, dx=None, aux_coef: float = 0.0,
+                        entropy_coef: float = 0.0) -> None:
     """Router gradients after ``moe_forward`` with the same cfg and workspace
     (see include/moe.h)."""
     rc = LIB.moe_router_backward(_ptr(x), _ptr(W_gate), _ptr(dout), float(aux_coef),
-                                 ctypes.byref(cfg), _ptr(dlogits), _ptr(dW_gate),
-                                 _ptr(dbias), _ptr(dx))
+                                 float(entropy_coef), ctypes.byref(cfg), _ptr(dlogits),
+                                 _ptr(dW_gate), _ptr(dbias), _ptr(dx))
     _check(rc, "moe_router_backward")
 
 

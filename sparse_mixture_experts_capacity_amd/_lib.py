@@ -83,7 +83,8 @@ def _load():
         "moe_route": (ctypes.c_int, [P, P, CFG, P, P, P, P, P, P, P, ST]),
         "moe_route_logits": (ctypes.c_int, [P, CFG, P, P, P, P, P, P, ST]),
         "moe_aux_loss": (ctypes.c_int, [P, P, CFG, ctypes.POINTER(ctypes.c_double)]),
-        "moe_router_backward": (ctypes.c_int, [P, P, P, ctypes.c_double, CFG, P, P, P, P]),
+        "moe_router_backward": (ctypes.c_int, [P, P, P, ctypes.c_double, ctypes.c_double, CFG,
+                                               P, P, P, P]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_timing_reset": (ctypes.c_int, []),

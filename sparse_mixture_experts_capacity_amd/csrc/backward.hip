@@ -47,7 +47,9 @@ __device__ __forceinline__ float wave_max(float v) {
 //   softmax over all experts read at the chosen ones:
 //          dl[i] = p_i (G_i - s) with G_i = dw_j for i = c_j, else 0;
 //   plus aux_scale p_i (f_i - sum_m f_m p_m), aux_scale = aux_coef E / T,
-//   f_i = counts_i / (T k).
+//   f_i = counts_i / (T k);
+//   plus ent_scale (-p_i (ln p_i + H_t)), ent_scale = entropy_coef / T, the
+//   gradient of the mean router entropy, H_t = -sum_i p_i ln p_i.
 // p is the full softmax of the stored scores (NaN as -infinity), formed as
 // the forward forms it.  Lane i holds experts i, i + 64, i + 128, i + 192.
 // ---------------------------------------------------------------------------
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(
     int64_t rows, bool vec4, const int32_t* __restrict__ slot, const int32_t* __restrict__ idx,
     const float* __restrict__ w, const float* __restrict__ logits,
     const int32_t* __restrict__ counts, int64_t T, int k, int E, int d, int chosen_softmax,
-    float aux_scale, float inv_tk, float* __restrict__ dlogits) {
+    float aux_scale, float ent_scale, float inv_tk, float* __restrict__ dlogits) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
@@ -136,6 +138,15 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(
     if (i < E) fp += counts[i] * inv_tk * (ex[v] * inv_z);
   }
   fp = wave_sum(fp);
+  // H_t = ln z - sum_i p_i (l_i - m); ln p_i = (l_i - m) - ln z
+  const float lnz = logf(z);
+  float plm = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const float p = ex[v] * inv_z;
+    if (p > 0.f) plm += p * (l[v] - m);
+  }
+  const float H = lnz - wave_sum(plm);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int i = lane + v * kWave;
@@ -143,6 +154,7 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(
     const float p = ex[v] * inv_z;
     float dl = chosen_softmax ? Wc[v] * (G[v] - s) : p * (G[v] - s);
     if (aux_scale != 0.f) dl += aux_scale * p * (counts[i] * inv_tk - fp);
+    if (ent_scale != 0.f && p > 0.f) dl -= ent_scale * p * ((l[v] - m - lnz) + H);
     dlogits[t * E + i] = dl;
   }
 }
@@ -338,12 +350,12 @@ hipError_t launch_gate_backward(const RouterBackward& b, hipStream_t s) {
   if (b.bf16)
     gate_backward_kernel<uint16_t><<<blocks, wpb * kWave, 0, s>>>(
         static_cast<const uint16_t*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
-        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.inv_tk,
+        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.ent_scale, b.inv_tk,
         b.dlogits);
   else
     gate_backward_kernel<float><<<blocks, wpb * kWave, 0, s>>>(
         static_cast<const float*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
-        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.inv_tk,
+        b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.ent_scale, b.inv_tk,
         b.dlogits);
   return hipGetLastError();
 }

@@ -120,6 +120,7 @@ struct RouterBackward {
   bool bf16;
   int chosen_softmax;       // gates are a softmax over the k chosen scores
   float aux_scale;          // aux_coef * E / T
+  float ent_scale;          // entropy_coef / T
   float inv_tk;             // 1 / (T k)
   float* dlogits;           // [T, E] out
   float* dW;                // [d, E] out or null

@@ -731,12 +731,13 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
 }
 
 int moe_router_backward(const void* x, const void* W_gate, const void* dout, double aux_coef,
-                        const moe_config_t* cfg, float* dlogits, float* dW_gate, float* dbias,
-                        float* dx) {
+                        double entropy_coef, const moe_config_t* cfg, float* dlogits,
+                        float* dW_gate, float* dbias, float* dx) {
   Plan p;
   int rc = make_plan(cfg, &p);
   if (rc != MOE_OK) return rc;
-  if (!isfinite(aux_coef)) return fail(MOE_EINVAL, "aux_coef must be finite");
+  if (!isfinite(aux_coef) || !isfinite(entropy_coef))
+    return fail(MOE_EINVAL, "aux_coef and entropy_coef must be finite");
   if (p.T == 0) {
     g_err.clear();
     return MOE_OK;
@@ -758,6 +759,7 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   b.T = p.T; b.k = p.k; b.E = p.E; b.d = p.d; b.bf16 = p.bf16;
   b.chosen_softmax = (p.gating == MOE_TOPK_THEN_SOFTMAX || p.renorm) ? 1 : 0;
   b.aux_scale = static_cast<float>(aux_coef * p.E / static_cast<double>(p.T));
+  b.ent_scale = static_cast<float>(entropy_coef / static_cast<double>(p.T));
   b.inv_tk = static_cast<float>(1.0 / (static_cast<double>(p.T) * p.k));
   b.dlogits = dlogits; b.dW = dW_gate; b.dbias = dbias; b.dx = dx;
   b.part = at<float>(ws, p.gpart);

@@ -559,28 +559,30 @@ def _bwd_case(O, gating, renorm, cf, overflow=None, T=14, d=6, F=8, E=5, k=2, S=
     return x, ex, Wg, b, dout, shape
 
 
-def _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=None):
-    """sum(dout * out) + alpha * aux, with the router reading x_router."""
+def _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=None, beta=0.0):
+    """sum(dout * out) + alpha * aux + beta * (mean router entropy), with the
+    router reading x_router."""
     xr = x if x_router is None else x_router
     res = O.forward(x, shape, lambda e: ex[e], logits=O.router_logits(xr, Wg, b))
-    return float(np.sum(dout * res["out"])) + alpha * res["stats"]["aux_loss"], res
+    return (float(np.sum(dout * res["out"])) + alpha * res["stats"]["aux_loss"]
+            + beta * res["stats"]["entropy_token"]), res
 
 
 def pin_router_backward_finite_differences(O):
     # Central differences of the layer's own forward (selection and capacity
     # decisions stay fixed: every decision margin is far above the step).
-    h, alpha = 1e-6, 0.7
+    h, alpha, beta = 1e-6, 0.7, 0.4
     for gating, renorm, cf, ovf, d in [(O.TOPK_THEN_SOFTMAX, True, 0.8, None, 6),
                                        (O.SOFTMAX_THEN_TOPK, False, 0.8, None, 6),
                                        (O.SOFTMAX_THEN_TOPK, True, 0.0, None, 6),
                                        (O.SOFTMAX_THEN_TOPK, False, 0.7, O.OVERFLOW_REROUTE, 6),
                                        (O.TOPK_THEN_SOFTMAX, True, 0.8, None, 5)]:  # d == E
         x, ex, Wg, b, dout, shape = _bwd_case(O, gating, renorm, cf, ovf, d=d)
-        L0, res = _loss(O, x, ex, Wg, b, dout, shape, alpha)
+        L0, res = _loss(O, x, ex, Wg, b, dout, shape, alpha, beta=beta)
         assert float(np.min(_full_gaps(res["logits"]))) > 5e-5   # steps move scores by ~1e-5
         if cf > 0:
             assert res["dispatch"]["overflowed"] > 0
-        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha)
+        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha, entropy_coef=beta)
         for name, arr, get in (("dW_gate", Wg, lambda v: (x, ex, v, b)),
                                ("dbias", b, lambda v: (x, ex, Wg, v))):
             num = np.zeros_like(arr)
@@ -588,8 +590,8 @@ def pin_router_backward_finite_differences(O):
                 up, dn = arr.copy(), arr.copy()
                 up[idx] += h
                 dn[idx] -= h
-                num[idx] = (_loss(O, *get(up), dout, shape, alpha)[0]
-                            - _loss(O, *get(dn), dout, shape, alpha)[0]) / (2 * h)
+                num[idx] = (_loss(O, *get(up), dout, shape, alpha, beta=beta)[0]
+                            - _loss(O, *get(dn), dout, shape, alpha, beta=beta)[0]) / (2 * h)
             assert np.allclose(g[name], num, rtol=1e-6, atol=1e-7), (name, gating, renorm)
         # dx: the router's share only (experts keep reading the unperturbed x)
         num = np.zeros_like(x)
@@ -597,8 +599,9 @@ def pin_router_backward_finite_differences(O):
             up, dn = x.copy(), x.copy()
             up[idx] += h
             dn[idx] -= h
-            num[idx] = (_loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=up)[0]
-                        - _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=dn)[0]) / (2 * h)
+            num[idx] = (_loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=up, beta=beta)[0]
+                        - _loss(O, x, ex, Wg, b, dout, shape, alpha, x_router=dn,
+                                beta=beta)[0]) / (2 * h)
         assert np.allclose(g["dx"], num, rtol=1e-6, atol=1e-7), ("dx", gating, renorm)
 
 
@@ -608,12 +611,12 @@ def _full_gaps(L):
 
 def pin_router_backward_autograd(O):
     # torch fp64 autograd of the gating with the selection held fixed.
-    alpha = 0.3
+    alpha, beta = 0.3, -0.6
     for gating, renorm in [(O.TOPK_THEN_SOFTMAX, True), (O.SOFTMAX_THEN_TOPK, False),
                            (O.SOFTMAX_THEN_TOPK, True)]:
         x, ex, Wg, b, dout, shape = _bwd_case(O, gating, renorm, 0.9, seed=17)
-        _, res = _loss(O, x, ex, Wg, b, dout, shape, alpha)
-        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha)
+        _, res = _loss(O, x, ex, Wg, b, dout, shape, alpha, beta=beta)
+        g = O.router_backward(x, Wg, res, shape, dout, aux_coef=alpha, entropy_coef=beta)
         T, E, k = shape.T, shape.E, shape.k
         sel = torch.as_tensor(res["sel"])
         Y = torch.zeros(T, k, shape.d, dtype=torch.float64)
@@ -626,8 +629,10 @@ def pin_router_backward_autograd(O):
             w = torch.gather(torch.softmax(L, dim=1), 1, sel)
         out = (w[:, :, None] * Y).sum(1)
         f = torch.as_tensor(res["dispatch"]["counts"], dtype=torch.float64) / (T * k)
-        aux = E * (f * torch.softmax(L, dim=1).mean(0)).sum()
-        loss = (torch.as_tensor(dout) * out).sum() + alpha * aux
+        P = torch.softmax(L, dim=1)
+        aux = E * (f * P.mean(0)).sum()
+        H = -(P * torch.log_softmax(L, dim=1)).sum(1).mean()
+        loss = (torch.as_tensor(dout) * out).sum() + alpha * aux + beta * H
         loss.backward()
         assert np.allclose(g["dlogits"], L.grad.numpy(), rtol=1e-10, atol=1e-12)
 
@@ -669,6 +674,19 @@ def pin_router_backward_closed_forms(O):
     g = O.router_backward(np.ones((T, 3)), np.zeros((3, E)), res, shape, np.zeros((T, 3)),
                           aux_coef=1.0)
     assert np.allclose(g["dlogits"], 0.0, atol=1e-15)
+    # Equal scores: the router entropy is at its maximum ln E, so its gradient
+    # vanishes.  With one dominant score, raising it lowers the entropy and
+    # raising any other score raises it.
+    L = np.zeros((T, E))
+    res = O.forward(np.ones((T, 3)), shape, lambda e: ex[e], logits=L)
+    g = O.router_backward(np.ones((T, 3)), np.zeros((3, E)), res, shape, np.zeros((T, 3)),
+                          entropy_coef=1.0)
+    assert np.allclose(g["dlogits"], 0.0, atol=1e-15)
+    L[:, 0] = 3.0
+    res = O.forward(np.ones((T, 3)), shape, lambda e: ex[e], logits=L)
+    g = O.router_backward(np.ones((T, 3)), np.zeros((3, E)), res, shape, np.zeros((T, 3)),
+                          entropy_coef=1.0)
+    assert np.all(g["dlogits"][:, 0] < 0) and np.all(g["dlogits"][:, 1:] > 0)
 
 
 def pin_router_backward_token_subset(O):

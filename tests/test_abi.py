@@ -130,16 +130,18 @@ def test_overflow_policies_size_the_workspace():
 def test_router_backward_argument_checks():
     # host-side validation only: nothing is launched
     c = cfg(T=64)
-    assert moe.LIB.moe_router_backward(None, None, None, 0.0, ctypes.byref(c), None, None,
+    assert moe.LIB.moe_router_backward(None, None, None, 0.0, 0.0, ctypes.byref(c), None, None,
                                        None, None) == moe.MOE_EINVAL
     assert "dout" in moe.moe_last_error()
     fake = 256   # never dereferenced: the checks fail first
-    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, ctypes.byref(c), fake, fake,
+    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, 0.0, ctypes.byref(c), fake, fake,
                                        None, None) == moe.MOE_EINVAL
     assert "x must be" in moe.moe_last_error()
-    assert moe.LIB.moe_router_backward(None, None, fake, float("inf"), ctypes.byref(c), fake,
+    assert moe.LIB.moe_router_backward(None, None, fake, float("inf"), 0.0, ctypes.byref(c), fake,
                                        None, None, None) == moe.MOE_EINVAL
-    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, ctypes.byref(c), fake, None,
+    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, float("nan"), ctypes.byref(c),
+                                       fake, None, None, None) == moe.MOE_EINVAL
+    assert moe.LIB.moe_router_backward(None, None, fake, 0.0, 0.0, ctypes.byref(c), fake, None,
                                        None, None) == moe.MOE_EWORKSPACE
-    assert moe.LIB.moe_router_backward(None, None, None, 0.0, ctypes.byref(cfg(T=0)), None,
+    assert moe.LIB.moe_router_backward(None, None, None, 0.0, 0.0, ctypes.byref(cfg(T=0)), None,
                                        None, None, None) == moe.MOE_OK

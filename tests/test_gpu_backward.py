@@ -9,7 +9,8 @@ D_j = sum_c |dout_c y_jc| times the relative error of the expert rows y
 fp32 layers).  A score gradient p_i (G_i - s) or w_i (dw_i - s), s = sum_j
 w_j dw_j, then has the bound tol * (p_i or w_i) * (D_i + sum_j w_j D_j)
 (D_i: that of the assignment on expert i), plus tol times the auxiliary
-term's own scale aux_coef (E/T) p_i (f_i + sum_m f_m p_m).  The weight, bias and input
+term's own scale aux_coef (E/T) p_i (f_i + sum_m f_m p_m) and the entropy
+term's entropy_coef (1/T) p_i (|ln p_i| + H_t).  The weight, bias and input
 gradients are linear in the score gradients, so their bounds are that bound
 B carried through the same maps: |x|^T B, sum_t B, B |W_gate|^T.  They are
 also checked, to 1e-5 of their RMS, against the fp64 products of the
@@ -33,7 +34,7 @@ def _dout(w: Workload, seed=7):
     return torch.randn((w.T, w.d), generator=g).to(w.torch_dtype)
 
 
-def _run_backward(run: Run, dout: torch.Tensor, aux_coef: float):
+def _run_backward(run: Run, dout: torch.Tensor, aux_coef: float, entropy_coef: float = 0.0):
     w = run.w
     cfg = config_for(w, bias=run.bias, stream=None)
     ws = moe.Workspace(moe.moe_workspace_size(cfg))
@@ -46,7 +47,7 @@ def _run_backward(run: Run, dout: torch.Tensor, aux_coef: float):
              dbias=torch.full((w.E,), float("nan"), device=DEV),
              dx=torch.full((w.T, w.d), float("nan"), device=DEV))
     moe.moe_router_backward(run.x, run.Wg, dd, cfg, g["dlogits"], g["dW_gate"], g["dbias"],
-                            g["dx"], aux_coef=aux_coef)
+                            g["dx"], aux_coef=aux_coef, entropy_coef=entropy_coef)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in g.items()}
 
@@ -57,7 +58,7 @@ def _within(got, ref, tol):
     return err <= tol * max(rms, 1e-30), err, rms
 
 
-def _dl_bound(fwd, dout64, w: Workload, alpha, tol, tokens=None):
+def _dl_bound(fwd, dout64, w: Workload, alpha, tol, tokens=None, beta=0.0):
     """Per-element bound on |dlogits - ref| (rows of ``tokens``, or all)."""
     T, E, k = w.T, w.E, w.k
     todo = range(T) if tokens is None else tokens
@@ -82,6 +83,9 @@ def _dl_bound(fwd, dout64, w: Workload, alpha, tol, tokens=None):
         else:
             B[t] = p * (G + s_abs)
         B[t] += abs(alpha) * (E / T) * p * (f + float(np.dot(f, p)))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            lnp = np.where(p > 0, np.log(p), 0.0)
+        B[t] += abs(beta) / T * p * (np.abs(lnp) - float(np.sum(p * lnp)))
     return tol * B
 
 
@@ -112,30 +116,30 @@ def _check_properties(g, x64, W64, bf16):
 
 BACKWARD_CASES = {
     "bf16_mixtral_drops_aux": (Workload("bw_mix", T=300, d=256, F=256, E=8, k=2,
-                                        capacity_factor=1.0, bias=SKEW_BIAS), 0.5),
+                                        capacity_factor=1.0, bias=SKEW_BIAS), 0.5, 0.2),
     "bf16_deepseek_shared": (Workload("bw_ds", T=256, d=256, F=128, E=32, k=6, S=2,
                                       gating=SOFTMAX_THEN_TOPK, renormalize=False,
-                                      capacity_factor=1.0), 0.25),
+                                      capacity_factor=1.0), 0.25, -0.1),
     "bf16_deepseek_renorm": (Workload("bw_dsr", T=200, d=128, F=128, E=16, k=2,
                                       gating=SOFTMAX_THEN_TOPK, renormalize=True,
-                                      capacity_factor=1.25), 1.0),
+                                      capacity_factor=1.25), 1.0, 0.0),
     # more than 64 experts: the weight-gradient GEMM takes 128-row tiles;
     # T = 130 leaves two tokens for the vector kernel
     "bf16_E96_tail": (Workload("bw_e96", T=130, d=128, F=64, E=96, k=4,
-                               capacity_factor=1.0), 0.2),
+                               capacity_factor=1.0), 0.2, 0.05),
     # few rows: the down projection is split along K, the rows are summed
-    "bf16_short_split": (Workload("bw_short", T=16, d=256, F=384, E=8, k=2), 0.0),
+    "bf16_short_split": (Workload("bw_short", T=16, d=256, F=384, E=8, k=2), 0.0, 0.3),
     "f32_reroute_shared": (Workload("bw_f32", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
-                                    capacity_factor=0.8, overflow=1), 0.3),
+                                    capacity_factor=0.8, overflow=1), 0.3, 0.5),
     "f32_E40_no_aux": (Workload("bw_f32e40", T=77, d=100, F=30, E=40, k=3, dtype="f32",
-                                capacity_factor=1.0), 0.0),
+                                capacity_factor=1.0), 0.0, 0.0),
 }
 
 
 @pytest.mark.parametrize("case", sorted(BACKWARD_CASES))
 def test_router_backward(case):
-    w, alpha = BACKWARD_CASES[case]
-    say(f"[router backward] {case} aux_coef={alpha}")
+    w, alpha, beta = BACKWARD_CASES[case]
+    say(f"[router backward] {case} aux_coef={alpha} entropy_coef={beta}")
     run = Run(w)
     g_route, _ = run.route()
     ref_fwd = run.oracle()
@@ -148,12 +152,12 @@ def test_router_backward(case):
     assert float(np.min(margin)) > max(1e-6, 4 * err)
     dout = _dout(w)
     ref = O.router_backward(to64(run.hx), to64(run.hWg), ref_fwd, shape_of(run.w), to64(dout),
-                            aux_coef=alpha)
-    g = _run_backward(run, dout, alpha)
+                            aux_coef=alpha, entropy_coef=beta)
+    g = _run_backward(run, dout, alpha, beta)
     tol = 1e-5 if w.dtype == "f32" else 2e-2
     for key in ("dlogits", "dW_gate", "dbias", "dx"):
         assert np.all(np.isfinite(g[key])), key
-    B = _dl_bound(ref_fwd, to64(dout), w, alpha, tol)
+    B = _dl_bound(ref_fwd, to64(dout), w, alpha, tol, beta=beta)
     x64, W64 = to64(run.hx), to64(run.hWg)
     _check_bounded("dlogits", g["dlogits"], ref["dlogits"], B)
     _check_bounded("dW_gate", g["dW_gate"], ref["dW_gate"], np.abs(x64).T @ B)
@@ -168,12 +172,12 @@ def test_router_backward(case):
 
 
 def test_router_backward_deterministic():
-    w, alpha = BACKWARD_CASES["bf16_deepseek_shared"]
+    w, alpha, beta = BACKWARD_CASES["bf16_deepseek_shared"]
     say("[router backward] determinism")
     run = Run(w)
     dout = _dout(w, seed=3)
-    a = _run_backward(run, dout, alpha)
-    b = _run_backward(run, dout, alpha)
+    a = _run_backward(run, dout, alpha, beta)
+    b = _run_backward(run, dout, alpha, beta)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
 
@@ -181,7 +185,7 @@ def test_router_backward_deterministic():
 @pytest.mark.parametrize("name", ["mixtral_prefill", "deepseek"])
 def test_router_backward_full_size_sampled(name):
     w = PRESETS[name]
-    alpha = 0.01
+    alpha, beta = 0.01, 0.001
     say(f"[router backward full] {name}")
     run = Run(w, gen_device=DEV)
     g_route, _ = run.route()
@@ -199,9 +203,9 @@ def test_router_backward_full_size_sampled(name):
     assert len(toks) >= 20
     dout = _dout(w, seed=11)
     ref = O.router_backward(to64(run.hx), to64(run.hWg), ref_fwd, shape_of(run.w),
-                            to64(dout), aux_coef=alpha, tokens=toks)
-    g = _run_backward(run, dout, alpha)
-    B = _dl_bound(ref_fwd, to64(dout), w, alpha, 2e-2, tokens=toks)[toks]
+                            to64(dout), aux_coef=alpha, tokens=toks, entropy_coef=beta)
+    g = _run_backward(run, dout, alpha, beta)
+    B = _dl_bound(ref_fwd, to64(dout), w, alpha, 2e-2, tokens=toks, beta=beta)[toks]
     say(f"  {len(toks)} sampled tokens")
     _check_bounded("dlogits", g["dlogits"][toks], ref["dlogits"][toks], B)
     _check_bounded("dx", g["dx"][toks], ref["dx"][toks], B @ np.abs(to64(run.hWg)).T)

@@ -98,7 +98,7 @@ def test_router_backward_graph_replay():
     def step():
         moe.moe_forward(run.x, run.Wg, run.W1, run.W3, run.W2, cfg, out)
         moe.moe_router_backward(run.x, run.Wg, dout, cfg, bufs["dl"], bufs["dW"], bufs["db"],
-                                bufs["dx"], aux_coef=0.1)
+                                bufs["dx"], aux_coef=0.1, entropy_coef=0.05)
 
     with torch.cuda.stream(s):
         step()

@@ -228,11 +228,13 @@ def _bwd_variant(mode):
     'aux_sign' flips the auxiliary term, 'dx_untransposed' multiplies by
     W_gate instead of its transpose (shapes allowing), 'dw_unweighted' leaves
     out the gate weight in the chosen-softmax Jacobian."""
-    def fn(x, W_gate, fwd, shape, dout, aux_coef=0.0, tokens=None):
+    def fn(x, W_gate, fwd, shape, dout, aux_coef=0.0, tokens=None, entropy_coef=0.0):
         if tokens is not None:   # the planted mistakes live in the full computation
-            return _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef, tokens)
+            return _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef, tokens,
+                                            entropy_coef)
         T, E, k = shape.T, shape.E, shape.k
-        g = _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef)
+        g = _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef,
+                                     entropy_coef=entropy_coef)
         if mode == "dropped":
             fwd2 = dict(fwd)
             yr = dict(fwd["yrows"])
@@ -240,7 +242,8 @@ def _bwd_variant(mode):
                 if a not in yr:
                     yr[a] = np.ones(shape.d)
             fwd2["yrows"] = yr
-            return _orig["router_backward"](x, W_gate, fwd2, shape, dout, aux_coef)
+            return _orig["router_backward"](x, W_gate, fwd2, shape, dout, aux_coef,
+                                            entropy_coef=entropy_coef)
         if mode == "selected_only":
             dl = g["dlogits"].copy()
             for t in range(T):
@@ -248,8 +251,21 @@ def _bwd_variant(mode):
                 for i in range(E):
                     if i not in keep:
                         dl[t, i] = 0.0
+        elif mode in ("ent_sign", "ent_no_H", "ent_no_T"):
+            g0 = _orig["router_backward"](x, W_gate, fwd, shape, dout, aux_coef)
+            part = g["dlogits"] - g0["dlogits"]
+            if mode == "ent_sign":
+                dl = g0["dlogits"] - part
+            elif mode == "ent_no_T":
+                dl = g0["dlogits"] + part * T
+            else:   # drops the + H_t inside the bracket: -p ln p only
+                p = fwd["p"]
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    lnp = np.where(p > 0, np.log(p), 0.0)
+                dl = g0["dlogits"] + entropy_coef / T * (-p * lnp)
         elif mode in ("aux_no_E", "aux_sign"):
-            g0 = _orig["router_backward"](x, W_gate, fwd, shape, dout, 0.0)
+            g0 = _orig["router_backward"](x, W_gate, fwd, shape, dout, 0.0,
+                                          entropy_coef=entropy_coef)
             aux_part = g["dlogits"] - g0["dlogits"]
             dl = g0["dlogits"] + (aux_part / E if mode == "aux_no_E" else -aux_part)
         elif mode == "dx_untransposed":
@@ -276,6 +292,9 @@ MUTATIONS = {
     "bwd_aux_sign": ("router_backward", _bwd_variant("aux_sign")),
     "bwd_dx_untransposed": ("router_backward", _bwd_variant("dx_untransposed")),
     "bwd_jacobian_unweighted": ("router_backward", _bwd_variant("dw_unweighted")),
+    "bwd_entropy_sign": ("router_backward", _bwd_variant("ent_sign")),
+    "bwd_entropy_without_H": ("router_backward", _bwd_variant("ent_no_H")),
+    "bwd_entropy_without_1_over_T": ("router_backward", _bwd_variant("ent_no_T")),
     "reroute_ties_to_high_index": ("dispatch_policy", _reroute_variant("high")),
     "reroute_onto_own_choice": ("dispatch_policy", _reroute_variant("own")),
     "reroute_to_worst_spare": ("dispatch_policy", _reroute_variant("worst")),
