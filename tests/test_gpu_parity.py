@@ -272,6 +272,24 @@ FORWARD_CASES = {
                                    capacity_factor=0.75, overflow=1),
     "f32_reroute_shared": Workload("f32_rr", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
                                    capacity_factor=0.8, overflow=1),
+    # 256 experts, top-8: most experts get a handful of rows
+    "bf16_E256_k8": Workload("bf16_e256", T=200, d=128, F=128, E=256, k=8,
+                             capacity_factor=1.0),
+    # one token with shared experts, softmax over all (a fine-grained decode step)
+    "bf16_T1_shared_ds": Workload("bf16_t1s", T=1, d=256, F=192, E=64, k=6, S=2,
+                                  gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    # a short fine-grained batch: 8 tokens, 6 of 64 experts each
+    "bf16_T8_fine": Workload("bf16_t8f", T=8, d=256, F=128, E=64, k=6, S=1,
+                             gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    # one slot per expert: almost everything dropped
+    "bf16_one_slot": Workload("bf16_1slot", T=300, d=128, F=128, E=8, k=2,
+                              capacity_factor=0.01),
+    # capacity above T: nothing can overflow
+    "bf16_capacity_above_T": Workload("bf16_bigcap", T=100, d=128, F=128, E=4, k=2,
+                                      capacity_factor=50.0),
+    # skewed routing with a tiny capacity, overflow sent to spare experts
+    "bf16_skew_reroute_tight": Workload("bf16_skrt", T=512, d=128, F=128, E=8, k=2,
+                                        capacity_factor=0.3, bias=SKEW_BIAS, overflow=1),
 }
 
 
