@@ -11,16 +11,27 @@
 //
 // Y may be split into `ysplit` partial sums over K (weight-streaming path);
 // the partials are added in a fixed order, so results are bitwise
-// reproducible.  One workgroup per token, columns strided over threads so
+// reproducible.  With one part, Y rows may be bf16 (half the bytes).  One workgroup per token, columns strided over threads so
 // each Y row is read with coalesced 16-byte loads.
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-template <bool BF16OUT>
+// Four consecutive elements of a row as fp32: column group c of a float row,
+// or of a bf16 row.
+__device__ __forceinline__ float4 load4f(const float* row, int c) {
+  return reinterpret_cast<const float4*>(row)[c];
+}
+__device__ __forceinline__ float4 load4f(const uint16_t* row, int c) {
+  const uint2 v = reinterpret_cast<const uint2*>(row)[c];
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
+template <bool BF16OUT, typename TY>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ Y, int ysplit, int64_t ysplit_stride,
+    const TY* __restrict__ Y, int ysplit, int64_t ysplit_stride,
     const int32_t* __restrict__ slot, const float* __restrict__ topk_w,
     const float* __restrict__ Ys, int ys_split, int64_t ys_stride, int64_t T,
     int k, int d, void* __restrict__ out) {
@@ -44,9 +55,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
         for (int u = 0; u < 8; ++u) {
           v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (p0 + u < ysplit) {
-            const float* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
-            if (vec) v[u] = reinterpret_cast<const float4*>(row)[c];
-            else v[u].x = row[c];
+            const TY* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
+            if (vec) v[u] = load4f(row, c);
+            else v[u].x = load_elem(row, c);
           }
         }
 #pragma unroll
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 }  // namespace
 
-hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
+hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_stride,
                           const int32_t* slot, const float* topk_w,
                           const float* Ys, int ys_split, int64_t ys_stride,
                           int64_t T, int k, int d, void* out, bool bf16,
@@ -104,12 +115,17 @@ hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
   int chunks = (ncols + tpb - 1) / tpb;
   if (T >= 256) chunks = 1;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
-  if (bf16)
-    combine_kernel<true><<<grid, tpb, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
-                                              ys_split, ys_stride, T, k, d, out);
-  else
-    combine_kernel<false><<<grid, tpb, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys,
-                                               ys_split, ys_stride, T, k, d, out);
+#define MOE_COMBINE(O, TY)                                                                 \
+  combine_kernel<O, TY><<<grid, tpb, 0, s>>>(static_cast<const TY*>(Y), ysplit, ysplit_stride, \
+                                             slot, topk_w, Ys, ys_split, ys_stride, T, k, d, out)
+  if (bf16) {
+    if (ybf16) MOE_COMBINE(true, uint16_t);
+    else MOE_COMBINE(true, float);
+  } else {
+    if (ybf16) MOE_COMBINE(false, uint16_t);
+    else MOE_COMBINE(false, float);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

@@ -481,6 +481,34 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
         }
       }
     }
+  } else if (p.c_bf16) {
+    // One K part, rows stored rounded to bf16 (N a multiple of 8).  The tile
+    // goes through LDS, free once the K loop is done, so that each thread
+    // writes whole 16-byte pieces of rows instead of 2-byte elements.
+    static_assert(BM * BN * 2 <= S::LDS, "bf16 output tile fits the LDS");
+    wait_vmcnt_lgkm0<0>();
+    __syncthreads();
+    uint16_t* sm = reinterpret_cast<uint16_t*>(smem);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          sm[rl * BN + wn * S::WCOLS + j * 16 + (lane & 15)] = f32_to_bf16(acc[i][j][r]);
+      }
+    }
+    __syncthreads();
+    uint16_t* Y = static_cast<uint16_t*>(p.C);
+    constexpr int CH = BN / 8;   // 16-byte pieces per tile row
+    for (int idx = tid; idx < BM * CH; idx += 64 * S::NW) {
+      const int rl = idx / CH;
+      const int col = n0 + (idx % CH) * 8;
+      if (rl < tc.nrows && col < p.N)
+        *reinterpret_cast<u32x4*>(Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo + col) =
+            *reinterpret_cast<const u32x4*>(sm + rl * BN + (idx % CH) * 8);
+    }
   } else {
     float* Y = static_cast<float*>(p.C) + tc.kpart * p.c_split;
 #pragma unroll
@@ -500,7 +528,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   }
 }
 
-// Shapes in use (the host picks one per GEMM through GroupedGemm::shape):
+// Shapes in use (the M-tile the host chooses picks one):
 //   0: 32-row M-tiles for short batches; 4-stage ring, one workgroup per CU;
 //      with narrow_n, 128-wide B tiles (80 KB, two workgroups per CU): twice
 //      the tiles, so the weights of several hit experts stream from more CUs.

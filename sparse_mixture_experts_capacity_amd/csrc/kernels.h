@@ -84,6 +84,7 @@ struct GroupedGemm {
   // rows at ((k / 32) * R + row) * 32 + k % 32.  0 = row-major.
   int64_t a_block_rows;     // A (then perm and lda are not used)
   int64_t c_block_rows;     // SwiGLU output H
+  int c_bf16;               // plain bf16 kernel, ksplit 1: store C rounded to bf16
 };
 // Xb = kept token rows x[perm[s] / topk] for slots s < *nrows_dev, K-blocked
 // with R rows.
@@ -105,7 +106,8 @@ struct RouterBackward {
   const void* x;            // [T, d] layer dtype
   const void* Wg;           // [d, E] layer dtype
   const void* dout;         // [T, d] layer dtype
-  const float* Y;           // expert output rows, ysplit K parts ystride apart
+  const void* Y;            // expert output rows, ysplit K parts ystride apart
+  bool ybf16;               // Y rows are bf16 (one part)
   int ysplit;
   int64_t ystride;
   int64_t rows;             // rows of each part (slots at or past it are not read)
@@ -150,7 +152,8 @@ hipError_t launch_router_dx(const RouterBackward& b, hipStream_t s);
 
 // ---- combine.hip -------------------------------------------------------------
 // out[t] = sum_j [slot >= 0] w[t,j] * sum_p Y[p][slot] + sum_p Ys[p][t]
-hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
+// Y is fp32, or bf16 when ybf16 (then ysplit is 1).
+hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_stride,
                           const int32_t* slot, const float* topk_w,
                           const float* Ys, int ys_split, int64_t ys_stride,
                           int64_t T, int k, int d, void* out, bool bf16,

@@ -136,6 +136,7 @@ struct Plan {
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
+  bool y_bf16 = false;           // routed down projection stores bf16 rows (one K part)
   bool small_route = false;      // top-k and dispatch in one workgroup
   bool blocked = false;          // GEMM1 writes H K-blocked; GEMM2 reads it so
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
@@ -377,7 +378,10 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->stats, sizeof(double) * 8, cur);
   add(p->H, es * p->rows_max * p->F, cur);
   add(p->Hs, es * p->T * p->S * p->F, cur);
-  add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
+  // With one K part the routed down projection's rows are stored in bf16:
+  // half the bytes written by the GEMM and read by the combine.
+  p->y_bf16 = p->bf16 && p->ffn2_split == 1 && p->d % 8 == 0;
+  add(p->Y, (p->y_bf16 ? 2 : sizeof(float)) * p->ffn2_split * p->rows_max * p->d, cur);
   add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
   add(p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur);
   const size_t rr = p->overflow == MOE_OVERFLOW_REROUTE ? sizeof(int32_t) * p->TK : 0;
@@ -661,6 +665,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d; g2.narrow_n = 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
+  g2.c_bf16 = p.y_bf16 ? 1 : 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
   // the S stacked W2 blocks in one pass (their sum).
@@ -717,7 +722,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   }
   {
     Timed t("combine", s);
-    HIP_TRY(moe::launch_combine(at<float>(ws, p.Y), p.ffn2_split, p.rows_max * p.d,
+    HIP_TRY(moe::launch_combine(at<void>(ws, p.Y), p.y_bf16, p.ffn2_split, p.rows_max * p.d,
                                 at<int32_t>(ws, p.slot), w,
                                 p.S > 0 ? at<float>(ws, p.Ys) : nullptr, p.shared2_split,
                                 p.T * p.d, p.T, p.k, p.d, out, p.bf16, s));
@@ -751,7 +756,8 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   void* ws = cfg->workspace;
   moe::RouterBackward b{};
   b.x = x; b.Wg = W_gate; b.dout = dout;
-  b.Y = at<float>(ws, p.Y); b.ysplit = p.ffn2_split; b.ystride = p.rows_max * p.d;
+  b.Y = at<void>(ws, p.Y); b.ybf16 = p.y_bf16; b.ysplit = p.ffn2_split;
+  b.ystride = p.rows_max * p.d;
   b.rows = p.rows_max;
   b.vec4 = p.d % 4 == 0 && reinterpret_cast<uintptr_t>(dout) % (4 * (p.bf16 ? 2 : 4)) == 0;
   b.slot = at<int32_t>(ws, p.slot); b.idx = at<int32_t>(ws, p.idx); b.w = at<float>(ws, p.w);
