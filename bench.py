@@ -397,16 +397,19 @@ def main():
         graph["tokens_per_s"] = w.T / (graph["ms_per_step"] * 1e-3)
         res["graph"] = graph
     if bwd is not None:
-        # The gate pass streams the kept expert rows (fp32) and dout once:
-        # it is bound by HBM.
+        # The gate pass streams the kept expert rows and dout once: it is
+        # bound by HBM.  Algorithmic bytes count each row in the layer's
+        # dtype (the library keeps them in bf16, or as fp32 K parts when the
+        # down projection is split).
         es = 2 if w.dtype == "bf16" else 4
-        gbytes = kept * w.d * 4 + w.T * w.d * es + 2 * w.T * w.E * 4 + 3 * w.T * w.k * 4
+        gbytes = kept * w.d * es + w.T * w.d * es + 2 * w.T * w.E * 4 + 3 * w.T * w.k * 4
         gms = bwd["kernels"].get("gate_backward", {}).get("avg_ms", float("nan"))
         gach = gbytes / (gms * 1e-3) / 1e9
         bwd["roofline"] = dict(kernel="gate_backward", bound="hbm", achieved=gach,
                                peak=PEAK_HBM_GBS, unit="GB/s", frac=gach / PEAK_HBM_GBS,
-                               per_launch=(f"{gbytes} bytes ({kept} fp32 expert rows, dout, "
-                                           f"scores and score gradients)"))
+                               per_launch=(f"{gbytes} bytes ({kept} expert rows and the "
+                                           f"dout rows in the layer dtype, scores and score "
+                                           f"gradients)"))
         res["router_backward"] = bwd
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, inp, args.cpu_sample_tokens)

@@ -329,17 +329,19 @@ __global__ __launch_bounds__(256) void transpose_gate_kernel(
 
 // dW_gate[c, e] = sum of the GEMM's K parts of dW^T[e, c] in part order, plus
 // the vector kernel's sum over the tokens past the last whole 64 (tail[c, e]).
+// Threads run over (e, c) with c fastest, so the parts are read coalesced.
 __global__ __launch_bounds__(256) void router_wgrad_finish_kernel(
     const float* __restrict__ partT, int nparts, const float* __restrict__ tail, int d, int E,
     float* __restrict__ dW) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t n = static_cast<int64_t>(d) * E;
   if (i >= n) return;
-  const int c = static_cast<int>(i / E), e = static_cast<int>(i - static_cast<int64_t>(c) * E);
+  const int e = static_cast<int>(i / d), c = static_cast<int>(i - static_cast<int64_t>(e) * d);
   float s = 0.f;
-  for (int q = 0; q < nparts; ++q) s += partT[(static_cast<int64_t>(q) * E + e) * d + c];
-  if (tail) s += tail[i];
-  dW[i] = s;
+  for (int q = 0; q < nparts; ++q) s += partT[static_cast<int64_t>(q) * n + i];
+  const int64_t o = static_cast<int64_t>(c) * E + e;
+  if (tail) s += tail[o];
+  dW[o] = s;
 }
 
 // dbias[e] = sum over t of dl[t, e]: one workgroup per expert, a strided

@@ -853,33 +853,55 @@ __global__ __launch_bounds__(256) void stats_kernel(
     const float* __restrict__ Ppart, const float* __restrict__ Hpart, int nblk,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kcount,
     int64_t T, int k, int E, double* __restrict__ out) {
-  __shared__ double P[kMaxExperts];
-  const int e = threadIdx.x;
-  if (e < E) {
-    double s = 0.0;
-    for (int b = 0; b < nblk; ++b) s += static_cast<double>(Ppart[static_cast<int64_t>(b) * E + e]);
-    P[e] = s / static_cast<double>(T);
-  }
-  __syncthreads();
-  if (e == 0) {
-    const double n = static_cast<double>(T) * k;
-    double aux = 0.0, auxk = 0.0, hl = 0.0, ht = 0.0;
-    int64_t dropped = 0;
-    for (int i = 0; i < E; ++i) {
-      const double f = counts ? counts[i] / n : 0.0;
-      const double fk = kcount ? kcount[i] / n : 0.0;
-      aux += f * P[i];
-      auxk += fk * P[i];
-      if (f > 0.0) hl -= f * log(f);
-      if (counts && kcount) dropped += counts[i] - kcount[i];
+  __shared__ double red[5][256];
+  const int tid = threadIdx.x;
+  const double n = static_cast<double>(T) * k;
+  // Thread e: P_e from the partial rows, 8 interleaved running sums (their
+  // loads in flight together) added in a fixed order; then its expert's
+  // terms of aux, aux over kept counts, the load entropy and the drops.
+  double terms[4] = {0.0, 0.0, 0.0, 0.0};
+  if (tid < E) {
+    double s8[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        s8[u] += static_cast<double>(Ppart[static_cast<int64_t>(b + u) * E + tid]);
     }
-    for (int b = 0; b < nblk; ++b) ht += static_cast<double>(Hpart[b]);
-    out[0] = E * aux;
-    out[1] = E * auxk;
-    out[2] = static_cast<double>(dropped) / n;
-    out[3] = hl;
-    out[4] = ht / static_cast<double>(T);
-    out[5] = static_cast<double>(dropped);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (b + u < nblk) s8[u] += static_cast<double>(Ppart[static_cast<int64_t>(b + u) * E + tid]);
+    double sum = 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += s8[u];
+    const double P = sum / static_cast<double>(T);
+    const double f = counts ? counts[tid] / n : 0.0;
+    const double fk = kcount ? kcount[tid] / n : 0.0;
+    terms[0] = f * P;
+    terms[1] = fk * P;
+    terms[2] = f > 0.0 ? -f * log(f) : 0.0;
+    terms[3] = (counts && kcount) ? static_cast<double>(counts[tid] - kcount[tid]) : 0.0;
+  }
+  // the per-token entropy partials, strided over the workgroup
+  double h = 0.0;
+  for (int b = tid; b < nblk; b += blockDim.x) h += static_cast<double>(Hpart[b]);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[q][tid] = terms[q];
+  red[4][tid] = h;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {   // fixed tree
+    if (tid < w)
+#pragma unroll
+      for (int q = 0; q < 5; ++q) red[q][tid] += red[q][tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    out[0] = E * red[0][0];
+    out[1] = E * red[1][0];
+    out[2] = red[3][0] / n;
+    out[3] = red[2][0];
+    out[4] = red[4][0] / static_cast<double>(T);
+    out[5] = red[3][0];
   }
 }
 
