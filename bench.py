@@ -33,9 +33,9 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM; the counter summaries are kept beside the profiles
-    "mixtral_prefill": ("867e93a264693add", 4525.59e6, 121.09e6),
-    "deepseek": ("867e93a264693add", 5370.47e6, 75.88e6),
-    "mixtral_decode_t64": ("867e93a264693add", 1892.93e6, 3.67e6),
+    "mixtral_prefill": ("6aeb8185bda30ce3", 4561.87e6, 121.22e6),
+    "deepseek": ("6aeb8185bda30ce3", 5371.32e6, 75.89e6),
+    "mixtral_decode_t64": ("6aeb8185bda30ce3", 1892.84e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.
