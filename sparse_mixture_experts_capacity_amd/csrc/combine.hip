@@ -11,8 +11,11 @@
 //
 // Y may be split into `ysplit` partial sums over K (weight-streaming path);
 // the partials are added in a fixed order, so results are bitwise
-// reproducible.  With one part, Y rows may be bf16 (half the bytes).  One workgroup per token, columns strided over threads so
-// each Y row is read with coalesced 16-byte loads.
+// reproducible.  With one part, Y rows may be bf16 (half the bytes).  One
+// workgroup per token, columns strided over threads so each Y row is read
+// with coalesced 16-byte loads.  For bf16 rows the loads of all k rows of a
+// column group are issued before the first is used (the kernel is bound by
+// memory latency, not by arithmetic), and the sum is taken in j order.
 #include "kernels.h"
 
 namespace moe {
@@ -100,6 +103,68 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+// bf16 Y rows, one K part, bf16 output, d % 8 == 0: each thread takes 8
+// columns (one 16-byte load per row).  Up to 8 rows' loads are in flight at
+// once; the weighted sum runs in j order as in combine_kernel, so the two
+// give the same bits.
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+}
+
+__global__ __launch_bounds__(512) void combine_bf16_rows_kernel(
+    const uint16_t* __restrict__ Y, const int32_t* __restrict__ slot,
+    const float* __restrict__ topk_w, const float* __restrict__ Ys, int ys_split,
+    int64_t ys_stride, int64_t T, int k, int d, uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  const int ncols = d / 8;
+  const int32_t* st = slot + t * k;
+  const float* wt = topk_w + t * k;
+  for (int c = blockIdx.y * blockDim.x + threadIdx.x; c < ncols; c += gridDim.y * blockDim.x) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (j0 + u < k) {
+          const int s = st[j0 + u];
+          if (s >= 0) v[u] = reinterpret_cast<const uint4*>(Y + static_cast<int64_t>(s) * d)[c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < k && st[j0 + u] >= 0) {
+          const float w = wt[j0 + u];
+          float y[8];
+          unpack8(v[u], y);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, y[e], acc[e]);
+        }
+      }
+    }
+    if (Ys) {
+      for (int p = 0; p < ys_split; ++p) {
+        const float4* row = reinterpret_cast<const float4*>(Ys + p * ys_stride + t * d);
+        const float4 a = row[2 * c], b = row[2 * c + 1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+    reinterpret_cast<uint4*>(out + t * d)[c] = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_stride,
@@ -108,6 +173,27 @@ hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_
                           int64_t T, int k, int d, void* out, bool bf16,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (ybf16 && bf16 && ysplit == 1 && (d & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    // 8 columns per thread; at most 512 threads per token, as few passes as
+    // possible with the threads evenly loaded.  Short batches: 64-thread
+    // workgroups over 64 column groups each.
+    const int n8 = d / 8;
+    int tpb, chunks;
+    if (T < 64) {
+      tpb = 64;
+      chunks = (n8 + 63) / 64;
+    } else {
+      const int passes = (n8 + 511) / 512;
+      tpb = ((n8 + passes - 1) / passes + 63) / 64 * 64;
+      chunks = 1;
+    }
+    const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
+    combine_bf16_rows_kernel<<<grid, tpb, 0, s>>>(static_cast<const uint16_t*>(Y), slot, topk_w,
+                                                  Ys, ys_split, ys_stride, T, k, d,
+                                                  static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
   // enough workgroups to cover the GPU even for a handful of tokens: short
   // batches take 64-thread workgroups, each over 64 column groups
   const int ncols = (d & 3) == 0 ? d / 4 : d;

@@ -218,6 +218,26 @@ __device__ __forceinline__ int bcol_of(int j, int wn) {
   return wn * S::WCOLS + j * 16;
 }
 
+// First tile row of MFMA row fragment i (16 rows) of wavefront row wm.  The
+// fragments are dealt to the WM wavefront rows in turn, so the rows of a
+// short tile (an expert's last) spread evenly over the wavefronts, and with
+// them over the SIMDs, when the fragments past the tile's end are skipped.
+template <class S>
+__device__ __forceinline__ int frag_row(int wm, int i) {
+  return (i * S::WM + wm) * 16;
+}
+
+// f(integral_constant<int, n>) for a run-time n in 0..N.
+template <int N, class F>
+__device__ __forceinline__ void with_count(int n, F& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N) f(std::integral_constant<int, N>{});
+    else with_count<N - 1>(n, f);
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
@@ -343,7 +363,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   };
   auto rd_a = [&](int stage, int h, int i) __attribute__((always_inline)) -> bf16x8 {
     const char* sb = smem + stage * S::STAGE;
-    const int m = wm * S::WROWS + i * 16 + i16;
+    const int m = frag_row<S>(wm, i) + i16;
     return *reinterpret_cast<const bf16x8*>(sb + m * S::A_ROW + a_chunk<S::CA>(m, h * 4 + g) * 16);
   };
   auto rd_b = [&](int stage, int h, int j) __attribute__((always_inline)) -> bf16x8 {
@@ -357,9 +377,13 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto load_frags = [&](Frags& f, int stage, int h) __attribute__((always_inline)) {
+  // MV: row fragments of this wavefront that hold tile rows (a constant of
+  // the specialised pipeline below); the others are neither read nor
+  // multiplied.
+  auto load_frags = [&](Frags& f, int stage, int h, auto mv_c) __attribute__((always_inline)) {
+    constexpr int MV = decltype(mv_c)::value;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) f.a[i] = rd_a(stage, h, i);
+    for (int i = 0; i < MV; ++i) f.a[i] = rd_a(stage, h, i);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) f.b[j] = rd_b(stage, h, j);
   };
@@ -368,19 +392,21 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   // into the same registers as they fall free: each B fragment after its
   // column, the A fragments during the last column.  So the next half's
   // reads overlap this half's MFMAs and no extra registers are held.
-  auto mfma_reload = [&](Frags& f, int nstage, int nh, bool more) __attribute__((always_inline)) {
+  auto mfma_reload = [&](Frags& f, int nstage, int nh, bool more, auto mv_c)
+                         __attribute__((always_inline)) {
+    constexpr int MV = decltype(mv_c)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       if (j < NJ - 1) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MV; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (more) f.b[j] = rd_b(nstage, nh, j);
         __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < MV; ++i) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (more) f.a[i] = rd_a(nstage, nh, i);
@@ -399,61 +425,66 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
   // transfers of step ks+1 have landed and its reads of step ks are done, a
   // barrier makes step ks+1 readable by all (its fragments are read during
   // that half) and frees step ks's slot, which is refilled with step ks+NS.
-  // A wavefront whose rows all lie past the tile's end (the last, short
-  // M-tile of an expert) keeps loading and meeting the barriers but skips
-  // its fragment reads and MFMAs.
-  const bool wactive =
-      (S::WM == 1) || (__builtin_amdgcn_readfirstlane(wm) * S::WROWS < tc.nrows);
+  // The pipeline is specialised on MV, the number of this wavefront's row
+  // fragments that hold tile rows: on an expert's last, short M-tile the
+  // fragments past the end are neither read nor multiplied, and a wavefront
+  // with none keeps loading and meeting the barriers only.
   const int nk = kb1 - kb0;
+  const int nfr = min((tc.nrows + 15) >> 4, BM / 16);   // >= 1
+  const int mv = min(MI, (nfr - __builtin_amdgcn_readfirstlane(wm) + S::WM - 1) / S::WM);
+  auto run = [&](auto mv_c) __attribute__((always_inline)) {
+    constexpr int MV = decltype(mv_c)::value;
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-    if (st < nk) issue(st, st);
-  Frags f;
-  if (nk > 0) {
-    wait_stages_lgkm0<S::LOADS>(min(NS - 1, nk - 1));
-    // A bare barrier: __syncthreads() adds a release fence that would wait
-    // for every transfer in flight, the later stages' included.
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    if (wactive) load_frags(f, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // One K step held in ring slot `stage` (a constant in the unrolled loop
-  // below, so every LDS address of the step is a fixed offset).  HAS_NEXT:
-  // a step ks+1 follows (every step but the last), so its stage is waited
-  // for, the slot of step ks is refilled, and its fragments are read ahead.
-  auto step_body = [&](int ks, int stage, auto has_next_c) __attribute__((always_inline)) {
-    constexpr bool HAS_NEXT = decltype(has_next_c)::value;
-    const int next_slot = stage == NS - 1 ? 0 : stage + 1;
-#pragma unroll
-    for (int h = 0; h < S::HALVES; ++h) {
-      if (HAS_NEXT && h == S::HALVES - 1) {
-        wait_stages_lgkm0<S::LOADS>(min(NS - 2, nk - ks - 2));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (ks + NS < nk) issue(ks + NS, stage);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (wactive) {
-        if (h + 1 < S::HALVES) mfma_reload(f, stage, h + 1, true);
-        else mfma_reload(f, next_slot, 0, HAS_NEXT);
-      }
+    for (int st = 0; st < NS; ++st)
+      if (st < nk) issue(st, st);
+    Frags f;
+    if (nk > 0) {
+      wait_stages_lgkm0<S::LOADS>(min(NS - 1, nk - 1));
+      // A bare barrier: __syncthreads() adds a release fence that would wait
+      // for every transfer in flight, the later stages' included.
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MV > 0) load_frags(f, 0, 0, mv_c);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // One K step held in ring slot `stage` (a constant in the unrolled loop
+    // below, so every LDS address of the step is a fixed offset).  HAS_NEXT:
+    // a step ks+1 follows (every step but the last), so its stage is waited
+    // for, the slot of step ks is refilled, and its fragments are read ahead.
+    auto step_body = [&](int ks, int stage, auto has_next_c) __attribute__((always_inline)) {
+      constexpr bool HAS_NEXT = decltype(has_next_c)::value;
+      const int next_slot = stage == NS - 1 ? 0 : stage + 1;
+#pragma unroll
+      for (int h = 0; h < S::HALVES; ++h) {
+        if (HAS_NEXT && h == S::HALVES - 1) {
+          wait_stages_lgkm0<S::LOADS>(min(NS - 2, nk - ks - 2));
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (ks + NS < nk) issue(ks + NS, stage);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (MV > 0) {
+          if (h + 1 < S::HALVES) mfma_reload(f, stage, h + 1, true, mv_c);
+          else mfma_reload(f, next_slot, 0, HAS_NEXT, mv_c);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    int ks = 0;
+    // steps 0 .. nk-2 (each followed by another), NS at a time, then the last
+    for (; ks + NS <= nk - 1; ks += NS) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) step_body(ks + u, u, yes{});
+    }
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+      if (ks + u < nk - 1) step_body(ks + u, u, yes{});
+    if (nk > 0) step_body(nk - 1, (nk - 1) % NS, no{});
   };
-  using yes = std::integral_constant<bool, true>;
-  using no = std::integral_constant<bool, false>;
-  int ks = 0;
-  // steps 0 .. nk-2 (each followed by another), NS at a time, then the last
-  for (; ks + NS <= nk - 1; ks += NS) {
-#pragma unroll
-    for (int u = 0; u < NS; ++u) step_body(ks + u, u, yes{});
-  }
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
-    if (ks + u < nk - 1) step_body(ks + u, u, yes{});
-  if (nk > 0) step_body(nk - 1, (nk - 1) % NS, no{});
+  with_count<MI>(mv, run);
 
   // ---- epilogue -----------------------------------------------------------
   // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
@@ -464,7 +495,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
+        const int rl = frag_row<S>(wm, i) + (lane >> 4) * 4 + r;
         if (rl >= tc.nrows) continue;
         const int64_t row = tc.row0 + rl;
 #pragma unroll
@@ -493,7 +524,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
+        const int rl = frag_row<S>(wm, i) + (lane >> 4) * 4 + r;
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           sm[rl * BN + wn * S::WCOLS + j * 16 + (lane & 15)] = f32_to_bf16(acc[i][j][r]);
@@ -515,7 +546,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rl = wm * S::WROWS + i * 16 + (lane >> 4) * 4 + r;
+        const int rl = frag_row<S>(wm, i) + (lane >> 4) * 4 + r;
         if (rl >= tc.nrows) continue;
         float* yrow = Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
 #pragma unroll
@@ -538,7 +569,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma
 //      one workgroup per CU.  For a few hundred rows per expert (fine-grained
 //      experts, where the weights' HBM traffic is the bound): one M-tile per
 //      expert reads each weight tile once, and on an expert's short tile the
-//      64-row wavefront rows with no rows skip their MFMAs.
+//      16-row fragments past its end are skipped.
 using ShapeShort = Shape<32, 256, 64, 4, 1, 4>;
 using ShapeShortN = Shape<32, 128, 64, 4, 1, 4>;
 using ShapeLongA = Shape<128, 256, 32, 8, 2, 3>;
