@@ -256,7 +256,9 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 }
 
 template <bool SWIGLU, class S>
-__global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU) void grouped_bf16_dma_kernel(
+// The second launch bound is the minimum wavefronts per SIMD: BLOCKS_PER_CU
+// workgroups of NW wavefronts over 4 SIMDs, which caps the registers.
+__global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grouped_bf16_dma_kernel(
     GroupedGemm p, int ntn, int nblocks) {
   constexpr int BM = S::BM, BN = S::BN, BK = S::BK, NS = S::NS, MI = S::MI, NJ = S::NJ;
   __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
