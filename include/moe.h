@@ -256,6 +256,11 @@ const char* moe_last_error(void);
  * names (each at most 63 chars) in a caller buffer of max*64 bytes.
  * Returns the number of distinct kernels (may exceed max). */
 int moe_timing_enable(int enable);
+/* Restricts timing to the named kernels: a comma-separated list of the names
+ * moe_timing_read reports (e.g. "ffn1_swiglu"); NULL or "" times every
+ * kernel again.  Each timed kernel adds two event records to the stream, so
+ * timing one kernel perturbs the step less than timing all of them. */
+int moe_timing_only(const char* names);
 int moe_timing_reset(void);
 int moe_timing_read(char* names, int64_t* launches, double* total_ms,
                     int max);

@@ -24,7 +24,7 @@ __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
     "moe_workspace_size", "moe_capacity", "moe_forward", "moe_route",
     "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
-    "moe_timing_enable",
+    "moe_timing_enable", "moe_timing_only",
     "moe_timing_reset", "moe_timing_read", "Workspace",
 ]
 
@@ -196,6 +196,17 @@ def moe_aux_loss(logits, counts, cfg: MoeConfig) -> float:
 
 def moe_timing_enable(enable: bool = True) -> None:
     LIB.moe_timing_enable(1 if enable else 0)
+
+
+def moe_timing_only(names=None) -> None:
+    """Time only the named kernels (a name or an iterable of names, as
+    moe_timing_read reports them); None times every kernel."""
+    if names is None:
+        LIB.moe_timing_only(None)
+    else:
+        if isinstance(names, str):
+            names = [names]
+        LIB.moe_timing_only(",".join(names).encode())
 
 
 def moe_timing_reset() -> None:

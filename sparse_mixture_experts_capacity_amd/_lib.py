@@ -87,6 +87,7 @@ def _load():
                                                P, P, P, P]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "moe_timing_only": (ctypes.c_int, [ctypes.c_char_p]),
         "moe_timing_reset": (ctypes.c_int, []),
         "moe_timing_read": (ctypes.c_int, [ctypes.c_char_p,
                                            ctypes.POINTER(ctypes.c_int64),

@@ -12,6 +12,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -41,6 +42,7 @@ struct TimedLaunch {
 struct TimingState {
   std::mutex mu;
   bool enabled = false;
+  std::vector<std::string> only;   // groups to time; empty: all
   std::vector<TimedLaunch> pending;
   std::vector<hipEvent_t> free_events;
   std::vector<std::string> names;
@@ -70,6 +72,9 @@ class Timed {
     TimingState& t = timing();
     std::lock_guard<std::mutex> lk(t.mu);
     if (!t.enabled) return;
+    if (!t.only.empty() &&
+        std::find(t.only.begin(), t.only.end(), std::string(name)) == t.only.end())
+      return;
     start_ = take_event(t);
     stop_ = take_event(t);
     if (start_ && stop_) hipEventRecord(start_, s_);
@@ -914,6 +919,24 @@ int moe_timing_enable(int enable) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);
   t.enabled = enable != 0;
+  return MOE_OK;
+}
+
+int moe_timing_only(const char* names) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.only.clear();
+  if (!names) return MOE_OK;
+  std::string cur;
+  for (const char* c = names;; ++c) {
+    if (*c == ',' || *c == '\0') {
+      if (!cur.empty()) t.only.push_back(cur);
+      cur.clear();
+      if (*c == '\0') break;
+    } else {
+      cur.push_back(*c);
+    }
+  }
   return MOE_OK;
 }
 
