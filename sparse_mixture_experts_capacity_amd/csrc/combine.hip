@@ -32,7 +32,8 @@ __device__ __forceinline__ float4 load4f(const uint16_t* row, int c) {
                      __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
 }
 
-template <bool BF16OUT, typename TY>
+// NB: K parts loaded together (in flight at once), then added in part order.
+template <bool BF16OUT, typename TY, int NB>
 __global__ __launch_bounds__(256) void combine_kernel(
     const TY* __restrict__ Y, int ysplit, int64_t ysplit_stride,
     const int32_t* __restrict__ slot, const float* __restrict__ topk_w,
@@ -50,12 +51,12 @@ __global__ __launch_bounds__(256) void combine_kernel(
       if (s < 0) continue;
       const float w = topk_w[t * k + j];
       float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-      // the parts are loaded 8 at a time (their loads in flight together)
+      // the parts are loaded NB at a time (their loads in flight together)
       // and added in part order
-      for (int p0 = 0; p0 < ysplit; p0 += 8) {
-        float4 v[8];
+      for (int p0 = 0; p0 < ysplit; p0 += NB) {
+        float4 v[NB];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < NB; ++u) {
           v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (p0 + u < ysplit) {
             const TY* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
@@ -64,7 +65,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
           }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < NB; ++u) {
           if (p0 + u < ysplit) {
             y.x += v[u].x; y.y += v[u].y; y.z += v[u].z; y.w += v[u].w;
           }
@@ -201,17 +202,24 @@ hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_
   int chunks = (ncols + tpb - 1) / tpb;
   if (T >= 256) chunks = 1;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
-#define MOE_COMBINE(O, TY)                                                                 \
-  combine_kernel<O, TY><<<grid, tpb, 0, s>>>(static_cast<const TY*>(Y), ysplit, ysplit_stride, \
-                                             slot, topk_w, Ys, ys_split, ys_stride, T, k, d, out)
+  // parts loaded together: as many as there are, up to 16 (registers)
+#define MOE_COMBINE_NB(O, TY, NB)                                                      \
+  combine_kernel<O, TY, NB><<<grid, tpb, 0, s>>>(static_cast<const TY*>(Y), ysplit,    \
+                                                 ysplit_stride, slot, topk_w, Ys,      \
+                                                 ys_split, ys_stride, T, k, d, out)
+#define MOE_COMBINE(O, TY)                  \
+  if (ysplit <= 2) MOE_COMBINE_NB(O, TY, 2); \
+  else if (ysplit <= 8) MOE_COMBINE_NB(O, TY, 8); \
+  else MOE_COMBINE_NB(O, TY, 16)
   if (bf16) {
-    if (ybf16) MOE_COMBINE(true, uint16_t);
-    else MOE_COMBINE(true, float);
+    if (ybf16) { MOE_COMBINE(true, uint16_t); }
+    else { MOE_COMBINE(true, float); }
   } else {
-    if (ybf16) MOE_COMBINE(false, uint16_t);
-    else MOE_COMBINE(false, float);
+    if (ybf16) { MOE_COMBINE(false, uint16_t); }
+    else { MOE_COMBINE(false, float); }
   }
 #undef MOE_COMBINE
+#undef MOE_COMBINE_NB
   return hipGetLastError();
 }
 

@@ -325,13 +325,16 @@ int make_plan(const moe_config_t* c, Plan* p) {
   p->blocked = p->bf16 && p->bm != moe::kGroupedBMShort;
   p->gather_x = p->blocked && p->bm == moe::kGroupedBM;
   // Router scores x W_gate on the MFMA GEMM when the weight rows are 16-byte
-  // aligned; K is split so that even short batches give ~512 workgroups, and
-  // the top-k pass adds the parts in a fixed order.
+  // aligned; K is split so that short batches give more workgroups, and the
+  // top-k pass adds the parts in a fixed order.  At most 16 parts: the top-k
+  // pass reads every part of a score before it can rank, 8 loads in flight
+  // at a time, so each 8 parts cost it a memory round trip.
   p->mfma_router = p->bf16 && (p->E % 8 == 0);
   if (p->mfma_router) {
     const int kk = p->d / 64;
     const int64_t mt = (p->T + p->static_bm - 1) / p->static_bm;
     int64_t ks = mt > 0 ? (512 + mt - 1) / mt : 1;
+    if (ks > 16) ks = 16;
     if (ks > kk) ks = kk;
     if (ks < 1) ks = 1;
     while (kk % ks) --ks;

@@ -200,6 +200,13 @@ ROUTE_CASES = {
                           gating=SOFTMAX_THEN_TOPK, renormalize=False),
     "f32_E40_ragged_d": Workload("f32_E40", T=77, d=100, F=30, E=40, k=3, dtype="f32",
                                  capacity_factor=1.0),
+    # short batches (one routing workgroup), router K split into up to 16
+    # parts, with and without a score bias
+    "bf16_fused_T1": Workload("bf16_f1", T=1, d=1024, F=64, E=8, k=2),
+    "bf16_fused_T3_E16": Workload("bf16_f3", T=3, d=384, F=64, E=16, k=4,
+                                  gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    "bf16_fused_T128_bias": Workload("bf16_f128", T=128, d=512, F=64, E=8, k=2,
+                                     capacity_factor=1.0, bias=SKEW_BIAS),
 }
 
 
