@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--weights", default="packed", choices=["packed", "row_major"],
+                    help="expert weight layout: packed once before timing (moe_pack_weights, "
+                         "not timed) or the row-major tensors as generated")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="after the timed steps, this many more with L2 and the 256 MB "
                          "Infinity Cache flushed before each (reported separately)")
@@ -187,18 +190,28 @@ def main():
     path = {"auto": moe.PATH_AUTO, "grouped": moe.PATH_GROUPED, "stream": moe.PATH_STREAM}[args.path]
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
+        packed = args.weights == "packed" and w.dtype == "bf16"
         cfg = moe.make_config(T=w.T, d_model=w.d, d_ff=w.F, n_experts=w.E, top_k=w.k,
                               n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
                               capacity_factor=w.capacity_factor, dtype=w.dtype,
                               ffn_path=path, logit_bias=inp.bias, stream=stream,
-                              overflow=w.overflow)
+                              overflow=w.overflow,
+                              weight_layout=moe.WEIGHTS_PACKED if packed else moe.WEIGHTS_ROW_MAJOR)
         ws = moe.Workspace(moe.moe_workspace_size(cfg))
         ws.bind(cfg)
         out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=dev)
+        W1, W3, W2 = inp.W1, inp.W3, inp.W2
+        if packed:
+            # once, as a server would at load time; not part of any timing
+            w13, w2b = moe.moe_packed_weight_bytes(cfg)
+            W1 = torch.empty(w13 // 2, dtype=torch.bfloat16, device=dev)
+            W3 = torch.empty(w13 // 2, dtype=torch.bfloat16, device=dev)
+            W2 = torch.empty(w2b // 2, dtype=torch.bfloat16, device=dev)
+            moe.moe_pack_weights(inp.W1, inp.W3, inp.W2, cfg, W1, W3, W2)
+            stream.synchronize()
 
         def step(stats=False):
-            return moe.moe_forward(inp.x, inp.W_gate, inp.W1, inp.W3, inp.W2, cfg, out,
-                                   stats=stats)
+            return moe.moe_forward(inp.x, inp.W_gate, W1, W3, W2, cfg, out, stats=stats)
 
         if args.copy_calibration_mib:
             n = args.copy_calibration_mib * (1 << 20) // 4
@@ -391,6 +404,7 @@ def main():
                    "n_experts": w.E, "top_k": w.k, "n_shared": w.S,
                    "capacity_factor": w.capacity_factor, "overflow": args.overflow,
                    "gating": "softmax_then_topk" if w.gating else "topk_then_softmax",
+                   "weights": "packed" if packed else "row_major",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer": {"active_tflops": layer_tflops,

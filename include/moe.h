@@ -116,6 +116,25 @@ typedef enum {
   MOE_OVERFLOW_SEQUENTIAL = 2
 } moe_overflow_t;
 
+/* How W1, W3 and W2 are stored (cfg->weight_layout).  The expert weights are
+ * the feed-forward matrices of [Mixtral explainer] "Plain explanation" para
+ * 2; the layout changes where each element sits, not what is computed, so a
+ * layer gives the same bits with either layout.
+ *   ROW_MAJOR  W1, W3 [E+S, d, F] and W2 [E+S, F, d] as described above.
+ *   PACKED     the copies moe_pack_weights writes (bf16 layers only): each
+ *              expert's matrix cut into blocks of 32 rows x Wb columns (Wb =
+ *              128 for W1 and W3, 256 for W2), each block stored as one
+ *              contiguous run, so one K step of one output tile of the
+ *              expert GEMMs reads whole runs instead of a short piece of
+ *              each of 32 rows.  For a [K, N] matrix of expert e, with N'
+ *              = N rounded up to Wb, element (k, n) sits at
+ *                e*K*N' + ((k/32)*(N'/Wb) + n/Wb)*32*Wb + (k%32)*Wb + n%Wb
+ *              and the N' - N pad columns hold zeros. */
+typedef enum {
+  MOE_WEIGHTS_ROW_MAJOR = 0,
+  MOE_WEIGHTS_PACKED = 1
+} moe_weight_layout_t;
+
 typedef struct {
   int64_t T;             /* tokens in this call, >= 0 */
   int32_t d_model;       /* d */
@@ -133,6 +152,7 @@ typedef struct {
   size_t workspace_bytes;
   void* stream;          /* hipStream_t */
   int32_t overflow;      /* moe_overflow_t (0 = drop) */
+  int32_t weight_layout; /* moe_weight_layout_t (0 = row-major) */
 } moe_config_t;
 
 typedef struct {
@@ -164,13 +184,29 @@ int moe_check_config(const moe_config_t* cfg);
  * cfg (workspace fields ignored).  0 when cfg is invalid. */
 size_t moe_workspace_size(const moe_config_t* cfg);
 
+/* Bytes of one packed copy of W1 (the same for W3) and of W2 for cfg's
+ * shapes (E+S experts, moe_weight_layout_t PACKED): *w13_bytes =
+ * 2*(E+S)*d*F', *w2_bytes = 2*(E+S)*F*d', F' and d' rounded up to 128 and
+ * 256.  Host only.  MOE_EUNSUPPORTED for fp32 layers. */
+int moe_packed_weight_bytes(const moe_config_t* cfg, size_t* w13_bytes, size_t* w2_bytes);
+
+/* Writes the packed copies (moe_weight_layout_t PACKED) of the row-major
+ * bf16 expert weights W1, W3, W2 into W1p, W3p (w13_bytes each) and W2p
+ * (w2_bytes), all caller-owned device memory that must not overlap the
+ * sources.  Enqueued on cfg->stream; cfg->weight_layout is not read.  Pack
+ * once, then pass W1p, W3p, W2p to moe_forward with weight_layout PACKED.
+ * MOE_EUNSUPPORTED for fp32 layers, MOE_EINVAL for a NULL pointer. */
+int moe_pack_weights(const void* W1, const void* W3, const void* W2, const moe_config_t* cfg,
+                     void* W1p, void* W3p, void* W2p);
+
 /* Capacity C for cfg: ceil(T*k*cf/E) with cf read as the shortest decimal
  * that round-trips the double (1.1 means 11/10), or T without a limit.
  * [Routing guide] "Plain explanation" para 5.  -1 when cfg is invalid. */
 int64_t moe_capacity(const moe_config_t* cfg);
 
 /* Full layer forward, steps 1-5 (and 6 when stats != NULL).
- *   x [T, d], W_gate [d, E], W1/W3 [E+S, d, F], W2 [E+S, F, d]: inputs,
+ *   x [T, d], W_gate [d, E], W1/W3 [E+S, d, F], W2 [E+S, F, d]: inputs
+ *   (W1, W3, W2 in cfg->weight_layout: row-major or packed),
  *   out [T, d]: output, fully overwritten.  stats: host struct or NULL. */
 int moe_forward(const void* x, const void* W_gate, const void* W1,
                 const void* W3, const void* W2, const moe_config_t* cfg,

@@ -18,12 +18,14 @@ from ._lib import (LIB, MoeConfig, MoeStats, MoeError, MOE_OK, MOE_EINVAL,  # no
                    MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, DTYPE_F32,
                    DTYPE_BF16, TOPK_THEN_SOFTMAX, SOFTMAX_THEN_TOPK, PATH_AUTO,
                    PATH_GROUPED, PATH_STREAM, OVERFLOW_DROP, OVERFLOW_REROUTE,
-                   OVERFLOW_SEQUENTIAL, EXPORTED_SYMBOLS)
+                   OVERFLOW_SEQUENTIAL, WEIGHTS_ROW_MAJOR, WEIGHTS_PACKED,
+                   EXPORTED_SYMBOLS)
 
 __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
     "moe_workspace_size", "moe_capacity", "moe_forward", "moe_route",
     "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
+    "moe_packed_weight_bytes", "moe_pack_weights",
     "moe_timing_enable", "moe_timing_only",
     "moe_timing_reset", "moe_timing_read", "Workspace",
 ]
@@ -52,7 +54,8 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
                 renormalize: bool = True, capacity_factor: float = 0.0,
                 dtype: str = "bf16", ffn_path: int = PATH_AUTO,
                 logit_bias=None, workspace=None, workspace_bytes: int = 0,
-                stream=0, overflow: int = OVERFLOW_DROP) -> MoeConfig:
+                stream=0, overflow: int = OVERFLOW_DROP,
+                weight_layout: int = WEIGHTS_ROW_MAJOR) -> MoeConfig:
     """Fill a moe_config_t.  ``stream`` = None means torch's current stream."""
     c = MoeConfig()
     c.T = int(T)
@@ -71,6 +74,7 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
     c.workspace_bytes = int(workspace_bytes)
     c.stream = _stream_handle(stream) if stream != 0 else None
     c.overflow = int(overflow)
+    c.weight_layout = int(weight_layout)
     return c
 
 
@@ -192,6 +196,21 @@ def moe_aux_loss(logits, counts, cfg: MoeConfig) -> float:
                           ctypes.byref(v))
     _check(rc, "moe_aux_loss")
     return v.value
+
+
+def moe_packed_weight_bytes(cfg: MoeConfig):
+    """(bytes of packed W1 = of packed W3, bytes of packed W2)."""
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(LIB.moe_packed_weight_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)),
+           "moe_packed_weight_bytes")
+    return a.value, b.value
+
+
+def moe_pack_weights(W1, W3, W2, cfg: MoeConfig, W1p, W3p, W2p) -> None:
+    """Write the packed copies of W1, W3, W2 into W1p, W3p, W2p (enqueued on
+    cfg.stream)."""
+    _check(LIB.moe_pack_weights(_ptr(W1), _ptr(W3), _ptr(W2), ctypes.byref(cfg), _ptr(W1p),
+                                _ptr(W3p), _ptr(W2p)), "moe_pack_weights")
 
 
 def moe_timing_enable(enable: bool = True) -> None:

@@ -14,6 +14,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 TOPK_THEN_SOFTMAX, SOFTMAX_THEN_TOPK = 0, 1
 PATH_AUTO, PATH_GROUPED, PATH_STREAM = 0, 1, 2
 OVERFLOW_DROP, OVERFLOW_REROUTE, OVERFLOW_SEQUENTIAL = 0, 1, 2
+WEIGHTS_ROW_MAJOR, WEIGHTS_PACKED = 0, 1
 
 
 class MoeError(RuntimeError):
@@ -40,6 +41,7 @@ class MoeConfig(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
         ("overflow", ctypes.c_int32),
+        ("weight_layout", ctypes.c_int32),
     ]
 
 
@@ -85,6 +87,9 @@ def _load():
         "moe_aux_loss": (ctypes.c_int, [P, P, CFG, ctypes.POINTER(ctypes.c_double)]),
         "moe_router_backward": (ctypes.c_int, [P, P, P, ctypes.c_double, ctypes.c_double, CFG,
                                                P, P, P, P]),
+        "moe_packed_weight_bytes": (ctypes.c_int, [CFG, ctypes.POINTER(ctypes.c_size_t),
+                                                   ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_pack_weights": (ctypes.c_int, [P, P, P, CFG, P, P, P]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_timing_only": (ctypes.c_int, [ctypes.c_char_p]),

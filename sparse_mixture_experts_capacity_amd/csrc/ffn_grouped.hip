@@ -302,7 +302,9 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   // B: load i fills rows (wave*B_LOADS + i)*B_ROWS_PER_LOAD onward; lane ->
   // row + lane/(BN/8), stored 16-byte chunk q = lane%(BN/8), which is half
   // (q&1) of stored segment q/2.  Columns past N read column 0 (their
-  // outputs are never stored).
+  // outputs are never stored).  With packed weights a step's rows of one
+  // tile are whole 32-row blocks: one contiguous run per block instead of a
+  // short piece of every row.  Either way the step advances by K-step x ldb.
   constexpr int BCH = BN / 8;                 // 16-byte chunks per B row
   const uint16_t* bsrc[S::B_LOADS];
 #pragma unroll
@@ -321,7 +323,16 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
       col = n0 + n;
     }
     if (col >= p.N) col = 0;
-    bsrc[i] = base + boff + static_cast<int64_t>(kr) * p.ldb + col;
+    int64_t bo;
+    if (p.b_block_cols) {
+      // packed: row kr of the step lies in block row kr / 32 (BK = 64 spans
+      // two), column col in block col / W
+      const int w = p.b_block_cols;
+      bo = static_cast<int64_t>(kr >> 5) * 32 * p.ldb + ((col / w) * 32 + (kr & 31)) * w + col % w;
+    } else {
+      bo = static_cast<int64_t>(kr) * p.ldb + col;
+    }
+    bsrc[i] = base + boff + bo;
   }
 
   // LDS byte address of this wavefront's destinations in stage 0
@@ -699,6 +710,30 @@ __global__ __launch_bounds__(256) void gather_blocked_kernel(
   }
 }
 
+// Packed weights: output element o (8 at a time, consecutive threads on
+// consecutive 16 bytes) of expert e is element (k, n) of its row-major
+// [K, N] matrix, or 0 past column N.
+__global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t* __restrict__ src,
+                                                          int64_t nexp, int K, int N, int W,
+                                                          int Npad, uint16_t* __restrict__ dst) {
+  const int64_t per = static_cast<int64_t>(K) * Npad;
+  const int64_t n8 = nexp * per / 8;
+  const int nbw = Npad / W;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n8;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t o = t * 8;
+    const int64_t e = o / per;
+    const int64_t rem = o - e * per;
+    const int64_t blk = rem / (32 * W);
+    const int within = static_cast<int>(rem - blk * 32 * W);
+    const int k = static_cast<int>(blk / nbw) * 32 + within / W;
+    const int n = static_cast<int>(blk % nbw) * W + within % W;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < N) v = *reinterpret_cast<const u32x4*>(src + (e * K + k) * static_cast<int64_t>(N) + n);
+    *reinterpret_cast<u32x4*>(dst + o) = v;
+  }
+}
+
 template <typename Kern>
 hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, int waves = 4) {
   const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n * g.ksplit;
@@ -723,6 +758,16 @@ hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
   }
   if (g.bm == kGroupedBMWide) return launch_bf16_shape<SWIGLU, dma::ShapeWide>(g, s);
   return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
+}
+hipError_t launch_pack_blocks(const void* src, int64_t nexp, int K, int N, int W, void* dst,
+                              hipStream_t s) {
+  const int Npad = (N + W - 1) / W * W;
+  const int64_t n8 = nexp * K * static_cast<int64_t>(Npad) / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 256 * 64);
+  pack_blocks_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(
+      static_cast<const uint16_t*>(src), nexp, K, N, W, Npad, static_cast<uint16_t*>(dst));
+  return hipGetLastError();
 }
 hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm, int topk,
                                  const int32_t* nrows_dev, int64_t R, int d, void* Xb,

@@ -85,7 +85,17 @@ struct GroupedGemm {
   int64_t a_block_rows;     // A (then perm and lda are not used)
   int64_t c_block_rows;     // SwiGLU output H
   int c_bf16;               // plain bf16 kernel, ksplit 1: store C rounded to bf16
+  // Packed B (bf16 kernels): 0 = row-major with row stride ldb; otherwise the
+  // block width W (128 or 256): element (k, n) of an expert's matrix at
+  // ((k / 32) * (ldb / W) + n / W) * 32 * W + (k % 32) * W + n % W, with ldb
+  // the padded N (a multiple of W) and b_stride = K * ldb.
+  int b_block_cols;
 };
+// Packed copy of nexp row-major [K, N] bf16 matrices in the layout above
+// (block width W, padded width Npad = N rounded up to W; pad columns zero).
+// K % 32 == 0, N % 8 == 0.
+hipError_t launch_pack_blocks(const void* src, int64_t nexp, int K, int N, int W, void* dst,
+                              hipStream_t s);
 // Xb = kept token rows x[perm[s] / topk] for slots s < *nrows_dev, K-blocked
 // with R rows.
 hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm, int topk,

@@ -221,6 +221,8 @@ int check(const moe_config_t* c) {
     return fail(MOE_EINVAL, "ffn_path = %d is not a moe_ffn_path_t", c->ffn_path);
   if (c->overflow < MOE_OVERFLOW_DROP || c->overflow > MOE_OVERFLOW_SEQUENTIAL)
     return fail(MOE_EINVAL, "overflow = %d is not a moe_overflow_t", c->overflow);
+  if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_PACKED)
+    return fail(MOE_EINVAL, "weight_layout = %d is not a moe_weight_layout_t", c->weight_layout);
   if (isnan(c->capacity_factor) || c->capacity_factor > 1e6)
     return fail(MOE_EINVAL, "capacity_factor must be a number <= 1e6");
   if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
@@ -234,9 +236,16 @@ int check(const moe_config_t* c) {
   } else {
     if (c->ffn_path == MOE_PATH_STREAM)
       return fail(MOE_EUNSUPPORTED, "fp32 layers run on the fp32 grouped kernels only");
+    if (c->weight_layout == MOE_WEIGHTS_PACKED)
+      return fail(MOE_EUNSUPPORTED, "packed weights are for bf16 layers");
   }
   return MOE_OK;
 }
+
+// Packed weights: block widths of W1/W3 and of W2, and the padded widths.
+constexpr int kPackW13 = 128;
+constexpr int kPackW2 = 256;
+int64_t pad_to(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // K parts for a GEMM with `tiles` output tiles and `ksteps` 64-deep K
 // steps: enough for ~512 workgroups (more than 1 only when the tiles alone
@@ -646,11 +655,15 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
                  idx, w, s);
   if (rc != MOE_OK) return rc;
 
-  const int64_t dF = static_cast<int64_t>(p.d) * p.F;
   // GEMM1 (routed): H[slot] = silu(x[token] W1[e]) * (x[token] W3[e])
+  // Packed weights: W1/W3 rows padded to F13 columns, W2 rows to D2.
+  const bool packed = cfg->weight_layout == MOE_WEIGHTS_PACKED;
+  const int F13 = packed ? static_cast<int>(pad_to(p.F, kPackW13)) : p.F;
+  const int D2 = packed ? static_cast<int>(pad_to(p.d, kPackW2)) : p.d;
   moe::GroupedGemm g1{};
   g1.A = x; g1.lda = p.d; g1.perm = at<int32_t>(ws, p.perm); g1.topk = p.k;
-  g1.B = W1; g1.B3 = W3; g1.b_stride = dF; g1.group_base = 0; g1.ldb = p.F;
+  g1.B = W1; g1.B3 = W3; g1.b_stride = static_cast<int64_t>(p.d) * F13; g1.group_base = 0;
+  g1.ldb = F13; g1.b_block_cols = packed ? kPackW13 : 0;
   g1.K = p.d; g1.N = p.F; g1.ngroups_n = 1; g1.C = at<void>(ws, p.H); g1.ldc = p.F;
   g1.c_group_col = 0; g1.tiles = at<moe::Tile>(ws, p.tiles); g1.ntiles = at<int32_t>(ws, p.ntiles);
   g1.tstart = at<int32_t>(ws, p.tstart); g1.n_experts = p.E; g1.ksplit = 1; g1.c_split = 0;
@@ -669,7 +682,8 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   // GEMM2 (routed): Y[slot] = H[slot] W2[e]
   moe::GroupedGemm g2 = g1;
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
-  g2.ldb = p.d; g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
+  g2.ldb = D2; g2.b_stride = static_cast<int64_t>(p.F) * D2; g2.b_block_cols = packed ? kPackW2 : 0;
+  g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
   g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d; g2.narrow_n = 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
@@ -689,7 +703,8 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     s2 = s1;
     s2.a_block_rows = s1.c_block_rows; s2.c_block_rows = 0;
     s2.A = at<void>(ws, p.Hs); s2.lda = static_cast<int64_t>(p.S) * p.F; s2.B = W2; s2.B3 = nullptr;
-    s2.b_stride = dF; s2.group_base = p.E; s2.ngroups_n = 1; s2.ldb = p.d;
+    s2.b_stride = static_cast<int64_t>(p.F) * D2; s2.group_base = p.E; s2.ngroups_n = 1;
+    s2.ldb = D2; s2.b_block_cols = packed ? kPackW2 : 0;
     s2.K = p.S * p.F; s2.N = p.d; s2.C = at<void>(ws, p.Ys); s2.ldc = p.d; s2.c_group_col = 0;
     s2.ksplit = p.shared2_split; s2.c_split = p.T * p.d;
   }
@@ -914,6 +929,35 @@ int moe_aux_loss(const float* logits, const int32_t* counts, const moe_config_t*
   HIP_TRY(hipMemcpyAsync(&v, at<double>(ws, p.stats), sizeof(double), hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
   *aux_out = v;
+  g_err.clear();
+  return MOE_OK;
+}
+
+int moe_packed_weight_bytes(const moe_config_t* cfg, size_t* w13_bytes, size_t* w2_bytes) {
+  int rc = check(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->dtype != MOE_DTYPE_BF16) return fail(MOE_EUNSUPPORTED, "packed weights are for bf16 layers");
+  const int64_t n = cfg->n_experts + cfg->n_shared;
+  if (w13_bytes)
+    *w13_bytes = static_cast<size_t>(2 * n * cfg->d_model * pad_to(cfg->d_ff, kPackW13));
+  if (w2_bytes)
+    *w2_bytes = static_cast<size_t>(2 * n * cfg->d_ff * pad_to(cfg->d_model, kPackW2));
+  g_err.clear();
+  return MOE_OK;
+}
+
+int moe_pack_weights(const void* W1, const void* W3, const void* W2, const moe_config_t* cfg,
+                     void* W1p, void* W3p, void* W2p) {
+  int rc = check(cfg);
+  if (rc != MOE_OK) return rc;
+  if (cfg->dtype != MOE_DTYPE_BF16) return fail(MOE_EUNSUPPORTED, "packed weights are for bf16 layers");
+  if (!W1 || !W3 || !W2 || !W1p || !W3p || !W2p)
+    return fail(MOE_EINVAL, "W1, W3, W2, W1p, W3p and W2p must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  const int64_t n = cfg->n_experts + cfg->n_shared;
+  HIP_TRY(moe::launch_pack_blocks(W1, n, cfg->d_model, cfg->d_ff, kPackW13, W1p, s));
+  HIP_TRY(moe::launch_pack_blocks(W3, n, cfg->d_model, cfg->d_ff, kPackW13, W3p, s));
+  HIP_TRY(moe::launch_pack_blocks(W2, n, cfg->d_ff, cfg->d_model, kPackW2, W2p, s));
   g_err.clear();
   return MOE_OK;
 }

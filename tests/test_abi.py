@@ -69,6 +69,9 @@ def cfg(**kw):
     (dict(overflow=moe.OVERFLOW_SEQUENTIAL), moe.MOE_OK),
     (dict(overflow=3), moe.MOE_EINVAL),
     (dict(overflow=-1), moe.MOE_EINVAL),
+    (dict(weight_layout=moe.WEIGHTS_PACKED), moe.MOE_OK),
+    (dict(weight_layout=2), moe.MOE_EINVAL),
+    (dict(dtype="f32", weight_layout=moe.WEIGHTS_PACKED), moe.MOE_EUNSUPPORTED),
 ])
 def test_check_config(kw, code):
     c = cfg(**kw)
@@ -106,9 +109,11 @@ def test_workspace_grows_with_tokens():
 
 
 def test_struct_layouts_match_the_header():
-    # moe_config_t ends with the overflow policy; moe_stats_t with the
+    # moe_config_t ends with the overflow policy and the weight layout
+    # (which fills the padding after it); moe_stats_t with the
     # overflow counters (offsets as the C compiler lays them out on x86-64)
     assert _lib.MoeConfig.overflow.offset == 88 and ctypes.sizeof(_lib.MoeConfig) == 96
+    assert _lib.MoeConfig.weight_layout.offset == 92
     assert _lib.MoeStats.rounds.offset == 96 and ctypes.sizeof(_lib.MoeStats) == 104
 
 
@@ -145,3 +150,29 @@ def test_router_backward_argument_checks():
                                        None, None) == moe.MOE_EWORKSPACE
     assert moe.LIB.moe_router_backward(None, None, None, 0.0, 0.0, ctypes.byref(cfg(T=0)), None,
                                        None, None, None) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("d,F,E,S", [(128, 256, 8, 0), (192, 320, 4, 2), (4096, 14336, 8, 0),
+                                     (5120, 1536, 160, 2)])
+def test_packed_weight_sizes(d, F, E, S):
+    # W1/W3 rows padded to a multiple of 128 columns, W2 rows to 256
+    c = cfg(d_model=d, d_ff=F, n_experts=E, n_shared=S)
+    w13, w2 = moe.moe_packed_weight_bytes(c)
+    pad = lambda v, m: -(-v // m) * m
+    assert w13 == 2 * (E + S) * d * pad(F, 128)
+    assert w2 == 2 * (E + S) * F * pad(d, 256)
+    assert w13 >= 2 * (E + S) * d * F and w2 >= 2 * (E + S) * F * d
+
+
+def test_pack_weights_argument_checks():
+    # host-side validation only: nothing is launched
+    c = cfg()
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_pack_weights(None, None, None, c, None, None, None)
+    assert e.value.code == moe.MOE_EINVAL
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_packed_weight_bytes(cfg(dtype="f32"))
+    assert e.value.code == moe.MOE_EUNSUPPORTED
+    fake = 256   # never dereferenced: the checks fail first
+    assert moe.LIB.moe_pack_weights(fake, fake, fake, ctypes.byref(cfg(dtype="f32")), fake, fake,
+                                    fake) == moe.MOE_EUNSUPPORTED
