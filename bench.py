@@ -32,10 +32,11 @@ PEAK_HBM_GBS = 8000.0
 # describes the kernel and the bench reports null.
 MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
-    # routed SwiGLU GEMM; the counter summaries are kept beside the profiles
-    "mixtral_prefill": ("6aeb8185bda30ce3", 4561.87e6, 121.22e6),
-    "deepseek": ("6aeb8185bda30ce3", 5371.32e6, 75.89e6),
-    "mixtral_decode_t64": ("6aeb8185bda30ce3", 1892.84e6, 3.67e6),
+    # routed SwiGLU GEMM on packed weights (the default layout); the counter
+    # summaries are kept beside the profiles
+    "mixtral_prefill": ("1fee33f4daec8352", 3934.61e6, 121.86e6),
+    "deepseek": ("1fee33f4daec8352", 5341.05e6, 75.62e6),
+    "mixtral_decode_t64": ("1fee33f4daec8352", 1891.60e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.
@@ -347,7 +348,7 @@ def main():
     dom_ms = t_dom / n_dom if n_dom else float("nan")
     digest = source_digest()
     meas = (MEASURED_TRAFFIC.get(w.name)
-            if w.overflow == 0 and args.capacity_factor is None else None)
+            if w.overflow == 0 and args.capacity_factor is None and packed else None)
     traffic = None
     if meas is not None and meas[0] == digest:
         traffic = meas[1] + meas[2]
