@@ -41,7 +41,8 @@
  *   - All layouts are dense row-major with no padding:
  *       x [T, d]; W_gate [d, E]; W1, W3 [E+S, d, F]; W2 [E+S, F, d];
  *       out [T, d]; logits [T, E] fp32; bias [E] fp32.
- *     The S shared experts follow the E routed experts in W1/W3/W2.
+ *     The S shared experts follow the E routed experts in W1/W3/W2, which
+ *     may instead be given in the packed layout (moe_weight_layout_t).
  *   - x, W_gate, W1, W3, W2 and out share cfg->dtype (fp32 or bf16); router
  *     logits, bias and gate weights are fp32; indices int32.
  *   - Work is enqueued on cfg->stream (a hipStream_t; NULL = the null

@@ -18,13 +18,19 @@
 // (8 consecutive k of one column per lane) are read with ds_read_b64_tr_b16,
 // which transposes 4 x 4 blocks of 16-bit values across each 16-lane group.
 // Both tiles use XOR swizzles instead of padding so the DMA rows stay dense
-// and the fragment reads are free of bank conflicts.  Tile shapes:
+// and the fragment reads are free of bank conflicts.  The weights may be
+// row-major or packed in 32-row blocks (then a tile's K step reads whole
+// contiguous runs); only the source addresses differ.  Tile shapes (the
+// list near the end of the dma namespace):
+//   32 x 256 or 32 x 128, K step 64, 4 wavefronts, 4 stages: short batches
+//     (decode), where the weights stream once and K may be split over
+//     several workgroups;
 //   128 x 256, K step 32, 8 wavefronts, 3 stages, 72 KB: two workgroups per
-//     CU, for experts with many rows (prefill);
-//   128 x 256, K step 64, 8 wavefronts, 3 stages, 144 KB: one workgroup per
-//     CU, for a few hundred rows per expert;
-//   32 x 256, K step 64, 4 wavefronts, 4 stages: short batches (decode), where
-//     the weights stream once and K may be split over several workgroups.
+//     CU, for experts with hundreds to ~1500 rows (prefill);
+//   256 x 256, K step 32, 8 wavefronts, 4 stages, 128 KB: one workgroup per
+//     CU, for a few hundred rows per expert or for thousands.
+// On an expert's last, short M-tile the 16-row fragments past its end are
+// neither read nor multiplied.
 //
 // SwiGLU epilogue: a tile's 256 B columns are 128 W1 columns followed by the
 // same 128 W3 columns, and each wavefront owns matching halves, so u and v of

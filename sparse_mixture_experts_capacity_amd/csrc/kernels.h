@@ -63,7 +63,7 @@ struct GroupedGemm {
   const void* B3;           // W3 base (SwiGLU only)
   int64_t b_stride;         // elements between consecutive experts
   int group_base;           // expert index of group 0
-  int ldb;                  // row stride of B (its N)
+  int ldb;                  // row stride of B: its N (packed: N padded to the block)
   int K;                    // contraction length
   int N;                    // output columns per group
   int ngroups_n;            // groups laid side by side along N (shared GEMM1)
@@ -103,7 +103,7 @@ hipError_t launch_gather_blocked(const void* x, int64_t ldx, const int32_t* perm
                                  hipStream_t s);
 constexpr int kGroupedBM = 128;   // M-tile of the bf16 MFMA kernels, long batches
 constexpr int kGroupedBMShort = 32;  // M-tile for short batches (few rows per expert)
-constexpr int kGroupedBMWide = 256;  // M-tile for a few hundred rows per expert
+constexpr int kGroupedBMWide = 256;  // M-tile for a few hundred, or thousands of, rows per expert
 constexpr int kF32BM = 64;        // M-tile of the fp32 kernels
 hipError_t launch_grouped_swiglu_bf16(const GroupedGemm& g, hipStream_t s);
 hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s);
