@@ -354,8 +354,10 @@ int make_plan(const moe_config_t* c, Plan* p) {
   // parts in a fixed order.  The estimate of routed M-tiles assumes at most
   // min(E, T*k) experts are hit.  The grouped path never splits; the
   // streaming path always splits as far as the workgroup target allows.
+  // Short batches' down projection takes 128-wide weight tiles (two
+  // workgroups per CU), so the same workgroup count needs half the K parts.
   if (p->bf16 && p->path != MOE_PATH_GROUPED) {
-    const int ntn2 = (p->d + 255) / 256;
+    const int ntn2 = p->bm == moe::kGroupedBMShort ? (p->d + 127) / 128 : (p->d + 255) / 256;
     const int64_t hit = p->TK < p->E ? p->TK : p->E;
     const int64_t mt_est = p->rows_max / p->bm + hit;
     p->ffn2_split = split_for(mt_est * ntn2, p->F / 64, p->path == MOE_PATH_STREAM);
@@ -370,7 +372,8 @@ int make_plan(const moe_config_t* c, Plan* p) {
     }
     if (p->S > 0) {
       const int64_t mts = (p->T + p->static_bm - 1) / p->static_bm;
-      p->shared2_split = split_for(mts * ntn2, p->S * p->F / 64, p->path == MOE_PATH_STREAM);
+      const int ntn2s = (p->d + 255) / 256;   // the shared experts keep 256-wide tiles
+      p->shared2_split = split_for(mts * ntn2s, p->S * p->F / 64, p->path == MOE_PATH_STREAM);
     }
   }
 
@@ -684,7 +687,8 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
   g2.ldb = D2; g2.b_stride = static_cast<int64_t>(p.F) * D2; g2.b_block_cols = packed ? kPackW2 : 0;
   g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
-  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d; g2.narrow_n = 0;
+  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
+  g2.narrow_n = p.bm == moe::kGroupedBMShort ? 1 : 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
   g2.c_bf16 = p.y_bf16 ? 1 : 0;
