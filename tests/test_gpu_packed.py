@@ -86,3 +86,60 @@ def test_forward_packed_equals_row_major(case):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out_rm.view(torch.int16))
     assert st["dropped"] >= 0
+
+
+def _packed_cfg(w, run, stream=None):
+    return moe.make_config(T=w.T, d_model=w.d, d_ff=w.F, n_experts=w.E, top_k=w.k,
+                           n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
+                           capacity_factor=w.capacity_factor, dtype=w.dtype,
+                           logit_bias=run.bias, stream=stream,
+                           weight_layout=moe.WEIGHTS_PACKED)
+
+
+def test_router_backward_after_packed_forward():
+    # the backward reads the forward's expert rows: the same bits either way
+    w = PACKED_CASES["fine_drops"]
+    say("[packed] router backward after a packed forward")
+    run = Run(w)
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    dout = torch.randn((w.T, w.d), generator=gen, device=DEV).to(w.torch_dtype)
+    results = []
+    for packed in (False, True):
+        cfg = _packed_cfg(w, run) if packed else config_for(w, bias=run.bias)
+        Ws = packed_copies(run, cfg) if packed else (run.W1, run.W3, run.W2)
+        ws = moe.Workspace(moe.moe_workspace_size(cfg))
+        ws.bind(cfg)
+        out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=DEV)
+        moe.moe_forward(run.x, run.Wg, *Ws, cfg, out)
+        bufs = [torch.empty((w.T, w.E), device=DEV), torch.empty((w.d, w.E), device=DEV),
+                torch.empty((w.E,), device=DEV), torch.empty((w.T, w.d), device=DEV)]
+        moe.moe_router_backward(run.x, run.Wg, dout, cfg, *bufs, aux_coef=0.05, entropy_coef=0.01)
+        torch.cuda.synchronize()
+        results.append(bufs)
+    for a, b in zip(*results):
+        assert torch.equal(a, b)
+
+
+def test_packed_forward_graph_replay():
+    w = PACKED_CASES["long_shared"]
+    say("[packed] forward captured into a graph")
+    run = Run(w)
+    s = torch.cuda.Stream()
+    cfg = _packed_cfg(w, run, stream=s)
+    W1p, W3p, W2p = packed_copies(run, cfg)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    out = torch.empty((w.T, w.d), dtype=w.torch_dtype, device=DEV)
+    with torch.cuda.stream(s):
+        moe.moe_forward(run.x, run.Wg, W1p, W3p, W2p, cfg, out)
+    s.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_forward(run.x, run.Wg, W1p, W3p, W2p, cfg, out)
+    for rep in range(3):
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
