@@ -20,12 +20,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def config_for(w: Workload, T=None, path=moe.PATH_AUTO, bias=None, stream=None):
+def config_for(w: Workload, T=None, path=moe.PATH_AUTO, bias=None, stream=None, packed=False):
     return moe.make_config(
         T=w.T if T is None else T, d_model=w.d, d_ff=w.F, n_experts=w.E,
         top_k=w.k, n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
         capacity_factor=w.capacity_factor, dtype=w.dtype, ffn_path=path,
-        logit_bias=bias, stream=stream, overflow=w.overflow)
+        logit_bias=bias, stream=stream, overflow=w.overflow,
+        weight_layout=moe.WEIGHTS_PACKED if packed else moe.WEIGHTS_ROW_MAJOR)
 
 
 def shape_of(w: Workload, T=None) -> O.LayerShape:
@@ -56,6 +57,7 @@ class Run:
         self.hWg = inp.W_gate.cpu()
         self.hbias = inp.bias.cpu() if inp.bias is not None else None
         self._hW = None
+        self._packed = None
         say(f"  inputs {w.name} T={w.T} d={w.d} F={w.F} E={w.E} k={w.k} S={w.S} "
             f"on {gen_device}: {time.time() - t0:.1f}s")
 
@@ -68,15 +70,25 @@ class Run:
         W1, W3, W2 = self.host_weights()
         return to64(W1[e]), to64(W3[e]), to64(W2[e])
 
-    def forward(self, path=moe.PATH_AUTO, stats=True, T=None):
+    def packed_weights(self, cfg):
+        """Packed copies of W1, W3, W2 (made once, as a server would)."""
+        if self._packed is None:
+            w13, w2 = moe.moe_packed_weight_bytes(cfg)
+            self._packed = tuple(torch.empty(n // 2, dtype=torch.bfloat16, device=DEV)
+                                 for n in (w13, w13, w2))
+            moe.moe_pack_weights(self.W1, self.W3, self.W2, cfg, *self._packed)
+            torch.cuda.synchronize()
+        return self._packed
+
+    def forward(self, path=moe.PATH_AUTO, stats=True, T=None, packed=False):
         w = self.w
         T = w.T if T is None else T
-        cfg = config_for(w, T=T, path=path, bias=self.bias, stream=None)
+        cfg = config_for(w, T=T, path=path, bias=self.bias, stream=None, packed=packed)
+        W = self.packed_weights(cfg) if packed else (self.W1, self.W3, self.W2)
         ws = moe.Workspace(moe.moe_workspace_size(cfg))
         ws.bind(cfg)
         out = torch.empty((T, w.d), dtype=w.torch_dtype, device=DEV)
-        st = moe.moe_forward(self.x[:T], self.Wg, self.W1, self.W3, self.W2, cfg,
-                             out, stats=stats)
+        st = moe.moe_forward(self.x[:T], self.Wg, *W, cfg, out, stats=stats)
         torch.cuda.synchronize()
         return out, st
 
