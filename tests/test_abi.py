@@ -11,8 +11,8 @@ import oracle.oracle as O
 import sparse_mixture_experts_capacity_amd as moe
 from sparse_mixture_experts_capacity_amd import _lib
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "moe.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
 
 
 def declared_symbols():
@@ -176,3 +176,14 @@ def test_pack_weights_argument_checks():
     fake = 256   # never dereferenced: the checks fail first
     assert moe.LIB.moe_pack_weights(fake, fake, fake, ctypes.byref(cfg(dtype="f32")), fake, fake,
                                     fake) == moe.MOE_EUNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback: without libmoe.so the package refuses to import
+    import subprocess
+    import sys
+    env = dict(os.environ, MOE_LIB=str(tmp_path / "libmoe_missing.so"))
+    r = subprocess.run([sys.executable, "-c", "import sparse_mixture_experts_capacity_amd"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libmoe_missing.so" in r.stderr
