@@ -126,7 +126,10 @@ def test_route_logits_sequential_bit_exact(case):
 def _route_logits_case(case, policy):
     say(f"[route_logits] {case} overflow policy {policy}")
     w, L = _logits_case(case)
-    w = w.with_(overflow=policy)
+    _check_route_logits(w.with_(overflow=policy), L, policy)
+
+
+def _check_route_logits(w, L, policy):
     T, E, k = w.T, w.E, w.k
     # oracle on the same fp32 values, widened exactly (a NaN score ranks as
     # -infinity in the library; the oracle, which takes numbers only, gets -1e30)
@@ -170,6 +173,78 @@ def _route_logits_case(case, policy):
     say(f"  ok: C={C} overflowed={D['overflowed']} rerouted={D['rerouted']} "
         f"dropped={D['dropped']} rounds={D['rounds']} aux={st['aux_loss']:.6f} "
         f"min margin={float(margin.min()) if T else 0:.3g}")
+
+
+# seeded random configurations: expert counts from 1 to 256, k up to 8,
+# batch sizes on both sides of the one-workgroup routing limit, capacity
+# factors from 0.3 to unlimited, both gating orders, every overflow policy,
+# and scores rounded to halves in some cases so that many ties occur
+def _sweep_case(i):
+    rng = np.random.default_rng(1000 + i)
+    E = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64, 100, 160, 256]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    T = int(rng.choice([1, 3, 17, 64, 100, 129, 500, 1000, 2500, 4097]))
+    cf = float(rng.choice([0.0, 0.3, 0.75, 1.0, 1.25, 2.0]))
+    gating = int(rng.integers(0, 2))
+    renorm = bool(rng.integers(0, 2))
+    policy = int(rng.choice([O.OVERFLOW_DROP, O.OVERFLOW_REROUTE, O.OVERFLOW_SEQUENTIAL]))
+    w = Workload(f"sweep{i}", T=T, d=64, F=64, E=E, k=k, gating=gating, renormalize=renorm,
+                 capacity_factor=cf, overflow=policy)
+    L = random_logits(T, E, seed=2000 + i, scale=float(rng.choice([0.5, 1.0, 4.0])))
+    if rng.random() < 0.3:
+        L = torch.round(L * 2.0) / 2.0
+    return w, L, policy
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_route_logits_random_sweep(i):
+    w, L, policy = _sweep_case(i)
+    say(f"[sweep {i}] T={w.T} E={w.E} k={w.k} cf={w.capacity_factor} gating={w.gating} "
+        f"renorm={w.renormalize} policy={policy}")
+    _check_route_logits(w, L, policy)
+
+
+# seeded random bf16 layers: every output element against the oracle
+# within the bf16 bound, and the packed weights giving the same bits
+def _forward_sweep_case(i):
+    rng = np.random.default_rng(3000 + i)
+    E = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    k = int(rng.integers(1, min(E, 6) + 1))
+    T = int(rng.choice([1, 5, 40, 130, 333, 700]))
+    d = int(rng.choice([64, 128, 192, 256]))
+    F = int(rng.choice([64, 128, 192, 320]))
+    S = int(rng.choice([0, 0, 1, 2]))
+    cf = float(rng.choice([0.0, 0.5, 1.0, 1.25]))
+    gating = int(rng.integers(0, 2))
+    policy = int(rng.choice([O.OVERFLOW_DROP, O.OVERFLOW_REROUTE, O.OVERFLOW_SEQUENTIAL]))
+    bias = tuple(float(v) for v in rng.normal(0, 1, E)) if rng.random() < 0.3 else None
+    return Workload(f"fsweep{i}", T=T, d=d, F=F, E=E, k=k, S=S, gating=gating,
+                    renormalize=bool(rng.integers(0, 2)), capacity_factor=cf, overflow=policy,
+                    bias=bias)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_forward_random_sweep(i):
+    w = _forward_sweep_case(i)
+    say(f"[forward sweep {i}] T={w.T} d={w.d} F={w.F} E={w.E} k={w.k} S={w.S} "
+        f"cf={w.capacity_factor} gating={w.gating} policy={w.overflow} bias={w.bias is not None}")
+    run = Run(w)
+    out, st = run.forward()
+    outp, _ = run.forward(stats=False, packed=True)
+    assert torch.equal(outp.view(torch.int16), out.view(torch.int16))
+    g_route, _ = run.route()
+    ref = run.oracle()
+    ties, _, _ = near_tie_tokens(g_route["logits"].numpy().astype(np.float64), ref,
+                                 full_order=w.overflow == O.OVERFLOW_REROUTE)
+    ok = comparable_tokens(w, ref, ties, w.T)
+    got = to64(out)
+    good, ratio, excess = output_within_tolerance(got[ok], ref["out"][ok], w)
+    say(f"  ratio {ratio:.2e}, excess over bound {excess:.2e}, near ties {len(ties)}")
+    assert np.all(np.isfinite(got))
+    assert good
+    if len(ties) == 0:
+        assert np.array_equal(st["counts"], ref["dispatch"]["counts"])
+        assert np.array_equal(st["kept"], ref["dispatch"]["kept"])
 
 
 def test_aux_loss_entry_point():
