@@ -24,7 +24,7 @@ import torch
 import oracle.oracle as O
 import sparse_mixture_experts_capacity_amd as moe
 from gpu_helpers import DEV, Run, config_for, full_order_margin, say, shape_of, to64
-from workloads import PRESETS, SKEW_BIAS, SOFTMAX_THEN_TOPK, Workload
+from workloads import PRESETS, SKEW_BIAS, SOFTMAX_THEN_TOPK, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -140,7 +140,10 @@ BACKWARD_CASES = {
 def test_router_backward(case):
     w, alpha, beta = BACKWARD_CASES[case]
     say(f"[router backward] {case} aux_coef={alpha} entropy_coef={beta}")
-    run = Run(w)
+    _check_backward_case(Run(w), w, alpha, beta)
+
+
+def _check_backward_case(run, w, alpha, beta):
     g_route, _ = run.route()
     ref_fwd = run.oracle()
     # no routing decision within the logits' error: the oracle and the
@@ -169,6 +172,45 @@ def test_router_backward(case):
         np.put_along_axis(unchosen, ref_fwd["sel"], False, axis=1)
         assert np.count_nonzero(g["dlogits"][unchosen]) > 0.9 * unchosen.sum()
     _check_properties(g, to64(run.hx), to64(run.hWg), w.dtype == "bf16")
+
+
+# seeded random layers (bf16 and fp32, both gating orders, drops, rounds
+# and rerouting, shared experts, aux and entropy terms of either sign).  The
+# check needs the library and the oracle to make the same routing choices, so
+# each case takes the first input seed whose oracle scores keep every
+# decision margin above 1e-4 (computed on the host, the same everywhere).
+def _backward_sweep_case(i):
+    rng = np.random.default_rng(4000 + i)
+    policy = (O.OVERFLOW_DROP, O.OVERFLOW_SEQUENTIAL, O.OVERFLOW_REROUTE)[i % 3]
+    E = int(rng.choice([2, 4, 6] if policy == O.OVERFLOW_REROUTE else [2, 4, 8, 12, 16]))
+    w = Workload(f"bsweep{i}", T=int(rng.choice([16, 40, 100, 160])),
+                 d=int(rng.choice([64, 128, 192])), F=int(rng.choice([64, 128, 192])),
+                 E=E, k=int(rng.integers(1, min(E - 1 if E > 1 else 1, 4) + 1)),
+                 S=int(rng.choice([0, 1])), gating=int(rng.integers(0, 2)),
+                 renormalize=bool(rng.integers(0, 2)),
+                 capacity_factor=0.0 if i == 7 else float(rng.choice(
+                     [1.0, 1.25, 1.5] if policy == O.OVERFLOW_REROUTE else [0.5, 0.75, 1.0])),
+                 overflow=policy, dtype="f32" if i % 4 == 3 else "bf16")
+    alpha = float(rng.choice([0.0, 0.1, 0.5]))
+    beta = float(rng.choice([0.0, 0.05, -0.1]))
+    for seed in range(50):
+        inp = make_inputs(w, seed=seed)
+        L = O.router_logits(inp.x.to(torch.float64).numpy(), inp.W_gate.to(torch.float64).numpy())
+        margin = (full_order_margin(L) if policy == O.OVERFLOW_REROUTE
+                  else O.topk_select(L, w.k)[1])
+        if float(np.min(margin)) > 1e-4:
+            return w, alpha, beta, seed
+    raise RuntimeError("no seed with clear routing margins")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_router_backward_random_sweep(i):
+    w, alpha, beta, seed = _backward_sweep_case(i)
+    say(f"[router backward sweep {i}] T={w.T} d={w.d} E={w.E} k={w.k} S={w.S} "
+        f"gating={w.gating} renorm={w.renormalize} cf={w.capacity_factor} "
+        f"policy={w.overflow} {w.dtype} aux={alpha} ent={beta} seed={seed}")
+    run = Run(w, seed=seed)
+    _check_backward_case(run, w, alpha, beta)
 
 
 def test_router_backward_deterministic():
