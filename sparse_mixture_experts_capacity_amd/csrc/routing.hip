@@ -320,9 +320,19 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
   __syncthreads();
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int it = 0; it < kDispatchChunk / kWave; ++it) {
+  // All of the lane's expert ids are loaded before the first is ranked, so
+  // the loads are in flight together rather than one per step.
+  constexpr int kSteps = kDispatchChunk / kWave;
+  int ids[kSteps];
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
     const int64_t a = base + it * kWave + lane;
-    const int ein = a < TK ? topk_idx[a] : -1;
+    ids[it] = a < TK ? topk_idx[a] : -1;
+  }
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int64_t a = base + it * kWave + lane;
+    const int ein = ids[it];
     const bool valid = ein >= 0 && ein < E;   // ids outside [0, E) are ignored
     const int e = valid ? ein : 0;
     uint64_t match = __ballot(valid);
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
 // Slot offsets (exclusive prefix sum of the kept counts kc, in LDS) and the
 // M-tile list of the grouped expert GEMMs: tiles of at most `bm` rows, expert
 // by expert, with tstart[e] the first tile of expert e and tstart[E] their
-// number.  Called by every thread of one workgroup (blockDim.x >= 1); off and
+// number.  Called by every thread of one workgroup (blockDim.x >= 64); off and
 // toff are LDS arrays of E + 1 entries.
 // ---------------------------------------------------------------------------
 __device__ void slot_offsets_and_tiles(const int* kc, int E, int bm, int* off, int* toff,
@@ -355,17 +365,45 @@ __device__ void slot_offsets_and_tiles(const int* kc, int E, int bm, int* off, i
                                        int32_t* __restrict__ ntiles,
                                        int32_t* __restrict__ tstart) {
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    int so = 0, ts = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = so;
-      toff[i] = ts;
-      so += kc[i];
-      if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+  if (tid < kWave) {
+    // Wavefront 0: lane l sums experts [l*per, (l+1)*per), a shuffle scan
+    // gives each lane the rows and tiles of the experts before its run, and
+    // the lane then writes its run's exclusive offsets.
+    const int per = (E + kWave - 1) / kWave;
+    const int i0 = tid * per;
+    int rows = 0, ntl = 0;
+    for (int u = 0; u < per; ++u) {
+      const int i = i0 + u;
+      if (i < E) {
+        rows += kc[i];
+        if (bm > 0) ntl += (kc[i] + bm - 1) / bm;
+      }
     }
-    off[E] = so;
-    toff[E] = ts;
-    if (ntiles) *ntiles = ts;
+    int rows_in = rows, ntl_in = ntl;   // inclusive scans over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int r = __shfl_up(rows_in, o);
+      const int t = __shfl_up(ntl_in, o);
+      if (tid >= o) {
+        rows_in += r;
+        ntl_in += t;
+      }
+    }
+    int so = rows_in - rows, ts = ntl_in - ntl;
+    for (int u = 0; u < per; ++u) {
+      const int i = i0 + u;
+      if (i < E) {
+        off[i] = so;
+        toff[i] = ts;
+        so += kc[i];
+        if (bm > 0) ts += (kc[i] + bm - 1) / bm;
+      }
+    }
+    if (tid == kWave - 1) {
+      off[E] = rows_in;
+      toff[E] = ntl_in;
+      if (ntiles) *ntiles = ntl_in;
+    }
   }
   __syncthreads();
   for (int i = tid; i <= E; i += blockDim.x) {
@@ -398,12 +436,22 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
   __shared__ int toff[kMaxExperts + 1];
   const int e = threadIdx.x;
   if (e < E) {
+    // 16 chunk totals are read before any is overwritten with its base, so
+    // their loads overlap.
+    constexpr int kBatch = 16;
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * E + e;
-      const int c = blkcnt[i];
-      blkcnt[i] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int c[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        c[u] = b0 + u < nblk ? blkcnt[static_cast<int64_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (b0 + u < nblk) {
+          blkcnt[static_cast<int64_t>(b0 + u) * E + e] = run;
+          run += c[u];
+        }
+      }
     }
     counts[e] = run;
     kc[e] = min(run, C);
