@@ -204,6 +204,27 @@ def test_route_logits_random_sweep(i):
     _check_route_logits(w, L, policy)
 
 
+# Dispatch at the edges of its batching: the chunk pass ranks 1024
+# assignments per workgroup and the scan reads each expert's chunk totals 16
+# at a time (16, 17 and 32 chunks below); the slot offsets are scanned by one
+# wavefront with 1, 2 or 4 experts per lane (E = 64, 65, 200).
+DISPATCH_EDGE_CASES = {
+    "chunks16_E64": Workload("de16", T=8192, d=64, F=64, E=64, k=2, capacity_factor=1.0),
+    "chunks17_E65": Workload("de17", T=8193, d=64, F=64, E=65, k=2, capacity_factor=1.0,
+                             gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    "chunks17_E65_reroute": Workload("de17r", T=8193, d=64, F=64, E=65, k=2,
+                                     capacity_factor=1.0, overflow=O.OVERFLOW_REROUTE),
+    "chunks32_E200": Workload("de32", T=4096, d=64, F=64, E=200, k=8, capacity_factor=0.9),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DISPATCH_EDGE_CASES))
+def test_dispatch_batch_edges(case):
+    w = DISPATCH_EDGE_CASES[case]
+    say(f"[dispatch edges] {case}: T*k = {w.T * w.k}, E = {w.E}")
+    _check_route_logits(w, random_logits(w.T, w.E, seed=17), w.overflow)
+
+
 # seeded random bf16 layers: every output element against the oracle
 # within the bf16 bound, and the packed weights giving the same bits
 def _forward_sweep_case(i):
