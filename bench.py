@@ -34,9 +34,9 @@ MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM on packed weights (the default layout); the counter
     # summaries are kept beside the profiles
-    "mixtral_prefill": ("45c2e2d532af311b", 3953.10e6, 121.83e6),
-    "deepseek": ("45c2e2d532af311b", 5340.75e6, 75.63e6),
-    "mixtral_decode_t64": ("45c2e2d532af311b", 1891.58e6, 3.67e6),
+    "mixtral_prefill": ("083d59d9489780bd", 3947.96e6, 121.81e6),
+    "deepseek": ("083d59d9489780bd", 5340.59e6, 75.62e6),
+    "mixtral_decode_t64": ("083d59d9489780bd", 1891.66e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.

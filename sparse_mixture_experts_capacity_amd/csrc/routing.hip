@@ -152,15 +152,38 @@ __device__ __forceinline__ void topk_token(
     float* __restrict__ topk_w, int* sidx, float (&pacc)[V], float& hacc) {
   float val[V];
   bool taken[V];
+  // The K parts of the lane's V scores, summed in the fixed order q = 0, 1,
+  // ...; kParts parts of every score are loaded before the first add, so
+  // V * kParts = 8 loads are in flight together.
+  constexpr int kParts = 8 / V > 2 ? 8 / V : 2;
+  float lsum[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) lsum[v] = 0.f;
+  for (int q0 = 0; q0 < nsplit; q0 += kParts) {
+    float part[V][kParts];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int i = gl + v * G;
+#pragma unroll
+      for (int u = 0; u < kParts; ++u)
+        part[v][u] = (i < E && q0 + u < nsplit)
+                         ? lpart[static_cast<int64_t>(q0 + u) * split_stride + t * E + i]
+                         : 0.f;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+      for (int u = 0; u < kParts; ++u) {
+        if (q0 + u < nsplit) lsum[v] = (q0 + u == 0) ? part[v][u] : lsum[v] + part[v][u];
+      }
+    }
+  }
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int i = gl + v * G;
     float l = -INFINITY;
     if (i < E) {
-      l = lpart[t * E + i];
-      // fixed order q = 0, 1, ...; unrolled so the loads are in flight together
-#pragma unroll 8
-      for (int q = 1; q < nsplit; ++q) l += lpart[q * split_stride + t * E + i];
+      l = lsum[v];
       if (bias) l += bias[i];
       if (logits_out) logits_out[t * E + i] = l;
       // A NaN score ranks as -infinity: never ahead of a number, ties by
