@@ -188,15 +188,22 @@ bool decimal_of(double cf, __int128* D, int* X) {
 // Capacity C = ceil(T*k*cf/E), exactly, with cf its shortest decimal.
 // [Routing guide] "MoE routing, fully explained" (allinfo.ai.kr), "Plain
 // explanation" para 5: batch x top-k x capacity factor / experts.
+// Every product stays below 2^127: T*k < 2^31, D < 10^18, cf <= 1e6 keeps
+// num below 2^31 * 10^24, and den grows only while it is at most num (once
+// den > num > 0 the quotient lies in (0, 1) and rounds up to 1).
 int64_t exact_capacity(int64_t T, int k, int E, double cf) {
   if (!(cf > 0.0)) return T;  // no limit
   __int128 D;
   int X;
   if (!decimal_of(cf, &D, &X)) return -1;
   __int128 num = static_cast<__int128>(T) * k * D;
+  if (num == 0) return 0;
   __int128 den = E;
   for (; X > 0; --X) num *= 10;
-  for (; X < 0; ++X) den *= 10;
+  for (; X < 0; ++X) {
+    if (den > num) return 1;
+    den *= 10;
+  }
   __int128 q = (num + den - 1) / den;
   return static_cast<int64_t>(q);
 }

@@ -95,6 +95,10 @@ def test_null_config():
     (10, 1, 4, 1.0), (1, 1, 8, 1.0), (7, 3, 5, 0.3), (4096, 6, 160, 0.0),
     (333, 2, 7, 1.3333), (64, 2, 8, -1.0), (1000, 8, 64, 2.0 / 3.0),
     (12345, 4, 13, 1e-3), (5, 2, 3, 123456.0), (0, 2, 8, 1.25),
+    # tiny positive factors: C is at least 1 (and no exponent overflows)
+    (2048, 2, 8, 1e-40), (2048, 2, 8, 1e-60), (2048, 2, 8, 1e-130),
+    (2048, 2, 8, 5e-324), (2 ** 30 - 1, 1, 1, 1e-300), (0, 2, 8, 1e-130),
+    (2 ** 30 - 1, 1, 256, 999999.999999999), (3, 1, 256, 1.2345678901234567e-7),
 ])
 def test_capacity_matches_oracle(T, k, E, cf):
     c = cfg(T=T, top_k=k, n_experts=E, capacity_factor=cf)
