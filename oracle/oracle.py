@@ -44,7 +44,8 @@ design notes):
 * overflow policies other than dropping: a rerouted assignment goes, after
   every first choice has taken its slot and in flat assignment order, to the
   best-scoring expert (ties to the lower index) that the token did not choose
-  and that still has a free slot, and keeps its gate weight; with sequential
+  and has not been sent to already, and that still has a free slot, and
+  keeps its gate weight; with sequential
   processing nothing is dropped, the output equals the unlimited layer's, and
   the number of capacity-sized rounds of the busiest expert is reported;
 * the router backward differentiates the gates, the softmax and the
@@ -258,8 +259,9 @@ def dispatch_policy(sel: np.ndarray, logits: np.ndarray, E: int, C: int,
     * reroute: first choices take slots as in ``dispatch``; then every
       assignment that found its expert full, in flat order a = t*k + j, goes
       to the best-scoring expert of token t (ties to the lower index) among
-      those t did not choose that still have a free slot, after the rows
-      already there; with no such expert it is dropped.
+      those that t did not choose, that t's earlier assignments were not
+      sent to, and that still have a free slot, after the rows already
+      there; with no such expert it is dropped.
     """
     T, k = sel.shape
     d = dispatch(sel, E, C)
@@ -287,7 +289,10 @@ def dispatch_policy(sel: np.ndarray, logits: np.ndarray, E: int, C: int,
         if expert[a] >= 0:
             continue
         t = a // k
+        # a token is never sent to one expert twice: its own choices and the
+        # spare experts its earlier assignments were sent to are excluded
         chosen = set(flat[t * k:(t + 1) * k])
+        chosen.update(int(expert[b]) for b in range(t * k, a) if expert[b] >= 0)
         best = -1
         for c in range(E):
             if c in chosen or fill[c] >= C:

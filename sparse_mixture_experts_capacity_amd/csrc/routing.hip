@@ -490,18 +490,23 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
 // pass 2 every expert holds its first min(count, C) assignments.  The
 // overflow assignments (rank >= C) are then handled one after another in flat
 // order a = t*k + j: each goes to the highest-scoring expert of token t (ties:
-// lower index; NaN as -infinity) that t did not choose and that still has a
-// free slot, behind the rows already there, or is dropped when none has.
+// lower index; NaN as -infinity) that t did not choose, that t's earlier
+// assignments were not sent to, and that still has a free slot, behind the
+// rows already there, or is dropped when none has.
 //   A. all threads list the overflow assignments in flat order (ovf);
 //   B. in chunks of up to kRerouteRows assignments: all threads copy the
 //      chunk's score rows into LDS, writing NaN where an expert is not
-//      available (full, or one of the token's own choices); then wavefront 0
-//      takes the chunk 64 assignments at a time, lane i the i-th: each lane
-//      finds the best available expert of its row, and the lanes are
-//      accepted in order up to the first one whose expert was filled by the
-//      lanes before it; the rest search again.  Each repeat means one more
-//      expert became full (its column is then set to NaN in every row of the
-//      chunk), so there are at most (overflow / 64) + E rounds;
+//      available (full, one of the token's own choices, or a spare expert
+//      one of its assignments of an earlier chunk was sent to); then
+//      wavefront 0 takes the chunk 64 assignments at a time, lane i the
+//      i-th: each lane finds the best available expert of its row, and the
+//      lanes are accepted in order up to the first one whose expert was
+//      filled by the lanes before it, or taken by a lane before it of the
+//      same token; the rest search again.  An accepted expert becomes NaN in
+//      the later rows of the same token (a token's rows are adjacent).  Each
+//      repeat means one more expert became full (its column is then set to
+//      NaN in every row of the chunk) or one more of a token's rows was
+//      placed, so the rounds are bounded;
 //   C. kcount becomes the final rows per expert; offsets and tiles as pass 2.
 // xdest[a] / xrel[a] (overflow assignments only) receive the new expert (or
 // -1) and the row inside its range.
@@ -593,19 +598,31 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
       srow[r * stride + c] = v;
     }
     __syncthreads();
-    // NaN at the token's own choices
+    // NaN at the token's own choices, and at the spare experts its overflow
+    // assignments of earlier chunks (before the chunk's first row, a0) were
+    // sent to; the chunk's own rows are excluded as they are placed
+    const int a0 = sa[0];
     for (int i = tid; i < rows * k; i += blockDim.x) {
       const int r = i / k;
       const int a = sa[r];
-      const int c = topk_idx[a - a % k + (i - r * k)];
-      if (c >= 0 && c < E) srow[r * stride + c] = kNaN;
+      const int aj = a - a % k + (i - r * k);
+      const int c = topk_idx[aj];
+      if (c >= 0 && c < E) {
+        srow[r * stride + c] = kNaN;
+        if (aj < a0 && blkbase[(aj / kDispatchChunk) * E + c] + lrank[aj] >= C) {
+          const int x = xdest[aj];
+          if (x >= 0 && x < E) srow[r * stride + x] = kNaN;
+        }
+      }
     }
     __syncthreads();
     if (wave == 0) {
       const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;   // bits of an expert index
+      const int qmax = min(k, kWave);   // a token's rows lie within k lanes
       for (int b0 = 0; b0 < rows; b0 += kWave) {
         const bool have = b0 + lane < rows;
         const int a = have ? sa[b0 + lane] : 0;
+        const int tok = have ? a / k : -1;
         const float* row = srow + (b0 + lane) * stride;
         bool pending = have;
         // best and second-best available expert of the row (-1: none, -2:
@@ -664,7 +681,16 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
           }
           const int fb = valid ? fill[e] : 0;
           const int ahead = __popcll(match & lt);
-          const uint64_t clash = __ballot(valid && fb + ahead >= C);
+          // an earlier lane of this round holding a row of the same token
+          // picked the same expert: the token may not take it twice
+          bool dup = false;
+          for (int q = 1; q < qmax; ++q) {
+            const int src = lane >= q ? lane - q : lane;
+            const int tq = __shfl(tok, src);
+            const int eq = __shfl(valid ? e : -1, src);
+            dup = dup || (lane >= q && valid && tq == tok && eq == e);
+          }
+          const uint64_t clash = __ballot(valid && (fb + ahead >= C || dup));
           const int first = clash ? __ffsll(static_cast<unsigned long long>(clash)) - 1 : kWave;
           const bool accept = pending && lane < first;
           if (accept) {
@@ -680,6 +706,29 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
           if (leader) fill[e] = nfill;
           room -= __popcll(took);
           pending = pending && !accept;
+          // the expert an accepted row took is no longer available to the
+          // token's later rows: NaN in their staged scores, and out of the
+          // best / second of the lanes of this batch holding them
+          const bool placed = accept && valid;
+          if (placed) {
+            for (int q = 1; q < k; ++q) {
+              const int r2 = b0 + lane + q;
+              if (r2 >= rows || sa[r2] / k != tok) break;
+              srow[r2 * stride + e] = kNaN;
+            }
+          }
+          for (int q = 1; q < qmax; ++q) {
+            const int src = lane >= q ? lane - q : lane;
+            const int tq = __shfl(tok, src);
+            const int eq = __shfl(placed ? e : -1, src);
+            if (lane >= q && pending && eq >= 0 && tq == tok) {
+              if (second == eq) second = -2;
+              if (best == eq) {
+                best = second;
+                second = -2;
+              }
+            }
+          }
           // experts this round filled up: unavailable in every row of the chunk
           uint64_t filled = __ballot(leader && nfill >= C);
           while (filled) {

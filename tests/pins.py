@@ -368,6 +368,36 @@ def pin_reroute_hand_example(O):
     assert list(D["kept"]) == [1, 1, 1, 1]
     assert (D["overflowed"], D["rerouted"], D["dropped"], D["rounds"]) == (2, 2, 0, 2)
     assert list(D["counts"]) == [2, 2, 0, 0]
+    # Both choices of one token overflow while a spare expert has room for
+    # two rows: the token is sent there once, and its second overflow goes
+    # to its next-best spare.  Three tokens, four experts, top-2, two slots
+    # (3 x 2 x 4/3 / 4 = 2): tokens 0 and 1 fill experts 0 and 1; token 2's
+    # first overflow (a=4) takes expert 2 (score 3 > 2), its second (a=5)
+    # skips expert 2 (already its own) and takes expert 3.
+    L = np.array([[4.0, 3.0, 0.0, 0.0],
+                  [4.0, 3.0, 0.0, 0.0],
+                  [4.0, 3.5, 3.0, 2.0]])
+    assert O.capacity(3, 2, 4, 4.0 / 3.0) == 2
+    sel, _ = O.topk_select(L, 2)
+    D = O.dispatch_policy(sel, L, 4, 2, O.OVERFLOW_REROUTE)
+    assert list(D["expert"]) == [0, 1, 0, 1, 2, 3]
+    assert list(D["kept"]) == [2, 2, 1, 1]
+    assert list(D["slot"]) == [0, 2, 1, 3, 4, 5]
+    assert (D["overflowed"], D["rerouted"], D["dropped"]) == (2, 2, 0)
+    # With expert 3 unavailable (k = 3: token 2 chose it) the second
+    # overflow has no spare left and is dropped rather than doubled up.
+    L3 = np.array([[4.0, 3.0, 0.0, 2.5],
+                   [4.0, 3.0, 0.0, 2.5],
+                   [4.0, 3.5, 3.0, 3.2]])
+    sel3, _ = O.topk_select(L3, 3)
+    assert [list(r) for r in sel3] == [[0, 1, 3], [0, 1, 3], [0, 1, 3]]
+    D = O.dispatch_policy(sel3, L3, 4, 3, O.OVERFLOW_REROUTE)
+    # every expert has 3 slots: tokens 0-2 fit on 0, 1, 3; nothing overflows
+    assert D["overflowed"] == 0
+    D = O.dispatch_policy(sel3, L3, 4, 2, O.OVERFLOW_REROUTE)
+    # 2 slots: token 2's three choices all overflow; only expert 2 is spare
+    assert list(D["expert"]) == [0, 1, 3, 0, 1, 3, 2, -1, -1]
+    assert (D["overflowed"], D["rerouted"], D["dropped"]) == (3, 1, 2)
     # First choices are placed before any rerouted row: expert 2 is token 2's
     # own choice, so token 1's overflow (a=1) must skip it and take expert 1,
     # and token 3's overflow finds nothing free and is dropped.
@@ -421,7 +451,7 @@ def _check_reroute(O, sel, L, E, C, D):
         if base["slot"][a] >= 0:
             continue
         t = a // k
-        chosen = set(flat[t * k:t * k + k])
+        chosen = set(flat[t * k:t * k + k]) | {ex[b] for b in range(t * k, a) if ex[b] >= 0}
         occ = [int(base["kept"][c]) + sum(1 for b in range(a) if base["slot"][b] < 0 and ex[b] == c)
                for c in range(E)]
         free = [c for c in range(E) if c not in chosen and occ[c] < C]
@@ -517,7 +547,10 @@ def pin_overflow_forward(O):
     one = _experts(1, d, F, 151)[0]
     ref = O.forward(x, _shape(O, T, d, F, E, k), lambda e: one, W_gate=Wg,
                     bias=bias)
-    rr = O.forward(x, _shape(O, T, d, F, E, k, cf=1.0,
+    # (At factor 1.0 every slot is needed and one token's last overflow finds
+    # only the spare its first overflow took, so one assignment is dropped;
+    # 1.1 leaves a slot to spare.)
+    rr = O.forward(x, _shape(O, T, d, F, E, k, cf=1.1,
                              overflow=O.OVERFLOW_REROUTE),
                    lambda e: one, W_gate=Wg, bias=bias)
     D = rr["dispatch"]

@@ -149,7 +149,8 @@ def _reroute_variant(mode):
     overflow land on another of the token's own choices, 'worst' takes the
     lowest-scoring spare expert, 'onepass' handles assignments strictly in
     flat order so a later first choice can find its slot taken, 'weightless'
-    runs rerouted rows but leaves them out of the combine."""
+    runs rerouted rows but leaves them out of the combine, 'twice' lets a
+    token's second overflow land on the spare expert its first one took."""
     def fn(sel, logits, E, C, policy=O.OVERFLOW_DROP):
         if policy != O.OVERFLOW_REROUTE:
             return _orig["dispatch_policy"](sel, logits, E, C, policy)
@@ -174,6 +175,8 @@ def _reroute_variant(mode):
                 continue
             t = a // k
             chosen = set(flat[t * k:(t + 1) * k])
+            if mode != "twice":
+                chosen.update(expert[b] for b in range(t * k, a) if expert[b] >= 0)
             cand = [c for c in range(E) if fill[c] < C and (mode == "own" or c not in chosen)]
             if mode == "own":
                 cand = [c for c in cand if c != e]
@@ -300,6 +303,7 @@ MUTATIONS = {
     "reroute_to_worst_spare": ("dispatch_policy", _reroute_variant("worst")),
     "reroute_single_pass": ("dispatch_policy", _reroute_variant("onepass")),
     "reroute_rows_not_combined": ("dispatch_policy", _reroute_variant("weightless")),
+    "reroute_same_spare_twice": ("dispatch_policy", _reroute_variant("twice")),
     "sequential_drops": ("dispatch_policy", _sequential_as_drop),
     "rounds_rounded_down": ("dispatch_policy", _rounds_floor),
     "dispatch_drops_earliest": ("dispatch", _drop_earliest),
