@@ -120,11 +120,22 @@ def cpu_baseline(w, inp, n_tokens: int):
 
     import oracle.oracle as O
 
+    # threads the oracle's BLAS actually uses, the host's logical CPUs and
+    # its CPU model
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     hx = inp.x.cpu()
     hWg = inp.W_gate.cpu()
     W1, W3, W2 = inp.W1.cpu(), inp.W3.cpu(), inp.W2.cpu()
@@ -161,6 +172,7 @@ def cpu_baseline(w, inp, n_tokens: int):
         n = w.T if slope <= 0 else int(64 + max(0.0, 12.0 - tb) / slope)
         toks, dt = timed(max(64, min(n, w.T)))
     return dict(value=len(toks) / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                cpu_model=cpu_model, cpu_count=os.cpu_count(),
                 sample=(f"{w.name}: routing, capacity dispatch and statistics of all {w.T} "
                         f"tokens plus expert and shared-expert outputs of {len(toks)} "
                         f"seeded sampled tokens, fp64 NumPy on the host; value = "
@@ -448,7 +460,8 @@ def main():
         res["router_backward"] = bwd
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, inp, args.cpu_sample_tokens)
-        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        res["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample",
+                                                   "cpu_model", "cpu_count")}
         res["cpu_baseline"]["routing_dispatch_stats_s"] = cb["routing_seconds"]
     print(json.dumps(res), flush=True)
 

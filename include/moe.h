@@ -102,9 +102,11 @@ typedef enum {
  * expert first takes its own assignments in flat order a = t*k + j, up to C.
  *   DROP        the rest contribute nothing.
  *   REROUTE     then the rest, in flat order, each go to the highest-scoring
- *               expert (ties: lower index) that token t did not choose and
- *               that still has a free slot, placed after the rows already
- *               there, with their own gate weight; dropped if none has room.
+ *               expert (ties: lower index) that token t did not choose, that
+ *               t's earlier assignments were not sent to (a token never
+ *               meets one expert twice) and that still has a free slot,
+ *               placed after the rows already there, with their own gate
+ *               weight; dropped if none has room.
  *               Runs a one-workgroup pass; short batches lose the fused
  *               single-kernel routing.
  *   SEQUENTIAL  nothing is dropped: every assignment is processed by its
@@ -154,6 +156,9 @@ typedef struct {
   void* stream;          /* hipStream_t */
   int32_t overflow;      /* moe_overflow_t (0 = drop) */
   int32_t weight_layout; /* moe_weight_layout_t (0 = row-major) */
+  int32_t out_fp32;      /* 0: out in cfg->dtype; 1: out is fp32 [T, d] for
+                            either dtype (a bf16 layer then stores the fp32
+                            sum it would otherwise round to bf16, RNE) */
 } moe_config_t;
 
 typedef struct {
@@ -208,7 +213,12 @@ int64_t moe_capacity(const moe_config_t* cfg);
 /* Full layer forward, steps 1-5 (and 6 when stats != NULL).
  *   x [T, d], W_gate [d, E], W1/W3 [E+S, d, F], W2 [E+S, F, d]: inputs
  *   (W1, W3, W2 in cfg->weight_layout: row-major or packed),
- *   out [T, d]: output, fully overwritten.  stats: host struct or NULL. */
+ *   out [T, d]: output in cfg->dtype (fp32 when cfg->out_fp32), fully
+ *   overwritten.  stats: host struct or NULL.
+ * Precision of bf16 layers: products of bf16 values summed in fp32; the
+ * hidden rows silu(u) * v are rounded to bf16 once before the down
+ * projection; expert rows, gate weights and the weighted sum stay fp32 up to
+ * the output, which is rounded once (or not, with out_fp32). */
 int moe_forward(const void* x, const void* W_gate, const void* W1,
                 const void* W3, const void* W2, const moe_config_t* cfg,
                 void* out, moe_stats_t* stats);

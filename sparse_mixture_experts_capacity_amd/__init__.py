@@ -55,8 +55,9 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
                 dtype: str = "bf16", ffn_path: int = PATH_AUTO,
                 logit_bias=None, workspace=None, workspace_bytes: int = 0,
                 stream=0, overflow: int = OVERFLOW_DROP,
-                weight_layout: int = WEIGHTS_ROW_MAJOR) -> MoeConfig:
-    """Fill a moe_config_t.  ``stream`` = None means torch's current stream."""
+                weight_layout: int = WEIGHTS_ROW_MAJOR, out_fp32: bool = False) -> MoeConfig:
+    """Fill a moe_config_t.  ``stream`` = None means torch's current stream.
+    ``out_fp32``: the layer writes ``out`` as fp32 whatever its dtype."""
     c = MoeConfig()
     c.T = int(T)
     c.d_model = int(d_model)
@@ -75,6 +76,7 @@ def make_config(T: int, d_model: int, d_ff: int, n_experts: int, top_k: int,
     c.stream = _stream_handle(stream) if stream != 0 else None
     c.overflow = int(overflow)
     c.weight_layout = int(weight_layout)
+    c.out_fp32 = int(out_fp32)
     return c
 
 

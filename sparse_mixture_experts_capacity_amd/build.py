@@ -36,32 +36,29 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, defines=(), objdir=OBJ) -> str:
-    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-x", "hip", "-c",
-           os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
-    """Compile every source and link ``out``.  ``defines`` are extra -D
-    macros (tuning knobs of the kernels)."""
-    objdir = OBJ if not defines else OBJ + "_" + "_".join(d.replace("=", "") for d in defines)
-    os.makedirs(objdir, exist_ok=True)
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libmoe.so next to this file."""
+    os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, defines, objdir), SOURCES))
-    tmp = out + ".tmp"
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, out)
+    os.replace(tmp, LIB)
     if verbose:
-        print(f"built {out}")
-    return out
+        print(f"built {LIB}")
+    return LIB
 
 
 if __name__ == "__main__":

@@ -55,7 +55,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 template <typename TOut>
 __global__ __launch_bounds__(256) void gate_backward_kernel(
-    const TOut* __restrict__ dout, const void* __restrict__ Yv, bool ybf16, int ysplit,
+    const TOut* __restrict__ dout, const void* __restrict__ Yv, int ysplit,
     int64_t ystride,
     int64_t rows, bool vec4, const int32_t* __restrict__ slot, const int32_t* __restrict__ idx,
     const float* __restrict__ w, const float* __restrict__ logits,
@@ -74,22 +74,7 @@ __global__ __launch_bounds__(256) void gate_backward_kernel(
     const int64_t a = t * k + j;
     const int sl = slot[a];
     float dwj = 0.f;
-    if (sl >= 0 && sl < rows && ybf16) {   // bf16 rows, one part
-      const uint16_t* y = static_cast<const uint16_t*>(Yv) + static_cast<int64_t>(sl) * d;
-      float acc = 0.f;
-      if (vec4) {
-#pragma unroll 4
-        for (int c4 = lane; c4 < d / 4; c4 += kWave) {
-          const f32x4 yv = load4(y, c4);
-          const f32x4 gv = load4(g, c4);
-          acc += gv.x * yv.x + gv.y * yv.y + gv.z * yv.z + gv.w * yv.w;
-        }
-      } else {
-#pragma unroll 4
-        for (int c = lane; c < d; c += kWave) acc += load_elem(g, c) * load_elem(y, c);
-      }
-      dwj = wave_sum(acc);
-    } else if (sl >= 0 && sl < rows) {   // slots outside the row buffer are never read
+    if (sl >= 0 && sl < rows) {   // slots outside the row buffer are never read
       const float* y = static_cast<const float*>(Yv) + static_cast<int64_t>(sl) * d;
       float acc = 0.f;
       if (vec4) {
@@ -367,12 +352,12 @@ hipError_t launch_gate_backward(const RouterBackward& b, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>((b.T + wpb - 1) / wpb);
   if (b.bf16)
     gate_backward_kernel<uint16_t><<<blocks, wpb * kWave, 0, s>>>(
-        static_cast<const uint16_t*>(b.dout), b.Y, b.ybf16, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
+        static_cast<const uint16_t*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
         b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.ent_scale, b.inv_tk,
         b.dlogits);
   else
     gate_backward_kernel<float><<<blocks, wpb * kWave, 0, s>>>(
-        static_cast<const float*>(b.dout), b.Y, b.ybf16, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
+        static_cast<const float*>(b.dout), b.Y, b.ysplit, b.ystride, b.rows, b.vec4, b.slot, b.idx, b.w,
         b.logits, b.counts, b.T, b.k, b.E, b.d, b.chosen_softmax, b.aux_scale, b.ent_scale, b.inv_tk,
         b.dlogits);
   return hipGetLastError();

@@ -9,33 +9,24 @@
 // assignment is simply not computed, so it adds nothing (the surviving gates
 // are not rescaled).
 //
-// Y may be split into `ysplit` partial sums over K (weight-streaming path);
-// the partials are added in a fixed order, so results are bitwise
-// reproducible.  With one part, Y rows may be bf16 (half the bytes).  One
-// workgroup per token, columns strided over threads so each Y row is read
-// with coalesced 16-byte loads.  For bf16 rows the loads of all k rows of a
-// column group are issued before the first is used (the kernel is bound by
-// memory latency, not by arithmetic), and the sum is taken in j order.
+// Y rows are fp32 and may be split into `ysplit` partial sums over K
+// (weight-streaming path); the partials are added in a fixed order, so
+// results are bitwise reproducible.  One workgroup per token, columns strided
+// over threads so each Y row is read with coalesced 16-byte loads.  With one
+// part, the loads of all k rows of a column group are issued before the
+// first is used (the kernel is bound by memory latency, not by arithmetic),
+// and the sum is taken in j order.  The output is stored rounded to bf16
+// (RNE) or as the fp32 sum itself; both kernels form the same fp32 sum, so a
+// bf16 output is exactly the rounding of the fp32 one.
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-// Four consecutive elements of a row as fp32: column group c of a float row,
-// or of a bf16 row.
-__device__ __forceinline__ float4 load4f(const float* row, int c) {
-  return reinterpret_cast<const float4*>(row)[c];
-}
-__device__ __forceinline__ float4 load4f(const uint16_t* row, int c) {
-  const uint2 v = reinterpret_cast<const uint2*>(row)[c];
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
-}
-
 // NB: K parts loaded together (in flight at once), then added in part order.
-template <bool BF16OUT, typename TY, int NB>
+template <bool BF16OUT, int NB>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const TY* __restrict__ Y, int ysplit, int64_t ysplit_stride,
+    const float* __restrict__ Y, int ysplit, int64_t ysplit_stride,
     const int32_t* __restrict__ slot, const float* __restrict__ topk_w,
     const float* __restrict__ Ys, int ys_split, int64_t ys_stride, int64_t T,
     int k, int d, void* __restrict__ out) {
@@ -59,9 +50,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
         for (int u = 0; u < NB; ++u) {
           v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (p0 + u < ysplit) {
-            const TY* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
-            if (vec) v[u] = load4f(row, c);
-            else v[u].x = load_elem(row, c);
+            const float* row = Y + (p0 + u) * ysplit_stride + static_cast<int64_t>(s) * d;
+            if (vec) v[u] = reinterpret_cast<const float4*>(row)[c];
+            else v[u].x = row[c];
           }
         }
 #pragma unroll
@@ -104,21 +95,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
-// bf16 Y rows, one K part, bf16 output, d % 8 == 0: each thread takes 8
-// columns (one 16-byte load per row).  Up to 8 rows' loads are in flight at
-// once; the weighted sum runs in j order as in combine_kernel, so the two
-// give the same bits.
-__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
-  f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
-  f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
-  f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
-  f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
-}
-
-__global__ __launch_bounds__(512) void combine_bf16_rows_kernel(
-    const uint16_t* __restrict__ Y, const int32_t* __restrict__ slot,
+// One K part, d % 8 == 0: each thread takes 8 columns (two 16-byte loads per
+// row).  Up to 8 rows' loads are in flight at once; the weighted sum runs in
+// j order with the same operations as combine_kernel, so the two give the
+// same bits.
+template <bool BF16OUT>
+__global__ __launch_bounds__(512) void combine_rows_kernel(
+    const float* __restrict__ Y, const int32_t* __restrict__ slot,
     const float* __restrict__ topk_w, const float* __restrict__ Ys, int ys_split,
-    int64_t ys_stride, int64_t T, int k, int d, uint16_t* __restrict__ out) {
+    int64_t ys_stride, int64_t T, int k, int d, void* __restrict__ out) {
   const int64_t t = blockIdx.x;
   if (t >= T) return;
   const int ncols = d / 8;
@@ -129,23 +114,27 @@ __global__ __launch_bounds__(512) void combine_bf16_rows_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     for (int j0 = 0; j0 < k; j0 += 8) {
-      uint4 v[8];
+      float4 v[8][2];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        v[u] = make_uint4(0u, 0u, 0u, 0u);
+        v[u][0] = v[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (j0 + u < k) {
           const int s = st[j0 + u];
-          if (s >= 0) v[u] = reinterpret_cast<const uint4*>(Y + static_cast<int64_t>(s) * d)[c];
+          if (s >= 0) {
+            const float4* row = reinterpret_cast<const float4*>(Y + static_cast<int64_t>(s) * d);
+            v[u][0] = row[2 * c];
+            v[u][1] = row[2 * c + 1];
+          }
         }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (j0 + u < k && st[j0 + u] >= 0) {
           const float w = wt[j0 + u];
-          float y[8];
-          unpack8(v[u], y);
+          const float y[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                              v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, y[e], acc[e]);
+          for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, 0.f + y[e], acc[e]);
         }
       }
     }
@@ -157,25 +146,30 @@ __global__ __launch_bounds__(512) void combine_bf16_rows_kernel(
         acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
       }
     }
-    uint4 o;
-    o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-    o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-    o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-    reinterpret_cast<uint4*>(out + t * d)[c] = o;
+    if (BF16OUT) {
+      uint4 o;
+      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+      reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + t * d)[c] = o;
+    } else {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + t * d);
+      o[2 * c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      o[2 * c + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_stride,
+hipError_t launch_combine(const float* Y, int ysplit, int64_t ysplit_stride,
                           const int32_t* slot, const float* topk_w,
                           const float* Ys, int ys_split, int64_t ys_stride,
-                          int64_t T, int k, int d, void* out, bool bf16,
+                          int64_t T, int k, int d, void* out, bool bf16out,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (ybf16 && bf16 && ysplit == 1 && (d & 7) == 0 &&
-      (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+  if (ysplit == 1 && (d & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
     // 8 columns per thread; at most 512 threads per token, as few passes as
     // possible with the threads evenly loaded.  Short batches: 64-thread
     // workgroups over 64 column groups each.
@@ -190,9 +184,12 @@ hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_
       chunks = 1;
     }
     const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
-    combine_bf16_rows_kernel<<<grid, tpb, 0, s>>>(static_cast<const uint16_t*>(Y), slot, topk_w,
-                                                  Ys, ys_split, ys_stride, T, k, d,
-                                                  static_cast<uint16_t*>(out));
+    if (bf16out)
+      combine_rows_kernel<true><<<grid, tpb, 0, s>>>(Y, slot, topk_w, Ys, ys_split, ys_stride,
+                                                    T, k, d, out);
+    else
+      combine_rows_kernel<false><<<grid, tpb, 0, s>>>(Y, slot, topk_w, Ys, ys_split, ys_stride,
+                                                     T, k, d, out);
     return hipGetLastError();
   }
   // enough workgroups to cover the GPU even for a handful of tokens: short
@@ -203,21 +200,15 @@ hipError_t launch_combine(const void* Y, bool ybf16, int ysplit, int64_t ysplit_
   if (T >= 256) chunks = 1;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(chunks));
   // parts loaded together: as many as there are, up to 16 (registers)
-#define MOE_COMBINE_NB(O, TY, NB)                                                      \
-  combine_kernel<O, TY, NB><<<grid, tpb, 0, s>>>(static_cast<const TY*>(Y), ysplit,    \
-                                                 ysplit_stride, slot, topk_w, Ys,      \
-                                                 ys_split, ys_stride, T, k, d, out)
-#define MOE_COMBINE(O, TY)                  \
-  if (ysplit <= 2) MOE_COMBINE_NB(O, TY, 2); \
-  else if (ysplit <= 8) MOE_COMBINE_NB(O, TY, 8); \
-  else MOE_COMBINE_NB(O, TY, 16)
-  if (bf16) {
-    if (ybf16) { MOE_COMBINE(true, uint16_t); }
-    else { MOE_COMBINE(true, float); }
-  } else {
-    if (ybf16) { MOE_COMBINE(false, uint16_t); }
-    else { MOE_COMBINE(false, float); }
-  }
+#define MOE_COMBINE_NB(O, NB)                                                          \
+  combine_kernel<O, NB><<<grid, tpb, 0, s>>>(Y, ysplit, ysplit_stride, slot, topk_w, Ys, \
+                                             ys_split, ys_stride, T, k, d, out)
+#define MOE_COMBINE(O)                  \
+  if (ysplit <= 2) MOE_COMBINE_NB(O, 2); \
+  else if (ysplit <= 8) MOE_COMBINE_NB(O, 8); \
+  else MOE_COMBINE_NB(O, 16)
+  if (bf16out) { MOE_COMBINE(true); }
+  else { MOE_COMBINE(false); }
 #undef MOE_COMBINE
 #undef MOE_COMBINE_NB
   return hipGetLastError();

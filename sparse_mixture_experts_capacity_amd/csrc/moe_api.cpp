@@ -141,7 +141,6 @@ struct Plan {
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
-  bool y_bf16 = false;           // routed down projection stores bf16 rows (one K part)
   bool small_route = false;      // top-k and dispatch in one workgroup
   bool blocked = false;          // GEMM1 writes H K-blocked; GEMM2 reads it so
   bool gather_x = false;         // GEMM1 reads a gathered, K-blocked copy of the token rows
@@ -230,6 +229,8 @@ int check(const moe_config_t* c) {
     return fail(MOE_EINVAL, "overflow = %d is not a moe_overflow_t", c->overflow);
   if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_PACKED)
     return fail(MOE_EINVAL, "weight_layout = %d is not a moe_weight_layout_t", c->weight_layout);
+  if (c->out_fp32 != 0 && c->out_fp32 != 1)
+    return fail(MOE_EINVAL, "out_fp32 = %d must be 0 or 1", c->out_fp32);
   if (isnan(c->capacity_factor) || c->capacity_factor > 1e6)
     return fail(MOE_EINVAL, "capacity_factor must be a number <= 1e6");
   if (c->T * static_cast<int64_t>(c->top_k) >= (int64_t(1) << 31))
@@ -405,10 +406,9 @@ int make_plan(const moe_config_t* c, Plan* p) {
   add(p->stats, sizeof(double) * 8, cur);
   add(p->H, es * p->rows_max * p->F, cur);
   add(p->Hs, es * p->T * p->S * p->F, cur);
-  // With one K part the routed down projection's rows are stored in bf16:
-  // half the bytes written by the GEMM and read by the combine.
-  p->y_bf16 = p->bf16 && p->ffn2_split == 1 && p->d % 8 == 0;
-  add(p->Y, (p->y_bf16 ? 2 : sizeof(float)) * p->ffn2_split * p->rows_max * p->d, cur);
+  // The routed down projection's rows stay fp32 (K parts summed by the
+  // combine), so the only roundings before the output's are the hidden rows'.
+  add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
   add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
   add(p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur);
   const size_t rr = p->overflow == MOE_OVERFLOW_REROUTE ? sizeof(int32_t) * p->TK : 0;
@@ -698,7 +698,6 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.narrow_n = p.bm == moe::kGroupedBMShort ? 1 : 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
-  g2.c_bf16 = p.y_bf16 ? 1 : 0;
   // Shared experts: all T token rows; GEMM1 lays the S experts side by side
   // along N into Hs [T, S*F]; GEMM2 contracts the S*F hidden columns against
   // the S stacked W2 blocks in one pass (their sum).
@@ -756,10 +755,10 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   }
   {
     Timed t("combine", s);
-    HIP_TRY(moe::launch_combine(at<void>(ws, p.Y), p.y_bf16, p.ffn2_split, p.rows_max * p.d,
+    HIP_TRY(moe::launch_combine(at<float>(ws, p.Y), p.ffn2_split, p.rows_max * p.d,
                                 at<int32_t>(ws, p.slot), w,
                                 p.S > 0 ? at<float>(ws, p.Ys) : nullptr, p.shared2_split,
-                                p.T * p.d, p.T, p.k, p.d, out, p.bf16, s));
+                                p.T * p.d, p.T, p.k, p.d, out, p.bf16 && !cfg->out_fp32, s));
   }
   if (stats) {
     rc = fill_stats(p, ws, s, stats, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.kcount));
@@ -790,7 +789,7 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   void* ws = cfg->workspace;
   moe::RouterBackward b{};
   b.x = x; b.Wg = W_gate; b.dout = dout;
-  b.Y = at<void>(ws, p.Y); b.ybf16 = p.y_bf16; b.ysplit = p.ffn2_split;
+  b.Y = at<void>(ws, p.Y); b.ysplit = p.ffn2_split;
   b.ystride = p.rows_max * p.d;
   b.rows = p.rows_max;
   b.vec4 = p.d % 4 == 0 && reinterpret_cast<uintptr_t>(dout) % (4 * (p.bf16 ? 2 : 4)) == 0;

@@ -60,6 +60,7 @@ def cfg(**kw):
     (dict(ffn_path=3), moe.MOE_EINVAL),
     (dict(capacity_factor=float("nan")), moe.MOE_EINVAL),
     (dict(capacity_factor=2e6), moe.MOE_EINVAL),
+    (dict(out_fp32=2), moe.MOE_EINVAL),
     (dict(T=2 ** 30, top_k=2), moe.MOE_EINVAL),
     (dict(d_model=96), moe.MOE_EUNSUPPORTED),
     (dict(d_ff=100), moe.MOE_EUNSUPPORTED),
@@ -113,11 +114,12 @@ def test_workspace_grows_with_tokens():
 
 
 def test_struct_layouts_match_the_header():
-    # moe_config_t ends with the overflow policy and the weight layout
-    # (which fills the padding after it); moe_stats_t with the
+    # moe_config_t ends with the overflow policy, the weight layout and the
+    # fp32-output flag; moe_stats_t with the
     # overflow counters (offsets as the C compiler lays them out on x86-64)
-    assert _lib.MoeConfig.overflow.offset == 88 and ctypes.sizeof(_lib.MoeConfig) == 96
+    assert _lib.MoeConfig.overflow.offset == 88 and ctypes.sizeof(_lib.MoeConfig) == 104
     assert _lib.MoeConfig.weight_layout.offset == 92
+    assert _lib.MoeConfig.out_fp32.offset == 96
     assert _lib.MoeStats.rounds.offset == 96 and ctypes.sizeof(_lib.MoeStats) == 104
 
 
@@ -183,11 +185,17 @@ def test_pack_weights_argument_checks():
 
 
 def test_missing_library_fails_loudly(tmp_path):
-    # no fallback: without libmoe.so the package refuses to import
+    # no fallback: a copy of the package without libmoe.so refuses to import
+    import shutil
     import subprocess
     import sys
-    env = dict(os.environ, MOE_LIB=str(tmp_path / "libmoe_missing.so"))
+    pkg = os.path.join(ROOT, "sparse_mixture_experts_capacity_amd")
+    dst = tmp_path / "sparse_mixture_experts_capacity_amd"
+    dst.mkdir()
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            shutil.copy(os.path.join(pkg, f), dst / f)
     r = subprocess.run([sys.executable, "-c", "import sparse_mixture_experts_capacity_amd"],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+                       cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
-    assert "ImportError" in r.stderr and "libmoe_missing.so" in r.stderr
+    assert "ImportError" in r.stderr and "libmoe.so is missing" in r.stderr
