@@ -223,6 +223,26 @@ int moe_forward(const void* x, const void* W_gate, const void* W1,
                 const void* W3, const void* W2, const moe_config_t* cfg,
                 void* out, moe_stats_t* stats);
 
+/* moe_forward for callers that cannot allocate device memory or bring a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, kernels and results (bit for bit)
+ * as moe_forward; cfg->workspace and cfg->workspace_bytes are ignored.
+ * Scratch is a fixed 64 MiB array in device memory (67108864 bytes), one per
+ * GPU the library runs on, kept until the process ends; its address is
+ * looked up on the first call on each device.  A layer whose
+ * moe_workspace_size(cfg) exceeds it is refused with MOE_EWORKSPACE before
+ * anything is enqueued (e.g. the Mixtral shape up to T = 256 tokens and the
+ * 160-expert DeepSeek shape up to T = 64 fit).  Nothing is allocated and,
+ * with stats == NULL, nothing but kernels is enqueued.  The kernels write
+ * every scratch byte they read, so nothing needs clearing between calls.
+ * Every call on one GPU shares that GPU's array: calls that may overlap in
+ * time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller; moe_router_backward cannot follow this entry
+ * point (it needs the forward's workspace). */
+int moe_forward_noalloc(const void* x, const void* W_gate, const void* W1,
+                        const void* W3, const void* W2, const moe_config_t* cfg,
+                        void* out, moe_stats_t* stats);
+
 /* Steps 1-3 (and 6 when stats != NULL): router scores, top-k, gates and
  * dispatch, without the experts.  Outputs (device, caller-owned):
  *   logits   [T, E] fp32  scores seen by top-k (bias included)

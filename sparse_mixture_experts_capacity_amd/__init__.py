@@ -23,7 +23,7 @@ from ._lib import (LIB, MoeConfig, MoeStats, MoeError, MOE_OK, MOE_EINVAL,  # no
 
 __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
-    "moe_workspace_size", "moe_capacity", "moe_forward", "moe_route",
+    "moe_workspace_size", "moe_capacity", "moe_forward", "moe_forward_noalloc", "moe_route",
     "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
     "moe_packed_weight_bytes", "moe_pack_weights",
     "moe_timing_enable", "moe_timing_only",
@@ -150,6 +150,20 @@ def moe_forward(x, W_gate, W1, W3, W2, cfg: MoeConfig, out,
                          ctypes.byref(cfg), _ptr(out),
                          ctypes.byref(st) if st is not None else None)
     _check(rc, "moe_forward")
+    return _stats_dict(st, counts, kept) if stats else None
+
+
+def moe_forward_noalloc(x, W_gate, W1, W3, W2, cfg: MoeConfig, out,
+                        stats: bool = False):
+    """moe_forward with the library's fixed scratch array instead of a
+    workspace (cfg.workspace is ignored): for callers that cannot allocate."""
+    st = counts = kept = None
+    if stats:
+        st, counts, kept = _stats_struct(cfg.n_experts)
+    rc = LIB.moe_forward_noalloc(_ptr(x), _ptr(W_gate), _ptr(W1), _ptr(W3), _ptr(W2),
+                                 ctypes.byref(cfg), _ptr(out),
+                                 ctypes.byref(st) if st is not None else None)
+    _check(rc, "moe_forward_noalloc")
     return _stats_dict(st, counts, kept) if stats else None
 
 

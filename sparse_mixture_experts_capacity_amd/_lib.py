@@ -82,6 +82,7 @@ def _load():
         "moe_workspace_size": (ctypes.c_size_t, [CFG]),
         "moe_capacity": (ctypes.c_int64, [CFG]),
         "moe_forward": (ctypes.c_int, [P, P, P, P, P, CFG, P, ST]),
+        "moe_forward_noalloc": (ctypes.c_int, [P, P, P, P, P, CFG, P, ST]),
         "moe_route": (ctypes.c_int, [P, P, CFG, P, P, P, P, P, P, P, ST]),
         "moe_route_logits": (ctypes.c_int, [P, CFG, P, P, P, P, P, P, ST]),
         "moe_aux_loss": (ctypes.c_int, [P, P, CFG, ctypes.POINTER(ctypes.c_double)]),

@@ -584,12 +584,12 @@ int fill_stats(const Plan& p, void* ws, hipStream_t s, moe_stats_t* st,
                               counts_dev, kcount_dev, p.T, p.k, p.E, at<double>(ws, p.stats), s));
   }
   double out[8];
-  std::vector<int32_t> cnt(p.E), kc(p.E);
+  int32_t cnt[moe::kMaxExperts] = {}, kc[moe::kMaxExperts] = {};
   HIP_TRY(hipMemcpyAsync(out, at<double>(ws, p.stats), sizeof(double) * 6, hipMemcpyDeviceToHost, s));
   if (counts_dev)
-    HIP_TRY(hipMemcpyAsync(cnt.data(), counts_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(cnt, counts_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
   if (kcount_dev)
-    HIP_TRY(hipMemcpyAsync(kc.data(), kcount_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(kc, kcount_dev, sizeof(int32_t) * p.E, hipMemcpyDeviceToHost, s));
   HIP_TRY(hipStreamSynchronize(s));
   st->aux_loss = out[0];
   st->aux_loss_kept = out[1];
@@ -613,6 +613,52 @@ int fill_stats(const Plan& p, void* ws, hipStream_t s, moe_stats_t* st,
   }
   if (p.overflow == MOE_OVERFLOW_REROUTE) st->rerouted = st->overflowed - st->dropped;
   return MOE_OK;
+}
+
+// ------------------------------------------------------- allocation-free
+// Scratch of moe_forward_noalloc, for callers that cannot allocate (code
+// under HIP graph capture, tight serving loops, harnesses that forbid
+// hipMalloc): one fixed array in device memory, which every GPU the library
+// runs on holds until the process ends.  In host code `scratch` names a host
+// stand-in, not the device array: kernels and copies only ever get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr after a failure
+// (moe_last_error says why).
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(MOE_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(MOE_EHIP, "device %d is beyond the %d devices the scratch table covers", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || p == nullptr) {
+      fail(MOE_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+           hipGetErrorString(r));
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
 }
 
 }  // namespace
@@ -766,6 +812,29 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   }
   g_err.clear();
   return MOE_OK;
+}
+
+int moe_forward_noalloc(const void* x, const void* W_gate, const void* W1, const void* W3,
+                        const void* W2, const moe_config_t* cfg, void* out, moe_stats_t* stats) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.total > kNoAllocScratchBytes)
+    return fail(MOE_EWORKSPACE,
+                "this layer needs %zu bytes of scratch; moe_forward_noalloc holds %zu "
+                "(use moe_forward with a workspace)", p.total, kNoAllocScratchBytes);
+  moe_config_t c = *cfg;
+  c.workspace = nullptr;
+  c.workspace_bytes = 0;
+  if (p.T > 0) {
+    if (!x || !W_gate || !W1 || !W3 || !W2 || !out)
+      return fail(MOE_EINVAL, "x, W_gate, W1, W3, W2 and out must be non-NULL");
+    void* ws = scratch_on_current_device();
+    if (!ws) return MOE_EHIP;
+    c.workspace = ws;
+    c.workspace_bytes = kNoAllocScratchBytes;
+  }
+  return moe_forward(x, W_gate, W1, W3, W2, &c, out, stats);
 }
 
 int moe_router_backward(const void* x, const void* W_gate, const void* dout, double aux_coef,

@@ -199,3 +199,18 @@ def test_missing_library_fails_loudly(tmp_path):
                        cwd=str(tmp_path), capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libmoe.so is missing" in r.stderr
+
+
+def test_noalloc_refuses_layers_beyond_its_scratch():
+    # checked before the scratch array is looked up, so no GPU is touched:
+    # the Mixtral-shaped prefill layer needs far more than the 64 MiB
+    big = cfg(T=2048, d_model=4096, d_ff=14336, n_experts=8, top_k=2)
+    assert moe.moe_workspace_size(big) > 64 << 20
+    fake = 256   # never dereferenced: the size check fails first
+    rc = moe.LIB.moe_forward_noalloc(fake, fake, fake, fake, fake, ctypes.byref(big), fake, None)
+    assert rc == moe.MOE_EWORKSPACE
+    assert "moe_forward_noalloc holds 67108864" in moe.moe_last_error()
+    # invalid configurations are refused as by moe_forward
+    bad = cfg(top_k=0)
+    assert moe.LIB.moe_forward_noalloc(fake, fake, fake, fake, fake, ctypes.byref(bad), fake,
+                                       None) == moe.MOE_EINVAL
