@@ -79,6 +79,10 @@ def parse():
                     help="after the timed steps, this many more with L2 and the 256 MB "
                          "Infinity Cache flushed before each (reported separately)")
     ap.add_argument("--flush-mib", type=int, default=512)
+    ap.add_argument("--decode-legs", default=None,
+                    help="comma-separated token counts of extra decode steps timed on the same "
+                         "weights (no capacity limit; default 1,64 for the Mixtral-shaped "
+                         "prefill workload, none otherwise; 'none' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one device copy of this many MiB before the steps "
                          "(a kernel of known traffic for scaling HBM counters)")
@@ -178,6 +182,72 @@ def cpu_baseline(w, inp, n_tokens: int):
                         f"seeded sampled tokens, fp64 NumPy on the host; value = "
                         f"{len(toks)} tokens / {dt:.2f} s wall"),
                 routing_seconds=dt_route, seconds=dt)
+
+
+def decode_leg(moe, w, inp, weights, packed, T, stream, args, dom):
+    """One decode batch of T tokens on workload w's weights (no capacity
+    limit): ms per step (wall clock over K steps), the routed SwiGLU GEMM's
+    time from HIP events in those steps, HBM fractions of the GEMM and of
+    the layer, and a graph replay of the step."""
+    import torch
+    dev = "cuda"
+    wd = w.with_(T=T, capacity_factor=0.0)
+    cfg = moe.make_config(T=T, d_model=w.d, d_ff=w.F, n_experts=w.E, top_k=w.k,
+                          n_shared=w.S, gating=w.gating, renormalize=w.renormalize,
+                          capacity_factor=0.0, dtype=w.dtype, logit_bias=inp.bias,
+                          stream=stream, overflow=w.overflow,
+                          weight_layout=moe.WEIGHTS_PACKED if packed else moe.WEIGHTS_ROW_MAJOR)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    x = inp.x[:T].contiguous()
+    out = torch.empty((T, w.d), dtype=w.torch_dtype, device=dev)
+
+    def step(stats=False):
+        return moe.moe_forward(x, inp.W_gate, *weights, cfg, out, stats=stats)
+
+    st = step(stats=True)
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+    moe.moe_timing_reset()
+    moe.moe_timing_only(dom)
+    moe.moe_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    stream.synchronize()
+    t1 = time.perf_counter()
+    moe.moe_timing_enable(False)
+    n_dom, t_dom = moe.moe_timing_read().get(dom, (0, 0.0))
+    ms = (t1 - t0) * 1e3 / args.steps
+    dom_ms = t_dom / n_dom if n_dom else float("nan")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+    del g
+    kept = int(sum(st["kept"]))
+    hit = int(sum(1 for c in st["kept"] if c > 0))
+    work = algorithmic_work(wd, kept, hit)
+    g1_bytes = work["gemm1_bytes"] + work["gemm1_io_bytes"]
+    return dict(
+        workload=f"{w.name} weights, first {T} token rows, no capacity limit",
+        T=T, ms_per_step=ms, tokens_per_s=T / (ms * 1e-3), graph_ms_per_step=graph_ms,
+        experts_hit=hit, kept_assignments=kept,
+        layer_bytes=work["bytes"],
+        layer_frac_of_hbm=work["bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        layer_frac_of_hbm_graph=work["bytes"] / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        dominant_kernel=dom, dominant_kernel_ms=dom_ms, dominant_kernel_bytes=g1_bytes,
+        dominant_kernel_frac_of_hbm=g1_bytes / (dom_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        kernel_ms_source="HIP events around this kernel in each timed step")
 
 
 def main():
@@ -346,6 +416,19 @@ def main():
                         kernels={n: (t / c if c else 0.0) for n, (c, t) in ckern.items()})
             del flush, sink
 
+        # Decode legs: the same expert weights (and the first T token rows)
+        # at decode batch sizes with no capacity limit, each timed like the
+        # main step (only the routed SwiGLU GEMM bracketed by events), plus a
+        # graph replay of the step.  Not part of the headline figure.
+        legs = {}
+        leg_ts = args.decode_legs
+        if leg_ts is None:
+            leg_ts = "1,64" if w.name == "mixtral_prefill" else ""
+        if leg_ts.strip().lower() == "none":
+            leg_ts = ""
+        for T in [int(v) for v in leg_ts.split(",") if v.strip()]:
+            legs[f"t{T}"] = decode_leg(moe, w, inp, (W1, W3, W2), packed, T, stream, args, dom)
+
     ms = (t1 - t0) * 1e3 / args.steps
     kept = int(sum(st["kept"]))
     hit = int(sum(1 for c in st["kept"] if c > 0))
@@ -443,6 +526,8 @@ def main():
     if graph is not None:
         graph["tokens_per_s"] = w.T / (graph["ms_per_step"] * 1e-3)
         res["graph"] = graph
+    if legs:
+        res["decode"] = legs
     if bwd is not None:
         # The gate pass streams the kept expert rows and dout once: it is
         # bound by HBM.  Algorithmic bytes count each row in the layer's

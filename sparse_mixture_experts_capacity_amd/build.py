@@ -22,13 +22,15 @@ ARCH = "gfx950"
 
 SOURCES = ["routing.hip", "ffn_grouped.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 
+# MFMA accumulators in architectural VGPRs: the MFMA kernels fit in 256
+# VGPRs, and the AGPR form makes the compiler copy accumulators between the
+# two files every loop iteration.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_VGPR_FORM = set()
+
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-mcode-object-version=5",
-    # MFMA accumulators in architectural VGPRs: the MFMA kernels fit in 256
-    # VGPRs, and the AGPR form makes the compiler copy accumulators between
-    # the two files every loop iteration.
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # Packed fp32 instructions are kept out of generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
@@ -38,7 +40,8 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [] if src in NO_VGPR_FORM else VGPR_FORM
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -40,226 +40,11 @@
 // The XCD-aware block order keeps consecutive logical tiles on one XCD; the
 // logical order runs M-tiles fastest, so the M-tiles sharing a weight tile
 // run together on one XCD and read it from HBM once.
-#include <algorithm>
-#include <type_traits>
-
-#include "kernels.h"
+#include "ffn_dma.h"
 
 namespace moe {
 namespace {
-
-struct TileCoords {
-  int group;   // expert index relative to group_base (routed) or 0
-  int row0;
-  int nrows;
-  int ntile;   // N-tile within the group
-  int ngroup;  // N-group (shared experts laid along N)
-  int kpart;   // part of a split K (static tiling)
-  bool valid;
-};
-
-// Block -> (expert, N-tile, M-tile).  The logical tile order runs expert by
-// expert, N-tile by N-tile, with the expert's M-tiles fastest, so a window of
-// consecutive logical tiles is a compact (all M-tiles) x (a few N-tiles) block
-// of one expert: its weight tiles and its token rows are each fetched once
-// into L2 and shared.  Hardware deals workgroups to the 8 XCDs round-robin
-// (block p -> XCD p % 8); each XCD takes a contiguous eighth of the logical
-// tiles that actually exist (their count is read from the device tile list),
-// so the XCDs stay balanced whatever the routing.
-template <int TBM>
-__device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
-                                                  int /*nblocks*/) {
-  TileCoords tc{0, 0, 0, 0, 0, 0, false};
-  const int ntn_all = ntn * p.ngroups_n;
-  const int mtiles = p.tiles ? *p.ntiles : (p.static_rows + TBM - 1) / TBM;
-  const int ks = p.ksplit;
-  const int total = mtiles * ntn_all * ks;
-  const int per = (total + 7) >> 3;
-  const int x = blockIdx.x & 7;
-  const int i = blockIdx.x >> 3;
-  if (i >= per) return tc;
-  const int LK = x * per + i;
-  if (LK >= total) return tc;
-  tc.kpart = LK % ks;   // K parts of one tile are adjacent: they share A rows
-  const int L = LK / ks;
-  int m, n_all;
-  if (p.tiles) {
-    // expert e owns logical tiles [tstart[e] * ntn_all, tstart[e+1] * ntn_all)
-    int lo = 0, hi = p.n_experts;            // find e with tstart[e]*ntn_all <= L
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tstart[mid] * ntn_all <= L) lo = mid; else hi = mid;
-    }
-    const int t0 = p.tstart[lo];
-    const int mt = p.tstart[lo + 1] - t0;
-    const int local = L - t0 * ntn_all;
-    n_all = local / mt;
-    m = t0 + local % mt;
-    const Tile t = p.tiles[m];
-    tc.group = t.group;
-    tc.row0 = t.row0;
-    tc.nrows = t.nrows;
-  } else {
-    n_all = L / mtiles;
-    m = L % mtiles;
-    tc.row0 = m * TBM;
-    tc.nrows = min(TBM, p.static_rows - tc.row0);
-  }
-  tc.ngroup = n_all / ntn;
-  tc.ntile = n_all % ntn;
-  tc.valid = tc.nrows > 0;
-  return tc;
-}
-
-// ===========================================================================
-// bf16 MFMA kernel, gfx950 data path
-//
-// Global -> LDS with global_load_lds_dwordx4 (the load unit writes LDS
-// directly: no staging registers, no LDS write instructions) into an
-// NS-deep ring of stages, so NS-1 K steps of loads are in flight while one is
-// computed.  The weight tile stays N-contiguous in LDS, exactly as it sits in
-// memory, and the MFMA B fragments are read with ds_read_b64_tr_b16, which
-// transposes 16-bit elements across each 16-lane group: source lane 4q+r
-// supplies columns 4r..4r+3 of row k_q, and result lane i receives column i
-// of rows k_0..k_3.  Two such reads give a lane the 8 consecutive k values of
-// one column that v_mfma_f32_16x16x32_bf16 takes.
-//
-// LDS layouts (no padding; XOR swizzles keep every read conflict-free):
-//   A stage: BM rows x 2*BK bytes; 16-byte chunk c of row m is stored at
-//            a_chunk(m, c) (an XOR of c with low bits of m).
-//   B stage: BK rows x 2*BN bytes; 32-byte segment s (16 columns) of row k
-//            sits at segment s ^ ((k & 3) | ((k >> 1) & 4)).
-//
-// The shape is a compile-time configuration: M-tile BM, B-tile width BN
-// (SwiGLU: BN/2 columns each of W1 and W3), K step BK, wavefronts NW (WM
-// along M), NS stages.  Configurations with at most 80 KB of LDS run two
-// workgroups per CU, so one workgroup's barrier, tile set-up and epilogue
-// overlap the other's MFMAs.
-// ===========================================================================
 namespace dma {
-
-template <int BM_, int BN_, int BK_, int NW_, int WM_, int NS_>
-struct Shape {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, NW = NW_, WM = WM_, NS = NS_;
-  static constexpr int WN = NW / WM;
-  static constexpr int WROWS = BM / WM;
-  static constexpr int WCOLS = BN / WN;
-  static constexpr int MI = WROWS / 16;              // MFMA tiles per wavefront
-  static constexpr int NJ = WCOLS / 16;
-  static constexpr int HALVES = BK / 32;             // 32-deep MFMA steps per stage
-  static constexpr int A_ROW = 2 * BK;               // bytes per A row
-  static constexpr int CA = BK / 8;                  // 16-byte chunks per A row
-  static constexpr int B_ROW = 2 * BN;               // bytes per B row
-  static constexpr int A_STAGE = BM * A_ROW;
-  static constexpr int B_STAGE = BK * B_ROW;
-  static constexpr int STAGE = A_STAGE + B_STAGE;
-  static constexpr int A_ROWS_PER_LOAD = 1024 / A_ROW;   // one 64-lane x 16 B load
-  static constexpr int B_ROWS_PER_LOAD = 1024 / B_ROW;
-  static constexpr int A_LOADS = A_STAGE / 1024 / NW;    // per thread per stage
-  static constexpr int B_LOADS = B_STAGE / 1024 / NW;
-  static constexpr int LOADS = A_LOADS + B_LOADS;
-  static constexpr int LDS = NS * STAGE;
-  static constexpr int BLOCKS_PER_CU = LDS <= 80 * 1024 ? 2 : 1;
-  static_assert(LDS <= 160 * 1024, "LDS");
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && NJ % 2 == 0 && MI >= 1, "shape");
-  static_assert(A_STAGE % (1024 * NW) == 0 && B_STAGE % (1024 * NW) == 0, "loads");
-  static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(BN / 16 <= 16 && BN >= 128, "B segments");
-  static_assert(3 * LOADS < 64, "vmcnt");
-};
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Stored position of 16-byte chunk c of A row m.  With 8 chunks per row
-// (BK = 64): c ^ (m & 7) ^ ((m >> 3) & 1); with 4 (BK = 32):
-// c ^ (m & 3) ^ ((m >> 2) & 3).  Either way 16 consecutive rows read at one
-// chunk hit 16 different 16-byte bank groups.
-template <int CA>
-__device__ __forceinline__ int a_chunk(int m, int c) {
-  if constexpr (CA == 8) return c ^ (m & 7) ^ ((m >> 3) & 1);
-  return c ^ (m & 3) ^ ((m >> 2) & 3);
-}
-__device__ __forceinline__ int b_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Wait until at most `later` stages of LOADS transfers each are in flight.
-template <int LOADS>
-__device__ __forceinline__ void wait_stages(int later) {
-  if (later >= 2) wait_vmcnt<2 * LOADS>();
-  else if (later == 1) wait_vmcnt<LOADS>();
-  else wait_vmcnt<0>();
-}
-
-// s_waitcnt: at most N vector-memory operations and no LDS operation of this
-// wavefront still in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-// ... until at most `later` (0..3) stages of LOADS transfers each remain.
-template <int LOADS>
-__device__ __forceinline__ void wait_stages_lgkm0(int later) {
-  if (later >= 3) wait_vmcnt_lgkm0<3 * LOADS>();
-  else if (later == 2) wait_vmcnt_lgkm0<2 * LOADS>();
-  else if (later == 1) wait_vmcnt_lgkm0<LOADS>();
-  else wait_vmcnt_lgkm0<0>();
-}
-
-// First B-tile column of MFMA tile j of wavefront column wn.
-template <class S, bool SWIGLU>
-__device__ __forceinline__ int bcol_of(int j, int wn) {
-  if constexpr (SWIGLU) {
-    constexpr int H = S::NJ / 2;   // first half: W1 columns, second half: W3
-    return (j < H) ? (wn * (S::WCOLS / 2) + j * 16)
-                   : (S::BN / 2 + wn * (S::WCOLS / 2) + (j - H) * 16);
-  }
-  return wn * S::WCOLS + j * 16;
-}
-
-// First tile row of MFMA row fragment i (16 rows) of wavefront row wm.  The
-// fragments are dealt to the WM wavefront rows in turn, so the rows of a
-// short tile (an expert's last) spread evenly over the wavefronts, and with
-// them over the SIMDs, when the fragments past the tile's end are skipped.
-template <class S>
-__device__ __forceinline__ int frag_row(int wm, int i) {
-  return (i * S::WM + wm) * 16;
-}
-
-// f(integral_constant<int, n>) for a run-time n in 0..N.
-template <int N, class F>
-__device__ __forceinline__ void with_count(int n, F& f) {
-  if constexpr (N == 0) {
-    f(std::integral_constant<int, 0>{});
-  } else {
-    if (n >= N) f(std::integral_constant<int, N>{});
-    else with_count<N - 1>(n, f);
-  }
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
-}
-
-// One 16-byte-per-lane global -> LDS transfer: lane i's 16 bytes from src land
-// at LDS byte address lds + 16 i.  Written as asm so that the compiler, which
-// cannot tell these LDS writes apart from the LDS reads of other stages, does
-// not wait for them before every LDS read; the kernel waits on vmcnt itself.
-// The instruction has no result register.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
 
 template <bool SWIGLU, class S>
 // The second launch bound is the minimum wavefronts per SIMD: BLOCKS_PER_CU
@@ -283,63 +68,8 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   const int n0 = tc.ntile * NOUT;
 
   // ---- DMA sources ---------------------------------------------------------
-  // A: load i of this wavefront fills rows (wave*A_LOADS + i)*A_ROWS_PER_LOAD
-  // onward; lane -> row + lane/CA, stored chunk lane%CA.  Rows past the
-  // tile's end repeat its first row (their results are not stored).  In the
-  // K-blocked layout (a_block_rows = R > 0) element (row, k) sits at
-  // ((k / 32) * R + row) * 32 + k % 32, so one K step of a tile's rows is a
-  // contiguous run of memory.
-  const uint16_t* A = static_cast<const uint16_t*>(p.A);
-  const uint16_t* asrc[S::A_LOADS];
-#pragma unroll
-  for (int i = 0; i < S::A_LOADS; ++i) {
-    const int r = (wave * S::A_LOADS + i) * S::A_ROWS_PER_LOAD + lane / S::CA;
-    const int rr = tc.row0 + (r < tc.nrows ? r : 0);
-    const int sc = a_chunk<S::CA>(r, lane % S::CA) * 8;   // source column in the step
-    if (p.a_block_rows > 0) {
-      asrc[i] = A + ((sc >> 5) * p.a_block_rows + rr) * 32 + (sc & 31);
-    } else {
-      const int64_t src = p.perm ? static_cast<int64_t>(p.perm[rr] / p.topk) : rr;
-      asrc[i] = A + src * p.lda + sc;
-    }
-  }
-  // element offset of K step k0 along A (a multiple of 32)
-  const int64_t a_kstride = p.a_block_rows > 0 ? p.a_block_rows : 1;
-  // B: load i fills rows (wave*B_LOADS + i)*B_ROWS_PER_LOAD onward; lane ->
-  // row + lane/(BN/8), stored 16-byte chunk q = lane%(BN/8), which is half
-  // (q&1) of stored segment q/2.  Columns past N read column 0 (their
-  // outputs are never stored).  With packed weights a step's rows of one
-  // tile are whole 32-row blocks: one contiguous run per block instead of a
-  // short piece of every row.  Either way the step advances by K-step x ldb.
-  constexpr int BCH = BN / 8;                 // 16-byte chunks per B row
-  const uint16_t* bsrc[S::B_LOADS];
-#pragma unroll
-  for (int i = 0; i < S::B_LOADS; ++i) {
-    const int kr = (wave * S::B_LOADS + i) * S::B_ROWS_PER_LOAD + lane / BCH;
-    const int q = lane % BCH;
-    const int seg = (q >> 1) ^ b_swz(kr);
-    const int n = seg * 16 + (q & 1) * 8;
-    const uint16_t* base;
-    int col;
-    if constexpr (SWIGLU) {
-      base = static_cast<const uint16_t*>(n < BN / 2 ? p.B : p.B3);
-      col = n0 + (n & (BN / 2 - 1));
-    } else {
-      base = static_cast<const uint16_t*>(p.B);
-      col = n0 + n;
-    }
-    if (col >= p.N) col = 0;
-    int64_t bo;
-    if (p.b_block_cols) {
-      // packed: row kr of the step lies in block row kr / 32 (BK = 64 spans
-      // two), column col in block col / W
-      const int w = p.b_block_cols;
-      bo = static_cast<int64_t>(kr >> 5) * 32 * p.ldb + ((col / w) * 32 + (kr & 31)) * w + col % w;
-    } else {
-      bo = static_cast<int64_t>(kr) * p.ldb + col;
-    }
-    bsrc[i] = base + boff + bo;
-  }
+  TileSources<SWIGLU, S> src;
+  src.init(p, tc, wave, lane, n0, boff);
 
   // LDS byte address of this wavefront's destinations in stage 0
   // (wave-uniform: M0 takes it).
@@ -352,15 +82,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   const int kbase = kb0 * BK;
   // step: K step to load; stage: its ring slot (step % NS).
   auto issue = [&](int step, int stage) __attribute__((always_inline)) {
-    const uint32_t sb = lds0 + stage * S::STAGE;
-    const int k0 = kbase + step * BK;
-#pragma unroll
-    for (int i = 0; i < S::A_LOADS; ++i)
-      dma16(asrc[i] + k0 * a_kstride, sb + (wave_u * S::A_LOADS + i) * 1024);
-    const int64_t kb = static_cast<int64_t>(k0) * p.ldb;
-#pragma unroll
-    for (int i = 0; i < S::B_LOADS; ++i)
-      dma16(bsrc[i] + kb, sb + S::A_STAGE + (wave_u * S::B_LOADS + i) * 1024);
+    src.issue(lds0 + stage * S::STAGE, kbase + step * BK, wave_u);
   };
 
   f32x4 acc[MI][NJ];
@@ -369,11 +91,6 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Fragment addressing (bytes within a stage).
-  const int g = lane >> 4;         // k block of 8 within a 32-k MFMA step
-  const int i16 = lane & 15;
-  const int tq = i16 >> 2, tr = i16 & 3;
-
   // One 32-deep half of a stage for this wavefront: MI A fragments
   // (ds_read_b128) and NJ B fragments (two transposing reads each).
   struct Frags {
@@ -381,20 +98,10 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
     bf16x8 b[NJ];
   };
   auto rd_a = [&](int stage, int h, int i) __attribute__((always_inline)) -> bf16x8 {
-    const char* sb = smem + stage * S::STAGE;
-    const int m = frag_row<S>(wm, i) + i16;
-    return *reinterpret_cast<const bf16x8*>(sb + m * S::A_ROW + a_chunk<S::CA>(m, h * 4 + g) * 16);
+    return frag_a<S>(smem + stage * S::STAGE, wm, h, i, lane);
   };
   auto rd_b = [&](int stage, int h, int j) __attribute__((always_inline)) -> bf16x8 {
-    const char* sb = smem + stage * S::STAGE;
-    const int k_lo = h * 32 + g * 8 + tq;   // rows of the two transposing reads
-    const int k_hi = k_lo + 4;
-    const int sg = bcol_of<S, SWIGLU>(j, wn) >> 4;
-    const char* blo = sb + S::A_STAGE + k_lo * S::B_ROW + ((sg ^ b_swz(k_lo)) * 32) + tr * 8;
-    const char* bhi = sb + S::A_STAGE + k_hi * S::B_ROW + ((sg ^ b_swz(k_hi)) * 32) + tr * 8;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)blo);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)bhi);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return frag_b<S, SWIGLU>(smem + stage * S::STAGE, wn, h, j, lane);
   };
   // MV: row fragments of this wavefront that hold tile rows (a constant of
   // the specialised pipeline below); the others are neither read nor
@@ -506,48 +213,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   with_count<MI>(mv, run);
 
   // ---- epilogue -----------------------------------------------------------
-  // MFMA 16x16 output: lane holds rows 4*(lane/16) + r, column lane % 16.
-  const int64_t cgo = static_cast<int64_t>(tc.ngroup) * p.c_group_col;
-  if constexpr (SWIGLU) {
-    uint16_t* H = static_cast<uint16_t*>(p.C);
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = frag_row<S>(wm, i) + (lane >> 4) * 4 + r;
-        if (rl >= tc.nrows) continue;
-        const int64_t row = tc.row0 + rl;
-#pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
-          const int col = n0 + wn * (S::WCOLS / 2) + j * 16 + (lane & 15);
-          if (col < p.N) {
-            const uint16_t h = f32_to_bf16(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
-            const int64_t c = cgo + col;
-            if (p.c_block_rows > 0)
-              H[((c >> 5) * p.c_block_rows + row) * 32 + (c & 31)] = h;
-            else
-              H[row * p.ldc + c] = h;
-          }
-        }
-      }
-    }
-  } else {
-    float* Y = static_cast<float*>(p.C) + tc.kpart * p.c_split;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rl = frag_row<S>(wm, i) + (lane >> 4) * 4 + r;
-        if (rl >= tc.nrows) continue;
-        float* yrow = Y + static_cast<int64_t>(tc.row0 + rl) * p.ldc + cgo;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int col = n0 + wn * S::WCOLS + j * 16 + (lane & 15);
-          if (col < p.N) yrow[col] = acc[i][j][r];
-        }
-      }
-    }
-  }
+  store_tile<SWIGLU, S>(p, tc, acc, wm, wn, lane, n0);
 }
 
 // Shapes in use (the M-tile the host chooses picks one):
@@ -712,21 +378,12 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t* __rest
   }
 }
 
-template <typename Kern>
-hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, int waves = 4) {
-  const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n * g.ksplit;
-  if (logical <= 0) return hipSuccess;
-  const int nblocks = static_cast<int>((logical + 7) / 8 * 8);
-  kern<<<nblocks, 64 * waves, 0, s>>>(g, ntn, nblocks);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 template <bool SWIGLU, class S>
 hipError_t launch_bf16_shape(const GroupedGemm& g, hipStream_t s) {
   const int cols = SWIGLU ? S::BN / 2 : S::BN;
-  return launch_grid(dma::grouped_bf16_dma_kernel<SWIGLU, S>, g, (g.N + cols - 1) / cols, s, S::NW);
+  return dma::launch_grid(dma::grouped_bf16_dma_kernel<SWIGLU, S>, g, (g.N + cols - 1) / cols, s, S::NW);
 }
 template <bool SWIGLU>
 hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
@@ -765,10 +422,10 @@ hipError_t launch_grouped_plain_bf16(const GroupedGemm& g, hipStream_t s) {
   return launch_bf16<false>(g, s);
 }
 hipError_t launch_grouped_swiglu_f32(const GroupedGemm& g, hipStream_t s) {
-  return launch_grid(grouped_f32_kernel<true>, g, (g.N + FBN - 1) / FBN, s);
+  return dma::launch_grid(grouped_f32_kernel<true>, g, (g.N + FBN - 1) / FBN, s);
 }
 hipError_t launch_grouped_plain_f32(const GroupedGemm& g, hipStream_t s) {
-  return launch_grid(grouped_f32_kernel<false>, g, (g.N + FBN - 1) / FBN, s);
+  return dma::launch_grid(grouped_f32_kernel<false>, g, (g.N + FBN - 1) / FBN, s);
 }
 
 }  // namespace moe
