@@ -312,6 +312,29 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout,
                         const moe_config_t* cfg, float* dlogits,
                         float* dW_gate, float* dbias, float* dx);
 
+/* Training side of the router ([Routing guide] "Plain explanation" para 4:
+ * the router's entropy is kept high early in training, so tokens try many
+ * experts, and lowered later; "Key insights" item 3: the trend of the
+ * load-balancing loss is one of the quantities to watch).  Host only: no
+ * GPU is touched.
+ *
+ * moe_entropy_coef: the weight of the mean router entropy H_tok in the loss
+ * (the entropy_coef of moe_router_backward) at `step` of `total_steps`:
+ * `high` at step 0, falling in a straight line to `low` at step
+ * total_steps - 1, held at `high` before and at `low` after; `low` when
+ * total_steps <= 1.  The pages give the direction only; the straight line
+ * is the plainest shape with it.  NaN for non-finite high or low. */
+double moe_entropy_coef(int64_t step, int64_t total_steps, double high, double low);
+
+/* moe_lb_trend: trend of a series of load-balancing losses (the aux_loss
+ * of successive forward calls, oldest first; host array of n values):
+ * *slope = the least-squares slope of value against step number, per step
+ * (sum (i - i_mean)(v_i - v_mean) / sum (i - i_mean)^2), *mean = the mean
+ * value.  Negative while the load evens out, near 0 once it has settled.
+ * MOE_EINVAL for n < 2, a NULL pointer or a non-finite value (outputs
+ * untouched). */
+int moe_lb_trend(const double* values, int64_t n, double* slope, double* mean);
+
 /* Reason for the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 

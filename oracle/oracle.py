@@ -549,6 +549,40 @@ def router_backward(x: np.ndarray, W_gate: np.ndarray, fwd: dict,
 
 
 # ---------------------------------------------------------------------------
+# Training-side quantities around the router.  [Routing guide] "Plain
+# explanation" paragraph 4: the router's entropy is kept high early in
+# training and lowered later; "Key insights" item 3 names the trend of the
+# load-balancing loss among the quantities to watch.
+# ---------------------------------------------------------------------------
+def entropy_schedule(step: int, total_steps: int, high: float, low: float) -> float:
+    """Weight of the mean router entropy in the loss at ``step``: ``high`` at
+    step 0, falling in a straight line to ``low`` at step total_steps - 1,
+    held at the ends outside that range.  The page gives only the direction
+    (high early, lower later); the straight line is the plainest shape with
+    it.  A run of one step uses ``low``."""
+    if total_steps <= 1:
+        return float(low)
+    s = min(max(int(step), 0), int(total_steps) - 1)
+    return float(high) + (float(low) - float(high)) * s / (int(total_steps) - 1)
+
+
+def load_balance_trend(values: Sequence[float]) -> dict:
+    """Trend of a series of load-balancing losses, one per training step:
+    the least-squares slope of value against step number (per step) and the
+    mean.  Written out as the normal equations of the straight-line fit:
+    slope = sum((i - i_mean)(v_i - v_mean)) / sum((i - i_mean)^2)."""
+    n = len(values)
+    if n < 2:
+        raise ValueError("a trend needs at least two values")
+    v = [float(a) for a in values]
+    i_mean = (n - 1) / 2.0
+    v_mean = sum(v) / n
+    num = sum((i - i_mean) * (v[i] - v_mean) for i in range(n))
+    den = sum((i - i_mean) ** 2 for i in range(n))
+    return dict(slope=num / den, mean=v_mean, last=v[-1], n=n)
+
+
+# ---------------------------------------------------------------------------
 # Brute-force top-k, used only to pin topk_select on tiny inputs.
 # ---------------------------------------------------------------------------
 def brute_topk_set(row: Sequence[float], k: int) -> tuple:

@@ -25,7 +25,8 @@ __all__ = [
     "MoeConfig", "MoeStats", "MoeError", "make_config", "moe_check_config",
     "moe_workspace_size", "moe_capacity", "moe_forward", "moe_forward_noalloc", "moe_route",
     "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
-    "moe_packed_weight_bytes", "moe_pack_weights",
+    "moe_packed_weight_bytes", "moe_pack_weights", "moe_entropy_coef", "moe_lb_trend",
+    "LoadBalanceTrend",
     "moe_timing_enable", "moe_timing_only",
     "moe_timing_reset", "moe_timing_read", "Workspace",
 ]
@@ -227,6 +228,52 @@ def moe_pack_weights(W1, W3, W2, cfg: MoeConfig, W1p, W3p, W2p) -> None:
     cfg.stream)."""
     _check(LIB.moe_pack_weights(_ptr(W1), _ptr(W3), _ptr(W2), ctypes.byref(cfg), _ptr(W1p),
                                 _ptr(W3p), _ptr(W2p)), "moe_pack_weights")
+
+
+def moe_entropy_coef(step: int, total_steps: int, high: float, low: float) -> float:
+    """Weight of the mean router entropy in the loss at ``step`` (include/moe.h)."""
+    return float(LIB.moe_entropy_coef(int(step), int(total_steps), float(high), float(low)))
+
+
+def moe_lb_trend(values) -> tuple:
+    """(slope per step, mean) of a series of load-balancing losses, oldest
+    first (include/moe.h)."""
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64))
+    slope, mean = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(LIB.moe_lb_trend(v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(v.size),
+                            ctypes.byref(slope), ctypes.byref(mean)), "moe_lb_trend")
+    return slope.value, mean.value
+
+
+class LoadBalanceTrend:
+    """The aux losses of the last ``window`` training steps (``add`` one per
+    step, e.g. ``stats["aux_loss"]`` of the forward); ``slope()`` and
+    ``mean()`` come from moe_lb_trend over that window."""
+
+    def __init__(self, window: int = 100):
+        if window < 2:
+            raise ValueError("window must be at least 2")
+        from collections import deque
+        self.window = int(window)
+        self._vals = deque(maxlen=self.window)
+        self.steps = 0
+
+    def add(self, aux_loss: float) -> None:
+        self._vals.append(float(aux_loss))
+        self.steps += 1
+
+    def __len__(self) -> int:
+        return len(self._vals)
+
+    def last(self):
+        return self._vals[-1] if self._vals else None
+
+    def slope(self):
+        return moe_lb_trend(list(self._vals))[0] if len(self._vals) >= 2 else None
+
+    def mean(self):
+        return moe_lb_trend(list(self._vals))[1] if len(self._vals) >= 2 else (
+            self._vals[0] if self._vals else None)
 
 
 def moe_timing_enable(enable: bool = True) -> None:

@@ -1041,6 +1041,35 @@ int moe_pack_weights(const void* W1, const void* W3, const void* W2, const moe_c
   return MOE_OK;
 }
 
+double moe_entropy_coef(int64_t step, int64_t total_steps, double high, double low) {
+  if (!isfinite(high) || !isfinite(low)) return NAN;
+  if (total_steps <= 1) return low;
+  const int64_t s = step < 0 ? 0 : (step > total_steps - 1 ? total_steps - 1 : step);
+  return high + (low - high) * (static_cast<double>(s) / static_cast<double>(total_steps - 1));
+}
+
+int moe_lb_trend(const double* values, int64_t n, double* slope, double* mean) {
+  if (!values || !slope || !mean) return fail(MOE_EINVAL, "values, slope and mean must be non-NULL");
+  if (n < 2) return fail(MOE_EINVAL, "a trend needs at least 2 values (got %lld)", (long long)n);
+  double sum = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (!isfinite(values[i])) return fail(MOE_EINVAL, "value %lld is not finite", (long long)i);
+    sum += values[i];
+  }
+  const double vm = sum / static_cast<double>(n);
+  const double im = static_cast<double>(n - 1) / 2.0;
+  double num = 0.0, den = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double di = static_cast<double>(i) - im;
+    num += di * (values[i] - vm);
+    den += di * di;
+  }
+  *slope = num / den;
+  *mean = vm;
+  g_err.clear();
+  return MOE_OK;
+}
+
 int moe_timing_enable(int enable) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> lk(t.mu);

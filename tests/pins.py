@@ -811,4 +811,70 @@ def pin_empty_call(O):
     assert list(res["dispatch"]["counts"]) == [0, 0, 0, 0]
 
 
+# ---------------------------------------------------------------- training side
+# [Routing guide] "Plain explanation" paragraph 4 (router entropy high early in
+# training, lower later) and "Key insights" item 3 (the load-balancing loss's
+# trend is a quantity to watch).
+def pin_entropy_schedule(O):
+    total, high, low = 101, 0.5, 0.01
+    vals = [O.entropy_schedule(s, total, high, low) for s in range(total)]
+    assert vals[0] == high and abs(vals[-1] - low) <= 1e-15       # the two ends
+    assert all(a > b for a, b in zip(vals, vals[1:]))             # falls every step
+    assert abs(vals[50] - (high + low) / 2) <= 1e-15              # halfway: the mean
+    steps = np.diff(vals)
+    assert np.allclose(steps, (low - high) / (total - 1), rtol=0, atol=1e-15)   # a line
+    assert O.entropy_schedule(10 ** 6, total, high, low) == vals[-1]   # held after the end
+    assert O.entropy_schedule(-5, total, high, low) == high            # and before the start
+    assert O.entropy_schedule(0, 1, high, low) == low
+
+
+def pin_load_balance_trend_library(O):
+    # the least-squares line of numpy.polyfit
+    r = _rng(21)
+    for n in (2, 3, 10, 57):
+        v = 1.5 + r.standard_normal(n) * 0.1 - 0.02 * np.arange(n)
+        res = O.load_balance_trend(list(v))
+        slope, intercept = np.polyfit(np.arange(n), v, 1)
+        assert abs(res["slope"] - slope) <= 1e-12 * max(1.0, abs(slope))
+        assert abs(res["mean"] - float(np.mean(v))) <= 1e-14
+        assert res["last"] == v[-1] and res["n"] == n
+
+
+def pin_load_balance_trend_closed_forms(O):
+    # an exact line gives its own slope; a constant (perfect balance, aux = 1
+    # every step) gives 0; adding a constant changes nothing; two points give
+    # their difference
+    assert abs(O.load_balance_trend([3.0 - 0.25 * i for i in range(9)])["slope"] + 0.25) <= 1e-15
+    assert O.load_balance_trend([1.0] * 7)["slope"] == 0.0
+    a = O.load_balance_trend([1.2, 1.7, 1.1, 1.4])["slope"]
+    b = O.load_balance_trend([11.2, 11.7, 11.1, 11.4])["slope"]
+    assert abs(a - b) <= 1e-12
+    assert O.load_balance_trend([2.0, 1.5])["slope"] == -0.5
+    try:
+        O.load_balance_trend([1.0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a single value has no trend")
+
+
+def pin_load_balance_trend_of_balancing_routing(O):
+    # Batches whose router bias toward expert 0 shrinks step by step (the
+    # load evening out): the aux loss of each batch (routing_stats) falls
+    # toward 1, so its trend is negative; with the bias growing it is
+    # positive.
+    r = _rng(22)
+    T, E, k = 400, 8, 2
+    def aux_of(bias0):
+        L = r.standard_normal((T, E))
+        L[:, 0] += bias0
+        sel, _ = O.topk_select(L, k)
+        D = O.dispatch(sel, E, T)
+        return O.routing_stats(D["counts"], D["kept"], O.softmax_all(L), T, k, E)["aux_loss"]
+    falling = [aux_of(b) for b in np.linspace(3.0, 0.0, 12)]
+    rising = [aux_of(b) for b in np.linspace(0.0, 3.0, 12)]
+    assert O.load_balance_trend(falling)["slope"] < 0 < O.load_balance_trend(rising)["slope"]
+    assert abs(falling[-1] - 1.0) < 0.1
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

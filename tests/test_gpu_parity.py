@@ -526,3 +526,33 @@ def test_forward_paths(case, path):
     say(f"[forward path={path}] {case}")
     run = Run(w)
     check_layer(run, f"{case}/path{path}", path=path)
+
+
+def test_load_balance_trend_of_gpu_batches():
+    # [Routing guide] "Key insights" item 3: the load-balancing loss's trend.
+    # Ten batches whose bias toward expert 0 shrinks: the GPU's aux loss per
+    # batch, and its trend through moe_lb_trend, against the oracle's.
+    w = Workload("trend", T=2000, d=64, F=64, E=8, k=2, capacity_factor=1.25)
+    cfg = config_for(w, stream=None)
+    ws = moe.Workspace(moe.moe_workspace_size(cfg))
+    ws.bind(cfg)
+    r = route_buffers(w.T, w.E, w.k)
+    gpu, ref = [], []
+    for i, b in enumerate(np.linspace(3.0, 0.0, 10)):
+        L = random_logits(w.T, w.E, seed=40 + i)
+        L[:, 0] += float(b)
+        st = moe.moe_route_logits(L.to(DEV), cfg, r["idx"], r["w"], r["counts"], r["offsets"],
+                                  r["perm"], r["slot"], stats=True)
+        L64 = L.to(torch.float64).numpy()
+        sel, _ = O.topk_select(L64, w.k)
+        D = O.dispatch(sel, w.E, O.capacity(w.T, w.k, w.E, w.capacity_factor))
+        aux = O.routing_stats(D["counts"], D["kept"], O.softmax_all(L64), w.T, w.k, w.E)["aux_loss"]
+        assert abs(st["aux_loss"] - aux) <= 1e-5 * aux
+        gpu.append(st["aux_loss"])
+        ref.append(aux)
+    slope, mean = moe.moe_lb_trend(gpu)
+    want = O.load_balance_trend(ref)
+    assert slope < 0
+    assert abs(slope - want["slope"]) <= 1e-4 * abs(want["slope"])
+    assert abs(mean - want["mean"]) <= 1e-5 * want["mean"]
+    say(f"  aux {gpu[0]:.4f} -> {gpu[-1]:.4f}, trend {slope:.4e} per step (oracle {want['slope']:.4e})")

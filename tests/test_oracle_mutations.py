@@ -288,7 +288,45 @@ def _bwd_variant(mode):
     return fn
 
 
+def _schedule_reversed(step, total_steps, high, low):
+    # rises from low to high instead of falling
+    return _orig["entropy_schedule"](step, total_steps, low, high)
+
+
+def _schedule_unclamped(step, total_steps, high, low):
+    if total_steps <= 1:
+        return float(low)
+    return float(high) + (float(low) - float(high)) * int(step) / (int(total_steps) - 1)
+
+
+def _trend_sign(values):
+    res = _orig["load_balance_trend"](values)
+    res["slope"] = -res["slope"]
+    return res
+
+
+def _trend_endpoints(values):
+    # the slope between the first and last value instead of the fitted line
+    res = _orig["load_balance_trend"](values)
+    res["slope"] = (float(values[-1]) - float(values[0])) / (len(values) - 1)
+    return res
+
+
+def _trend_unnormalised(values):
+    # the covariance without dividing by the spread of the step numbers
+    res = _orig["load_balance_trend"](values)
+    n = len(values)
+    m = (n - 1) / 2.0
+    res["slope"] = res["slope"] * sum((i - m) ** 2 for i in range(n)) / n
+    return res
+
+
 MUTATIONS = {
+    "schedule_rises": ("entropy_schedule", _schedule_reversed),
+    "schedule_not_held_at_ends": ("entropy_schedule", _schedule_unclamped),
+    "trend_sign": ("load_balance_trend", _trend_sign),
+    "trend_endpoints_only": ("load_balance_trend", _trend_endpoints),
+    "trend_unnormalised": ("load_balance_trend", _trend_unnormalised),
     "bwd_dropped_rows_counted": ("router_backward", _bwd_variant("dropped")),
     "bwd_no_signal_to_unchosen": ("router_backward", _bwd_variant("selected_only")),
     "bwd_aux_without_E": ("router_backward", _bwd_variant("aux_no_E")),
