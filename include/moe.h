@@ -335,6 +335,17 @@ double moe_entropy_coef(int64_t step, int64_t total_steps, double high, double l
  * untouched). */
 int moe_lb_trend(const double* values, int64_t n, double* slope, double* mean);
 
+/* Debugging aid: workspace canaries.  While enabled (process-wide), the
+ * workspace plan puts a 256-byte guard after every region (so
+ * moe_workspace_size grows by a few KB; size the workspace after enabling),
+ * and every call that uses the workspace first fills the guards with 0xA5
+ * (hipMemsetAsync: not for graph capture).  moe_debug_check(cfg) waits for
+ * cfg->stream and returns how many guards of cfg->workspace no longer hold
+ * the pattern (0: none; moe_last_error names the region before the first
+ * overwritten guard), or a negative status.  Off by default. */
+int moe_debug_canaries(int enable);
+int moe_debug_check(const moe_config_t* cfg);
+
 /* Reason for the last failing call on this thread ("" if none). */
 const char* moe_last_error(void);
 

@@ -26,6 +26,7 @@ __all__ = [
     "moe_workspace_size", "moe_capacity", "moe_forward", "moe_forward_noalloc", "moe_route",
     "moe_route_logits", "moe_aux_loss", "moe_router_backward", "moe_last_error",
     "moe_packed_weight_bytes", "moe_pack_weights", "moe_entropy_coef", "moe_lb_trend",
+    "moe_debug_canaries", "moe_debug_check",
     "LoadBalanceTrend",
     "moe_timing_enable", "moe_timing_only",
     "moe_timing_reset", "moe_timing_read", "Workspace",
@@ -228,6 +229,20 @@ def moe_pack_weights(W1, W3, W2, cfg: MoeConfig, W1p, W3p, W2p) -> None:
     cfg.stream)."""
     _check(LIB.moe_pack_weights(_ptr(W1), _ptr(W3), _ptr(W2), ctypes.byref(cfg), _ptr(W1p),
                                 _ptr(W3p), _ptr(W2p)), "moe_pack_weights")
+
+
+def moe_debug_canaries(enable: bool = True) -> None:
+    """Workspace guards after every region (size workspaces after this)."""
+    LIB.moe_debug_canaries(1 if enable else 0)
+
+
+def moe_debug_check(cfg: MoeConfig) -> int:
+    """Number of overwritten workspace guards of cfg.workspace (waits for
+    cfg.stream)."""
+    rc = LIB.moe_debug_check(ctypes.byref(cfg))
+    if rc < 0:
+        _check(rc, "moe_debug_check")
+    return rc
 
 
 def moe_entropy_coef(step: int, total_steps: int, high: float, low: float) -> float:

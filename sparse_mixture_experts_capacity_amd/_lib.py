@@ -92,6 +92,8 @@ def _load():
                                                    ctypes.POINTER(ctypes.c_size_t)]),
         "moe_pack_weights": (ctypes.c_int, [P, P, P, CFG, P, P, P]),
         "moe_last_error": (ctypes.c_char_p, []),
+        "moe_debug_canaries": (ctypes.c_int, [ctypes.c_int]),
+        "moe_debug_check": (ctypes.c_int, [CFG]),
         "moe_entropy_coef": (ctypes.c_double, [ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
                                                ctypes.c_double]),
         "moe_lb_trend": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.c_int64,

@@ -120,6 +120,15 @@ struct Region {
   size_t off = 0, bytes = 0;
 };
 
+// Debug canaries (moe_debug_canaries): with them on, every workspace region
+// is followed by a guard of kCanaryBytes holding kCanaryByte, written at the
+// start of each call and compared by moe_debug_check, so a kernel that
+// writes past the end of its region is caught.
+constexpr int kMaxGuards = 48;
+constexpr size_t kCanaryBytes = 256;
+constexpr unsigned char kCanaryByte = 0xA5;
+std::atomic<bool> g_canaries{false};
+
 struct Plan {
   int64_t T = 0;
   int d = 0, F = 0, E = 0, k = 0, S = 0;
@@ -155,6 +164,10 @@ struct Plan {
   int64_t bwd_Tp = 0, bwd_T64 = 0;
   int bwd_wsplit = 1;            // K parts of the weight-gradient GEMM
   size_t total = 0;
+  // debug canaries: a guard of kCanaryBytes after every region
+  int nguards = 0;
+  size_t guard_off[kMaxGuards];
+  const char* guard_name[kMaxGuards];
 };
 
 // Shortest decimal that round-trips the double, as digits D and exponent X:
@@ -274,6 +287,16 @@ void add(Region& r, size_t bytes, size_t& cursor) {
   r.bytes = bytes;
   cursor = align_up(cursor + bytes);
 }
+// add() plus, with canaries on, a guard after the region.
+void add_guarded(Plan* p, Region& r, size_t bytes, size_t& cursor, const char* name) {
+  add(r, bytes, cursor);
+  if (g_canaries.load(std::memory_order_relaxed) && p->nguards < kMaxGuards) {
+    p->guard_off[p->nguards] = cursor;
+    p->guard_name[p->nguards] = name;
+    ++p->nguards;
+    cursor = align_up(cursor + kCanaryBytes);
+  }
+}
 
 int make_plan(const moe_config_t* c, Plan* p) {
   int rc = check(c);
@@ -387,34 +410,34 @@ int make_plan(const moe_config_t* c, Plan* p) {
 
   const size_t es = p->bf16 ? 2 : 4;
   size_t cur = 0;
-  add(p->logits, sizeof(float) * p->T * p->E, cur);
-  add(p->lpart, sizeof(float) * (p->mfma_router ? p->router_split : 0) * p->T * p->E, cur);
-  add(p->idx, sizeof(int32_t) * p->TK, cur);
-  add(p->w, sizeof(float) * p->TK, cur);
-  add(p->lrank, sizeof(int32_t) * p->TK, cur);
-  add(p->blkcnt, sizeof(int32_t) * static_cast<size_t>(p->nblk_dispatch) * p->E, cur);
-  add(p->counts, sizeof(int32_t) * p->E, cur);
-  add(p->kcount, sizeof(int32_t) * p->E, cur);
-  add(p->offsets, sizeof(int32_t) * (p->E + 1), cur);
-  add(p->slot, sizeof(int32_t) * p->TK, cur);
-  add(p->perm, sizeof(int32_t) * p->TK, cur);
-  add(p->tiles, sizeof(moe::Tile) * (p->max_mtiles + 1), cur);
-  add(p->ntiles, sizeof(int32_t) * 4, cur);
-  add(p->tstart, sizeof(int32_t) * (p->E + 1), cur);
-  add(p->ppart, sizeof(float) * static_cast<size_t>(p->topk_blocks) * p->E, cur);
-  add(p->hpart, sizeof(float) * p->topk_blocks, cur);
-  add(p->stats, sizeof(double) * 8, cur);
-  add(p->H, es * p->rows_max * p->F, cur);
-  add(p->Hs, es * p->T * p->S * p->F, cur);
+  add_guarded(p, p->logits, sizeof(float) * p->T * p->E, cur, "logits");
+  add_guarded(p, p->lpart, sizeof(float) * (p->mfma_router ? p->router_split : 0) * p->T * p->E, cur, "lpart");
+  add_guarded(p, p->idx, sizeof(int32_t) * p->TK, cur, "idx");
+  add_guarded(p, p->w, sizeof(float) * p->TK, cur, "w");
+  add_guarded(p, p->lrank, sizeof(int32_t) * p->TK, cur, "lrank");
+  add_guarded(p, p->blkcnt, sizeof(int32_t) * static_cast<size_t>(p->nblk_dispatch) * p->E, cur, "blkcnt");
+  add_guarded(p, p->counts, sizeof(int32_t) * p->E, cur, "counts");
+  add_guarded(p, p->kcount, sizeof(int32_t) * p->E, cur, "kcount");
+  add_guarded(p, p->offsets, sizeof(int32_t) * (p->E + 1), cur, "offsets");
+  add_guarded(p, p->slot, sizeof(int32_t) * p->TK, cur, "slot");
+  add_guarded(p, p->perm, sizeof(int32_t) * p->TK, cur, "perm");
+  add_guarded(p, p->tiles, sizeof(moe::Tile) * (p->max_mtiles + 1), cur, "tiles");
+  add_guarded(p, p->ntiles, sizeof(int32_t) * 4, cur, "ntiles");
+  add_guarded(p, p->tstart, sizeof(int32_t) * (p->E + 1), cur, "tstart");
+  add_guarded(p, p->ppart, sizeof(float) * static_cast<size_t>(p->topk_blocks) * p->E, cur, "ppart");
+  add_guarded(p, p->hpart, sizeof(float) * p->topk_blocks, cur, "hpart");
+  add_guarded(p, p->stats, sizeof(double) * 8, cur, "stats");
+  add_guarded(p, p->H, es * p->rows_max * p->F, cur, "H");
+  add_guarded(p, p->Hs, es * p->T * p->S * p->F, cur, "Hs");
   // The routed down projection's rows stay fp32 (K parts summed by the
   // combine), so the only roundings before the output's are the hidden rows'.
-  add(p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur);
-  add(p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur);
-  add(p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur);
+  add_guarded(p, p->Y, sizeof(float) * p->ffn2_split * p->rows_max * p->d, cur, "Y");
+  add_guarded(p, p->Ys, sizeof(float) * p->shared2_split * (p->S > 0 ? p->T : 0) * p->d, cur, "Ys");
+  add_guarded(p, p->Xb, p->gather_x ? es * p->rows_max * p->d : 0, cur, "Xb");
   const size_t rr = p->overflow == MOE_OVERFLOW_REROUTE ? sizeof(int32_t) * p->TK : 0;
-  add(p->ovf, rr, cur);
-  add(p->xdest, rr, cur);
-  add(p->xrel, rr, cur);
+  add_guarded(p, p->ovf, rr, cur, "ovf");
+  add_guarded(p, p->xdest, rr, cur, "xdest");
+  add_guarded(p, p->xrel, rr, cur, "xrel");
   // Router backward.  bf16 layers: both router products run on the MFMA
   // GEMM with bf16 score gradients; the weight gradient's K (tokens) is
   // split for ~512 workgroups with at most 16 MiB of partial sums.  fp32
@@ -437,10 +460,10 @@ int make_plan(const moe_config_t* c, Plan* p) {
     if (ks > 64) ks = 64;
     if (ks < 1) ks = 1;
     p->bwd_wsplit = static_cast<int>(ks);
-    add(p->gpart, sizeof(float) * (ks * ed + ed + p->E), cur);
-    add(p->bdlb, 2 * static_cast<size_t>(p->T) * p->bwd_Kp, cur);
-    add(p->bdlT, 2 * static_cast<size_t>(p->E) * p->bwd_Tp, cur);
-    add(p->bWt, 2 * static_cast<size_t>(p->bwd_Kp) * p->d, cur);
+    add_guarded(p, p->gpart, sizeof(float) * (ks * ed + ed + p->E), cur, "gpart");
+    add_guarded(p, p->bdlb, 2 * static_cast<size_t>(p->T) * p->bwd_Kp, cur, "bdlb");
+    add_guarded(p, p->bdlT, 2 * static_cast<size_t>(p->E) * p->bwd_Tp, cur, "bdlT");
+    add_guarded(p, p->bWt, 2 * static_cast<size_t>(p->bwd_Kp) * p->d, cur, "bWt");
   } else {
     const int64_t per = static_cast<int64_t>(p->d) * p->E + p->E;
     int64_t nc = (p->T + 255) / 256;
@@ -452,7 +475,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
     if (p->bwd_tokens_per_chunk < 1) p->bwd_tokens_per_chunk = 1;
     p->bwd_chunks = static_cast<int>((p->T + p->bwd_tokens_per_chunk - 1) / p->bwd_tokens_per_chunk);
     if (p->bwd_chunks < 1) p->bwd_chunks = 1;
-    add(p->gpart, sizeof(float) * per * p->bwd_chunks, cur);
+    add_guarded(p, p->gpart, sizeof(float) * per * p->bwd_chunks, cur, "gpart");
   }
   p->total = cur;
   return MOE_OK;
@@ -479,6 +502,13 @@ int check_workspace(const moe_config_t* c, const Plan& p) {
     if (e_ != hipSuccess)                                                          \
       return fail(MOE_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
   } while (0)
+
+// Debug canaries: write every guard of the plan (see kCanaryBytes).
+int arm_canaries(const Plan& p, void* ws, hipStream_t s) {
+  for (int i = 0; i < p.nguards; ++i)
+    HIP_TRY(hipMemsetAsync(static_cast<char*>(ws) + p.guard_off[i], kCanaryByte, kCanaryBytes, s));
+  return MOE_OK;
+}
 
 // Step 1: router scores.  Returns, through lsrc/nsplit/bias, where the
 // top-k pass finds them: K-split partial sums of the MFMA GEMM (bias added
@@ -701,6 +731,8 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
     return MOE_OK;
   }
   void* ws = cfg->workspace;
+  rc = arm_canaries(p, ws, s);
+  if (rc != MOE_OK) return rc;
   int32_t* idx = at<int32_t>(ws, p.idx);
   float* w = at<float>(ws, p.w);
   Scores sc;
@@ -856,6 +888,8 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   if (rc != MOE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   void* ws = cfg->workspace;
+  rc = arm_canaries(p, ws, s);
+  if (rc != MOE_OK) return rc;
   moe::RouterBackward b{};
   b.x = x; b.Wg = W_gate; b.dout = dout;
   b.Y = at<void>(ws, p.Y); b.ysplit = p.ffn2_split;
@@ -940,6 +974,8 @@ int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg, float*
     g_err.clear();
     return MOE_OK;
   }
+  rc = arm_canaries(p, cfg->workspace, s);
+  if (rc != MOE_OK) return rc;
   Scores sc;
   rc = run_router(p, cfg->workspace, x, W_gate, cfg->logit_bias, s, &sc);
   if (rc != MOE_OK) return rc;
@@ -971,6 +1007,8 @@ int moe_route_logits(const float* logits, const moe_config_t* cfg, int32_t* topk
     g_err.clear();
     return MOE_OK;
   }
+  rc = arm_canaries(p, cfg->workspace, static_cast<hipStream_t>(cfg->stream));
+  if (rc != MOE_OK) return rc;
   rc = route_common(p, cfg, Scores{logits, 1, 0, nullptr}, nullptr, topk_idx, topk_w, counts,
                     offsets, perm, slot, stats);
   if (rc == MOE_OK) g_err.clear();
@@ -993,6 +1031,8 @@ int moe_aux_loss(const float* logits, const int32_t* counts, const moe_config_t*
   if (rc != MOE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   void* ws = cfg->workspace;
+  rc = arm_canaries(p, ws, s);
+  if (rc != MOE_OK) return rc;
   {
     Timed t("softmax_stats", s);
     HIP_TRY(moe::launch_topk_gate(logits, 1, 0, nullptr, nullptr, p.T, p.E, 1, p.gating,
@@ -1039,6 +1079,45 @@ int moe_pack_weights(const void* W1, const void* W3, const void* W2, const moe_c
   HIP_TRY(moe::launch_pack_blocks(W2, n, cfg->d_ff, cfg->d_model, kPackW2, W2p, s));
   g_err.clear();
   return MOE_OK;
+}
+
+int moe_debug_canaries(int enable) {
+  g_canaries.store(enable != 0, std::memory_order_relaxed);
+  return MOE_OK;
+}
+
+int moe_debug_check(const moe_config_t* cfg) {
+  Plan p;
+  int rc = make_plan(cfg, &p);
+  if (rc != MOE_OK) return rc;
+  if (p.nguards == 0) {
+    g_err.clear();
+    return 0;
+  }
+  rc = check_workspace(cfg, p);
+  if (rc != MOE_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  HIP_TRY(hipStreamSynchronize(s));
+  unsigned char buf[kCanaryBytes];
+  int bad = 0;
+  const char* first = nullptr;
+  for (int i = 0; i < p.nguards; ++i) {
+    HIP_TRY(hipMemcpy(buf, static_cast<const char*>(cfg->workspace) + p.guard_off[i], kCanaryBytes,
+                      hipMemcpyDeviceToHost));
+    for (size_t j = 0; j < kCanaryBytes; ++j) {
+      if (buf[j] != kCanaryByte) {
+        if (!first) first = p.guard_name[i];
+        ++bad;
+        break;
+      }
+    }
+  }
+  if (bad) {
+    fail(MOE_OK, "%d workspace guard(s) overwritten; the first after region '%s'", bad, first);
+    return bad;
+  }
+  g_err.clear();
+  return 0;
 }
 
 double moe_entropy_coef(int64_t step, int64_t total_steps, double high, double low) {

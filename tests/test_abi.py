@@ -214,3 +214,16 @@ def test_noalloc_refuses_layers_beyond_its_scratch():
     bad = cfg(top_k=0)
     assert moe.LIB.moe_forward_noalloc(fake, fake, fake, fake, fake, ctypes.byref(bad), fake,
                                        None) == moe.MOE_EINVAL
+
+
+def test_debug_canaries_grow_the_workspace():
+    c = cfg(T=512)
+    plain = moe.moe_workspace_size(c)
+    moe.moe_debug_canaries(True)
+    try:
+        guarded = moe.moe_workspace_size(c)
+    finally:
+        moe.moe_debug_canaries(False)
+    assert guarded > plain
+    assert (guarded - plain) % 256 == 0 and (guarded - plain) // 256 >= 20
+    assert moe.moe_workspace_size(c) == plain
