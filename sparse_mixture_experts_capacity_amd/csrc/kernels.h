@@ -10,6 +10,15 @@ namespace moe {
 hipError_t launch_router(const void* x, const void* Wg, const float* bias,
                          float* logits, int64_t T, int d, int E, bool bf16,
                          hipStream_t s);
+// Router scores of a short bf16 batch as nparts K parts of d / nparts
+// columns each (lpart[p][t][e], parts T * E apart), for the top-k pass to
+// add in part order.  E = 8 or 16, T * E <= 64, d / nparts a multiple of 4;
+// x and Wg 16-byte aligned.
+inline bool router_parts_fit(int64_t T, int E, int d) {
+  return (E == 8 || E == 16) && T >= 1 && T * E <= 64 && d > 0 && d % 4 == 0;
+}
+hipError_t launch_router_parts(const void* x, const void* Wg, int T, int d, int E, int nparts,
+                               float* lpart, hipStream_t s);
 int topk_group_size(int E);
 // Router scores are read as the sum of `nsplit` partial arrays (split_stride
 // apart) plus the optional bias, in a fixed order; when logits_out is given

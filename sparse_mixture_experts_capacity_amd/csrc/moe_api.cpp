@@ -147,6 +147,7 @@ struct Plan {
   int max_mtiles = 0;
   int static_bm = 0;             // M-tile of the GEMMs over all T token rows
   bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
+  bool parts_router = false;     // short batches: the K-part router instead (aligned x, W_gate)
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
@@ -379,6 +380,15 @@ int make_plan(const moe_config_t* c, Plan* p) {
     if (ks < 1) ks = 1;
     while (kk % ks) --ks;
     p->router_split = static_cast<int>(ks);
+    // Short batches with 8 or 16 experts: one wavefront per K part, at most
+    // 8 parts (one load round in the top-k pass).  The MFMA router takes the
+    // same parts when x or W_gate is not 16-byte aligned.
+    if (moe::router_parts_fit(p->T, p->E, p->d)) {
+      int np = kk < 8 ? kk : 8;
+      while (kk % np) --np;
+      p->router_split = np;
+      p->parts_router = true;
+    }
   }
   // Down projections with few tiles (short batches: a few rows per expert)
   // split K so ~512 workgroups stream the weights; the combine adds the
@@ -522,7 +532,14 @@ struct Scores {
 
 int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
                const float* bias, hipStream_t s, Scores* sc) {
-  if (p.mfma_router) {
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(W_gate) % 16 == 0);
+  if (p.parts_router && aligned16) {
+    Timed t("router", s);
+    HIP_TRY(moe::launch_router_parts(x, W_gate, static_cast<int>(p.T), p.d, p.E, p.router_split,
+                                     at<float>(ws, p.lpart), s));
+    *sc = Scores{at<float>(ws, p.lpart), p.router_split, p.T * p.E, bias};
+  } else if (p.mfma_router) {
     moe::GroupedGemm r{};
     r.A = x; r.lda = p.d; r.perm = nullptr; r.topk = 1;
     r.B = W_gate; r.B3 = nullptr; r.b_stride = 0; r.group_base = 0; r.ldb = p.E;

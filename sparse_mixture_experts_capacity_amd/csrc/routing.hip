@@ -124,6 +124,111 @@ hipError_t launch_router(const void* x, const void* Wg, const float* bias,
 }
 
 // ---------------------------------------------------------------------------
+// Router scores of a short bf16 batch in K parts ([Mixtral explainer]
+// "Plain explanation" para 3: one score per expert from the token's vector):
+// part p of score (t, e) is sum over its column range of x[t][c] Wg[c][e],
+// and the top-k pass adds the parts in part order.  One wavefront per part.
+// Lane l takes columns 4l .. 4l+3 of each 256-column run of the part and
+// keeps NV = TM * NE register sums, one per (token, expert) for T <= TM
+// tokens (the rows from T on read as zero).  The wavefront then sums them by
+// recursive halving: at lane bit b (b = 5, 4, ...), a lane keeps the half of
+// its current sums that its bit selects and adds the partner's copy of that
+// half, so after log2 NV exchanges lane l holds sum index l >> (6 - log2 NV)
+// over 2^log2 NV lanes; an xor butterfly over the lower lane bits completes
+// it.  NV - 1 + (6 - log2 NV) exchanges in all, in a fixed order.
+// ---------------------------------------------------------------------------
+template <int NE, int TM>
+__global__ __launch_bounds__(64) void router_parts_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg, int T, int d, int cols,
+    float* __restrict__ lpart) {
+  constexpr int NV = TM * NE;
+  constexpr int LV = NV == 8 ? 3 : NV == 16 ? 4 : NV == 32 ? 5 : 6;
+  static_assert((1 << LV) == NV, "NV must be 8, 16, 32 or 64");
+  const int lane = threadIdx.x;
+  const int c_begin = blockIdx.x * cols;
+  const int c_end = c_begin + cols;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  for (int c0 = c_begin + 4 * lane; c0 < c_end; c0 += 4 * kWave) {
+    uint4 wv[4][NE / 8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int h = 0; h < NE / 8; ++h)
+        wv[q][h] = *reinterpret_cast<const uint4*>(Wg + static_cast<int64_t>(c0 + q) * NE + 8 * h);
+    uint2 xv[TM];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+      xv[t] = t < T ? *reinterpret_cast<const uint2*>(x + static_cast<int64_t>(t) * d + c0)
+                    : make_uint2(0u, 0u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float w[NE];
+#pragma unroll
+      for (int h = 0; h < NE / 8; ++h) {
+        const uint32_t u[4] = {wv[q][h].x, wv[q][h].y, wv[q][h].z, wv[q][h].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          w[8 * h + 2 * r] = __uint_as_float(u[r] << 16);
+          w[8 * h + 2 * r + 1] = __uint_as_float(u[r] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const uint32_t xw = q < 2 ? xv[t].x : xv[t].y;
+        const float xq = __uint_as_float((q & 1) ? (xw & 0xffff0000u) : (xw << 16));
+#pragma unroll
+        for (int e = 0; e < NE; ++e) v[t * NE + e] = fmaf(xq, w[e], v[t * NE + e]);
+      }
+    }
+  }
+  // recursive halving over lane bits 5 .. 6 - LV
+#pragma unroll
+  for (int st = 0; st < LV; ++st) {
+    const int off = kWave >> (st + 1);
+    const int half = NV >> (st + 1);
+    const bool upper = (lane & off) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float keep = upper ? v[i + half] : v[i];
+      const float send = upper ? v[i] : v[i + half];
+      v[i] = keep + __shfl_xor(send, off);
+    }
+  }
+  float r = v[0];
+#pragma unroll
+  for (int off = (kWave >> LV) >> 1; off >= 1; off >>= 1) r += __shfl_xor(r, off);
+  constexpr int kLow = kWave >> LV;   // lanes sharing one sum index
+  const int idx = lane / kLow;
+  if (lane % kLow == 0 && idx < T * NE)
+    lpart[static_cast<int64_t>(blockIdx.x) * T * NE + idx] = r;
+}
+
+hipError_t launch_router_parts(const void* x, const void* Wg, int T, int d, int E, int nparts,
+                               float* lpart, hipStream_t s) {
+  if (!router_parts_fit(T, E, d) || nparts < 1 || d % nparts || (d / nparts) % 4)
+    return hipErrorInvalidValue;
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* wb = static_cast<const uint16_t*>(Wg);
+  const int cols = d / nparts;
+#define MOE_PARTS_LAUNCH(NE, TM) \
+  router_parts_kernel<NE, TM><<<nparts, kWave, 0, s>>>(xb, wb, T, d, cols, lpart)
+  if (E == 8) {
+    if (T <= 1) MOE_PARTS_LAUNCH(8, 1);
+    else if (T <= 2) MOE_PARTS_LAUNCH(8, 2);
+    else if (T <= 4) MOE_PARTS_LAUNCH(8, 4);
+    else MOE_PARTS_LAUNCH(8, 8);
+  } else {
+    if (T <= 1) MOE_PARTS_LAUNCH(16, 1);
+    else if (T <= 2) MOE_PARTS_LAUNCH(16, 2);
+    else MOE_PARTS_LAUNCH(16, 4);
+  }
+#undef MOE_PARTS_LAUNCH
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Top-k + gates + softmax statistics.  A group of G lanes (G a power of two,
 // G >= E/4) handles one token; lane g of the group holds the scores of
 // experts g, g+G, g+2G, g+3G.  k rounds of a group-wide argmax by butterfly
@@ -862,14 +967,16 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     if (gl == 0) hbuf[grp] = hacc;
     for (int i = tid; i < kSmallWaves * E; i += blockDim.x) ccnt[i / E][i % E] = 0;
     __syncthreads();
+    // groups from T on took no token and hold zeros: the sums stop before them
+    const int gused = min(ngroups, T);
     for (int e = tid; e < E; e += blockDim.x) {
       float sp = 0.f;
-      for (int g = 0; g < ngroups; ++g) sp += pbuf[g * E + e];
+      for (int g = 0; g < gused; ++g) sp += pbuf[g * E + e];
       Ppart[e] = sp;
     }
     if (tid == 0) {
       float sh = 0.f;
-      for (int g = 0; g < ngroups; ++g) sh += hbuf[g];
+      for (int g = 0; g < gused; ++g) sh += hbuf[g];
       Hpart[0] = sh;
     }
   }

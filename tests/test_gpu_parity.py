@@ -296,13 +296,19 @@ ROUTE_CASES = {
                           gating=SOFTMAX_THEN_TOPK, renormalize=False),
     "f32_E40_ragged_d": Workload("f32_E40", T=77, d=100, F=30, E=40, k=3, dtype="f32",
                                  capacity_factor=1.0),
-    # short batches (one routing workgroup), router K split into up to 16
-    # parts, with and without a score bias
+    # short batches (one routing workgroup), router scores in K parts, with
+    # and without a score bias
     "bf16_fused_T1": Workload("bf16_f1", T=1, d=1024, F=64, E=8, k=2),
     "bf16_fused_T3_E16": Workload("bf16_f3", T=3, d=384, F=64, E=16, k=4,
                                   gating=SOFTMAX_THEN_TOPK, renormalize=False),
     "bf16_fused_T128_bias": Workload("bf16_f128", T=128, d=512, F=64, E=8, k=2,
                                      capacity_factor=1.0, bias=SKEW_BIAS),
+    # the K-part router (E = 8 or 16, T * E <= 64): 8 parts of 512 columns
+    # (two runs per lane), a token bound above T, a score bias
+    "bf16_parts_T5_bias": Workload("bf16_p5", T=5, d=4096, F=64, E=8, k=2,
+                                   capacity_factor=1.0, bias=SKEW_BIAS),
+    # 5 parts of 128 columns, T at the token bound
+    "bf16_parts_T8_d640": Workload("bf16_p8", T=8, d=640, F=64, E=8, k=2),
 }
 
 
