@@ -34,13 +34,14 @@ MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM on packed weights (the default layout); the counter
     # summaries are kept beside the profiles
-    "mixtral_prefill": ("083d59d9489780bd", 3947.96e6, 121.81e6),
-    "deepseek": ("083d59d9489780bd", 5340.59e6, 75.62e6),
-    "mixtral_decode_t64": ("083d59d9489780bd", 1891.66e6, 3.67e6),
+    "mixtral_prefill": ("7b127e6b08507684", 3977.86e6, 121.78e6),
+    "deepseek": ("7b127e6b08507684", 5341.09e6, 75.59e6),
+    "mixtral_decode_t64": ("7b127e6b08507684", 1891.72e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.
-SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "moe_api.cpp", "common.h", "kernels.h")
+SOURCE_FILES = ("routing.hip", "ffn_grouped.hip", "ffn_dma.h", "moe_api.cpp", "common.h",
+                "kernels.h")
 
 
 def source_digest() -> str:
