@@ -90,7 +90,7 @@ __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
 //
 // LDS layouts (no padding; XOR swizzles keep every read conflict-free):
 //   A stage: BM rows x 2*BK bytes; 16-byte chunk c of row m is stored at
-//            a_chunk(m, c) (an XOR of c with low bits of m).
+//            a_chunk(m, c) (an XOR of c with bits 1-2 of m).
 //   B stage: BK rows x 2*BN bytes; 32-byte segment s (16 columns) of row k
 //            sits at segment s ^ ((k & 3) | ((k >> 1) & 4)).
 //
@@ -135,14 +135,18 @@ struct Shape {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Stored position of 16-byte chunk c of A row m.  With 8 chunks per row
-// (BK = 64): c ^ (m & 7) ^ ((m >> 3) & 1); with 4 (BK = 32):
-// c ^ (m & 3) ^ ((m >> 2) & 3).  Either way 16 consecutive rows read at one
-// chunk hit 16 different 16-byte bank groups.
+// Stored position of 16-byte chunk c of A row m.  The A fragment read
+// (ds_read_b128: lane l takes row l % 16, chunk l / 16 of a 32-deep half)
+// runs in four LDS cycles of 16 lanes over 16 bank groups of 16 bytes.
+// Measured with the bank-conflict counter, lanes share a cycle when they
+// agree in lane bit 5 and in the parity of lane bits 2-4 (not simply 16
+// consecutive lanes).  With 4 chunks per row (BK = 32): c ^ ((m >> 1) & 2);
+// with 8 (BK = 64): c ^ (m & 6).  Either way the 16 lanes of a cycle hit 16
+// different bank groups in both halves.
 template <int CA>
 __device__ __forceinline__ int a_chunk(int m, int c) {
-  if constexpr (CA == 8) return c ^ (m & 7) ^ ((m >> 3) & 1);
-  return c ^ (m & 3) ^ ((m >> 2) & 3);
+  if constexpr (CA == 8) return c ^ (m & 6);
+  return c ^ ((m >> 1) & 2);
 }
 __device__ __forceinline__ int b_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
