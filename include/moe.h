@@ -45,6 +45,9 @@
  *     may instead be given in the packed layout (moe_weight_layout_t).
  *   - x, W_gate, W1, W3, W2 and out share cfg->dtype (fp32 or bf16); router
  *     logits, bias and gate weights are fp32; indices int32.
+ *   - x, W_gate, W1, W3, W2, out (and the packed weight buffers) must be
+ *     16-byte aligned, as device allocations are; a view that starts
+ *     part-way into an allocation may not be, and is rejected (MOE_EINVAL).
  *   - Work is enqueued on cfg->stream (a hipStream_t; NULL = the null
  *     stream) and returns before it finishes, unless a host-side result is
  *     requested (stats != NULL, moe_aux_loss), in which case the call waits

@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -147,7 +148,7 @@ struct Plan {
   int max_mtiles = 0;
   int static_bm = 0;             // M-tile of the GEMMs over all T token rows
   bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
-  bool parts_router = false;     // short batches: the K-part router instead (aligned x, W_gate)
+  bool parts_router = false;     // short batches: the K-part router instead
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
@@ -381,8 +382,7 @@ int make_plan(const moe_config_t* c, Plan* p) {
     while (kk % ks) --ks;
     p->router_split = static_cast<int>(ks);
     // Short batches with 8 or 16 experts: one wavefront per K part, at most
-    // 8 parts (one load round in the top-k pass).  The MFMA router takes the
-    // same parts when x or W_gate is not 16-byte aligned.
+    // 8 parts (one load round in the top-k pass).
     if (moe::router_parts_fit(p->T, p->E, p->d)) {
       int np = kk < 8 ? kk : 8;
       while (kk % np) --np;
@@ -496,6 +496,16 @@ T* at(void* ws, const Region& r) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + r.off);
 }
 
+// The kernels read and write x, W_gate, the expert weights and out with
+// 16-byte vector loads and global -> LDS transfers, so those pointers must be
+// 16-byte aligned (device allocations are; a view that starts part-way into
+// an allocation need not be).  NULL passes here; it is checked on its own.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (reinterpret_cast<uintptr_t>(q) % 16 != 0) return false;
+  return true;
+}
+
 int check_workspace(const moe_config_t* c, const Plan& p) {
   if (p.T == 0) return MOE_OK;
   if (!c->workspace) return fail(MOE_EWORKSPACE, "workspace is NULL (need %zu bytes)", p.total);
@@ -532,9 +542,7 @@ struct Scores {
 
 int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
                const float* bias, hipStream_t s, Scores* sc) {
-  const bool aligned16 = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
-                         (reinterpret_cast<uintptr_t>(W_gate) % 16 == 0);
-  if (p.parts_router && aligned16) {
+  if (p.parts_router) {
     Timed t("router", s);
     HIP_TRY(moe::launch_router_parts(x, W_gate, static_cast<int>(p.T), p.d, p.E, p.router_split,
                                      at<float>(ws, p.lpart), s));
@@ -739,6 +747,8 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   if (rc != MOE_OK) return rc;
   if (p.T > 0 && (!x || !W_gate || !W1 || !W3 || !W2 || !out))
     return fail(MOE_EINVAL, "x, W_gate, W1, W3, W2 and out must be non-NULL");
+  if (p.T > 0 && !aligned16({x, W_gate, W1, W3, W2, out}))
+    return fail(MOE_EINVAL, "x, W_gate, W1, W3, W2 and out must be 16-byte aligned");
   rc = check_workspace(cfg, p);
   if (rc != MOE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
@@ -901,6 +911,7 @@ int moe_router_backward(const void* x, const void* W_gate, const void* dout, dou
   if (!dout || !dlogits) return fail(MOE_EINVAL, "dout and dlogits must be non-NULL");
   if (dW_gate && !x) return fail(MOE_EINVAL, "x must be non-NULL when dW_gate is requested");
   if (dx && !W_gate) return fail(MOE_EINVAL, "W_gate must be non-NULL when dx is requested");
+  if (!aligned16({x, W_gate})) return fail(MOE_EINVAL, "x and W_gate must be 16-byte aligned");
   rc = check_workspace(cfg, p);
   if (rc != MOE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
@@ -983,6 +994,8 @@ int moe_route(const void* x, const void* W_gate, const moe_config_t* cfg, float*
   if (rc != MOE_OK) return rc;
   if (p.T > 0 && (!x || !W_gate || !topk_idx))
     return fail(MOE_EINVAL, "x, W_gate and topk_idx must be non-NULL");
+  if (p.T > 0 && !aligned16({x, W_gate}))
+    return fail(MOE_EINVAL, "x and W_gate must be 16-byte aligned");
   rc = check_workspace(cfg, p);
   if (rc != MOE_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
@@ -1089,6 +1102,8 @@ int moe_pack_weights(const void* W1, const void* W3, const void* W2, const moe_c
   if (cfg->dtype != MOE_DTYPE_BF16) return fail(MOE_EUNSUPPORTED, "packed weights are for bf16 layers");
   if (!W1 || !W3 || !W2 || !W1p || !W3p || !W2p)
     return fail(MOE_EINVAL, "W1, W3, W2, W1p, W3p and W2p must be non-NULL");
+  if (!aligned16({W1, W3, W2, W1p, W3p, W2p}))
+    return fail(MOE_EINVAL, "W1, W3, W2, W1p, W3p and W2p must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   const int64_t n = cfg->n_experts + cfg->n_shared;
   HIP_TRY(moe::launch_pack_blocks(W1, n, cfg->d_model, cfg->d_ff, kPackW13, W1p, s));

@@ -158,6 +158,36 @@ def test_router_backward_argument_checks():
                                        None, None, None) == moe.MOE_OK
 
 
+def test_misaligned_tensors_are_refused():
+    # host-side validation only: nothing is launched.  The kernels move x,
+    # W_gate, the expert weights and out in 16-byte pieces, so a pointer 2
+    # bytes into an allocation (a bf16 view starting one element in) is an
+    # argument error, reported before the workspace is looked at.
+    c = cfg(T=64)
+    ok, off = 256, 258
+    for args in ([off, ok, ok, ok, ok, ok], [ok, off, ok, ok, ok, ok], [ok, ok, off, ok, ok, ok],
+                 [ok, ok, ok, off, ok, ok], [ok, ok, ok, ok, off, ok], [ok, ok, ok, ok, ok, off]):
+        x, wg, w1, w3, w2, out = args
+        rc = moe.LIB.moe_forward(x, wg, w1, w3, w2, ctypes.byref(c), out, None)
+        assert rc == moe.MOE_EINVAL
+        assert "16-byte aligned" in moe.moe_last_error()
+    idx = 512
+    assert moe.LIB.moe_route(off, ok, ctypes.byref(c), None, idx, None, None, None, None, None,
+                             None) == moe.MOE_EINVAL
+    assert "16-byte aligned" in moe.moe_last_error()
+    assert moe.LIB.moe_router_backward(off, ok, ok, 0.0, 0.0, ctypes.byref(c), ok, ok, None,
+                                       None) == moe.MOE_EINVAL
+    assert "16-byte aligned" in moe.moe_last_error()
+    assert moe.LIB.moe_pack_weights(ok, ok, ok, ctypes.byref(cfg()), ok, off,
+                                    ok) == moe.MOE_EINVAL
+    assert "16-byte aligned" in moe.moe_last_error()
+    # aligned pointers get past the check to the missing workspace
+    assert moe.LIB.moe_forward(ok, ok, ok, ok, ok, ctypes.byref(c), ok, None) == moe.MOE_EWORKSPACE
+    # no tokens: nothing is read, so nothing is checked
+    assert moe.LIB.moe_forward(off, off, off, off, off, ctypes.byref(cfg(T=0)), off,
+                               None) == moe.MOE_OK
+
+
 @pytest.mark.parametrize("d,F,E,S", [(128, 256, 8, 0), (192, 320, 4, 2), (4096, 14336, 8, 0),
                                      (5120, 1536, 160, 2)])
 def test_packed_weight_sizes(d, F, E, S):
