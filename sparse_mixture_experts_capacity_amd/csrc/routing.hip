@@ -604,14 +604,14 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
 //      available (full, one of the token's own choices, or a spare expert
 //      one of its assignments of an earlier chunk was sent to); then
 //      wavefront 0 takes the chunk 64 assignments at a time, lane i the
-//      i-th: each lane finds the best available expert of its row, and the
-//      lanes are accepted in order up to the first one whose expert was
-//      filled by the lanes before it, or taken by a lane before it of the
-//      same token; the rest search again.  An accepted expert becomes NaN in
-//      the later rows of the same token (a token's rows are adjacent).  Each
-//      repeat means one more expert became full (its column is then set to
-//      NaN in every row of the chunk) or one more of a token's rows was
-//      placed, so the rounds are bounded;
+//      i-th, in rounds: each pending lane takes the r-th best available
+//      expert of its row, r being the number of its token's rows on earlier
+//      pending lanes (a token's rows are adjacent and see the same available
+//      experts, so they pick distinct ones), and the lanes are accepted in
+//      order up to the first one whose expert the lanes before it filled.
+//      An accepted expert becomes NaN in the later rows of the same token,
+//      a full expert in every row of the chunk.  The first pending lane is
+//      always accepted, so a batch takes at most 64 rounds;
 //   C. kcount becomes the final rows per expert; offsets and tiles as pass 2.
 // xdest[a] / xrel[a] (overflow assignments only) receive the new expert (or
 // -1) and the row inside its range.
@@ -619,6 +619,9 @@ __global__ __launch_bounds__(256) void dispatch_scan_kernel(
 constexpr int kRerouteThreads = 1024;
 constexpr int kRerouteLds = kWave * (kMaxExperts + 1);   // floats of staged scores
 constexpr int kRerouteRows = 1792;   // rows staged at most: kRerouteLds / 9, floor to 64
+// QN: best experts a row keeps from one scan (k rounded up to 2, 4, 6 or 8:
+// a token has at most k - 1 rows ahead of any of its rows).
+template <int QN>
 __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
     const int32_t* __restrict__ blkbase, const float* __restrict__ logits, int64_t TK,
@@ -730,51 +733,105 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
         const int tok = have ? a / k : -1;
         const float* row = srow + (b0 + lane) * stride;
         bool pending = have;
-        // best and second-best available expert of the row (-1: none, -2:
-        // not known).  Availability only shrinks, so when the best fills up
-        // the second becomes the best and the row needs no rescan.
-        int best = -2, second = -2;
-        while (__ballot(pending)) {
-          // a best that is not known, or no longer has room, needs a scan
-          const bool scan = pending && (best == -2 || (best >= 0 && fill[best] >= C));
-          if (__ballot(scan)) {
-            if (scan && room > 0) {
-              // strict > over ascending indices keeps the lower index on
-              // ties; unavailable entries are NaN and never compare greater
-              float bv = -INFINITY, sv = -INFINITY;
-              int b = -1, s2 = -1;
-#pragma unroll 2
-              for (int c0 = 0; c0 < E8; c0 += 8) {
-                float v[8];
+        // The row's best available experts at its last scan, best first
+        // (ncand of them; `more`: the scan found others beyond QN).
+        // Availability only shrinks, so entries are re-checked, not rescanned.
+        int cand[QN];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = row[c0 + u];
+        for (int i = 0; i < QN; ++i) cand[i] = -1;
+        int ncand = 0;
+        bool more = false, known = false;
+        // Every round accepts at least the first pending lane (rank 0, an
+        // available expert or none), so 64 rounds suffice; the bound only
+        // guards against a hang.
+        for (int round = 0; round <= kWave && __ballot(pending); ++round) {
+          // rows of the same token on earlier pending lanes: this row takes
+          // the token's rank-th best available expert (all of a token's
+          // pending rows see the same available experts)
+          int rank = 0;
+          for (int q = 1; q < qmax; ++q) {
+            const int src = lane >= q ? lane - q : lane;
+            const int tq = __shfl(tok, src);
+            const int pq = __shfl(pending ? 1 : 0, src);
+            if (lane >= q && pq && tq == tok) ++rank;
+          }
+          int pick = -1, nvalid = 0;
+          if (pending && known) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                  const bool top = v[u] > bv;
-                  const bool mid = !top && v[u] > sv;
-                  s2 = top ? b : (mid ? c0 + u : s2);
-                  sv = top ? bv : (mid ? v[u] : sv);
-                  b = top ? c0 + u : b;
-                  bv = top ? v[u] : bv;
+            for (int i = 0; i < QN; ++i) {
+              if (i < ncand) {
+                const int c = cand[i];
+                const float v = row[c];
+                if (fill[c] < C && v == v) {
+                  if (nvalid == rank) pick = c;
+                  ++nvalid;
                 }
               }
-              // available experts that score -infinity come after the rest,
-              // by index: they fill the best / second places left empty
-              if (s2 < 0) {
-                for (int c = 0; c < E8; ++c) {
-                  if (row[c] != -INFINITY || c == b) continue;
-                  if (b < 0) { b = c; continue; }
-                  s2 = c;
-                  break;
-                }
-              }
-              best = b;
-              second = s2;
-            } else if (scan) {
-              best = second = -1;   // no free slot anywhere
             }
           }
-          const int cur = pending ? best : -1;
+          const bool scan = pending && (!known || (pick < 0 && more));
+          if (__ballot(scan)) {
+            if (scan) {
+              ncand = 0;
+              more = false;
+              if (room > 0) {
+                // strict > over ascending indices keeps the lower index on
+                // ties; NaN (unavailable) is skipped; -infinity ranks after
+                // every number, by index
+                float cv[QN];
+                int ci[QN];
+#pragma unroll
+                for (int i = 0; i < QN; ++i) {
+                  cv[i] = 0.f;
+                  ci[i] = -1;
+                }
+                int navail = 0;
+                for (int c0 = 0; c0 < E8; c0 += 8) {
+                  float v8[8];
+#pragma unroll
+                  for (int u = 0; u < 8; ++u) v8[u] = row[c0 + u];
+#pragma unroll
+                  for (int u = 0; u < 8; ++u) {
+                    const float v = v8[u];
+                    if (v == v) {
+                      ++navail;
+                      bool bt[QN];
+#pragma unroll
+                      for (int i = 0; i < QN; ++i) bt[i] = ci[i] < 0 || v > cv[i];
+#pragma unroll
+                      for (int i = QN - 1; i >= 1; --i) {
+                        if (bt[i - 1]) {
+                          cv[i] = cv[i - 1];
+                          ci[i] = ci[i - 1];
+                        } else if (bt[i]) {
+                          cv[i] = v;
+                          ci[i] = c0 + u;
+                        }
+                      }
+                      if (bt[0]) {
+                        cv[0] = v;
+                        ci[0] = c0 + u;
+                      }
+                    }
+                  }
+                }
+                ncand = min(navail, QN);
+                more = navail > QN;
+#pragma unroll
+                for (int i = 0; i < QN; ++i) cand[i] = ci[i];
+              }
+              known = true;
+              pick = -1;
+#pragma unroll
+              for (int i = 0; i < QN; ++i)
+                if (i == rank && i < ncand) pick = cand[i];
+            }
+          }
+          // no pick: dropped when the token has no expert left for this row;
+          // with candidates beyond the cached ones, the row waits for the
+          // token's earlier rows (`again`: accepted no further this round)
+          const bool again = pending && pick < 0 && more;
+          const int cur = pending ? pick : -1;
           // lanes before this one (in this round) that picked the same expert
           const bool valid = cur >= 0;
           const int e = valid ? cur : 0;
@@ -786,16 +843,7 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
           }
           const int fb = valid ? fill[e] : 0;
           const int ahead = __popcll(match & lt);
-          // an earlier lane of this round holding a row of the same token
-          // picked the same expert: the token may not take it twice
-          bool dup = false;
-          for (int q = 1; q < qmax; ++q) {
-            const int src = lane >= q ? lane - q : lane;
-            const int tq = __shfl(tok, src);
-            const int eq = __shfl(valid ? e : -1, src);
-            dup = dup || (lane >= q && valid && tq == tok && eq == e);
-          }
-          const uint64_t clash = __ballot(valid && (fb + ahead >= C || dup));
+          const uint64_t clash = __ballot((valid && fb + ahead >= C) || again);
           const int first = clash ? __ffsll(static_cast<unsigned long long>(clash)) - 1 : kWave;
           const bool accept = pending && lane < first;
           if (accept) {
@@ -812,26 +860,12 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
           room -= __popcll(took);
           pending = pending && !accept;
           // the expert an accepted row took is no longer available to the
-          // token's later rows: NaN in their staged scores, and out of the
-          // best / second of the lanes of this batch holding them
-          const bool placed = accept && valid;
-          if (placed) {
+          // token's later rows: NaN in their staged scores
+          if (accept && valid) {
             for (int q = 1; q < k; ++q) {
               const int r2 = b0 + lane + q;
               if (r2 >= rows || sa[r2] / k != tok) break;
               srow[r2 * stride + e] = kNaN;
-            }
-          }
-          for (int q = 1; q < qmax; ++q) {
-            const int src = lane >= q ? lane - q : lane;
-            const int tq = __shfl(tok, src);
-            const int eq = __shfl(placed ? e : -1, src);
-            if (lane >= q && pending && eq >= 0 && tq == tok) {
-              if (second == eq) second = -2;
-              if (best == eq) {
-                best = second;
-                second = -2;
-              }
             }
           }
           // experts this round filled up: unavailable in every row of the chunk
@@ -841,11 +875,6 @@ __global__ __launch_bounds__(kRerouteThreads) void dispatch_reroute_kernel(
             filled &= filled - 1;
             const int cf = __shfl(e, l);
             for (int r = lane; r < rows; r += kWave) srow[r * stride + cf] = kNaN;
-            if (second == cf) second = -2;
-            if (best == cf) {
-              best = second;
-              second = -2;
-            }
           }
           __builtin_amdgcn_wave_barrier();
         }
@@ -903,10 +932,17 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
   dispatch_rank_kernel<<<nblk, 64, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
   dispatch_scan_kernel<<<1, 256, 0, s>>>(blkcnt, nblk, E, C, counts, kcount,
                                          offsets, bm, tiles, ntiles, tstart);
-  if (rr)
-    dispatch_reroute_kernel<<<1, kRerouteThreads, 0, s>>>(
-        topk_idx, lrank, blkcnt, rr->logits, TK, rr->k, E, C, kcount, offsets, bm, tiles,
-        ntiles, tstart, rr->ovf, rr->xdest, rr->xrel);
+  if (rr) {
+#define MOE_REROUTE(QN)                                                                   \
+  dispatch_reroute_kernel<QN><<<1, kRerouteThreads, 0, s>>>(                               \
+      topk_idx, lrank, blkcnt, rr->logits, TK, rr->k, E, C, kcount, offsets, bm, tiles, ntiles, \
+      tstart, rr->ovf, rr->xdest, rr->xrel)
+    if (rr->k <= 2) MOE_REROUTE(2);
+    else if (rr->k <= 4) MOE_REROUTE(4);
+    else if (rr->k <= 6) MOE_REROUTE(6);
+    else MOE_REROUTE(8);
+#undef MOE_REROUTE
+  }
   dispatch_scatter_kernel<<<(TK + 255) / 256, 256, 0, s>>>(
       topk_idx, lrank, blkcnt, offsets, TK, E, C, slot, perm, rr ? rr->xdest : nullptr,
       rr ? rr->xrel : nullptr);
