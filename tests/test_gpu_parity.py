@@ -379,6 +379,12 @@ FORWARD_CASES = {
                                       capacity_factor=1.0, overflow=1),
     "bf16_short_reroute": Workload("bf16_short_rr", T=64, d=128, F=192, E=4, k=2,
                                    capacity_factor=0.75, overflow=1),
+    # every token's 12 choices among the same 12 of 32 experts: up to 12
+    # overflow rows per token, more than the 8 best experts a row keeps
+    # from one scan, so later rows of a token wait a round
+    "bf16_reroute_k12": Workload("bf16_rr_k12", T=96, d=128, F=64, E=32, k=12,
+                                 capacity_factor=1.0, overflow=1,
+                                 bias=(4.0,) * 12 + (0.0,) * 20),
     "f32_reroute_shared": Workload("f32_rr", T=150, d=72, F=40, E=6, k=2, S=1, dtype="f32",
                                    capacity_factor=0.8, overflow=1),
     # 256 experts, top-8: most experts get a handful of rows
