@@ -170,9 +170,10 @@ def rne_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def record(entry: dict) -> None:
-    """Append one parity result to gpurun_out/parity_ratios.jsonl (the
-    per-workload record of max|d| / RMS(ref))."""
-    d = os.path.join(ROOT, "gpurun_out")
+    """Append one parity result to parity_ratios.jsonl (the per-workload
+    record of max|d| / RMS(ref)) in $MOE_TEST_RECORDS, by default
+    test_records/ at the repository root."""
+    d = os.environ.get("MOE_TEST_RECORDS") or os.path.join(ROOT, "test_records")
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "parity_ratios.jsonl"), "a") as f:
         f.write(json.dumps(entry) + "\n")
