@@ -299,6 +299,17 @@ struct TileSources {
     }
   }
 
+  // Transfer idx (A loads first, then B loads) of this wavefront's share of
+  // the K step starting at k0, into the stage at LDS byte address sb.
+  template <int IDX>
+  __device__ __forceinline__ void issue_one(uint32_t sb, int k0, int wave_u) const {
+    if constexpr (IDX < S::A_LOADS) {
+      dma16(asrc[IDX] + k0 * a_kstride, sb + (wave_u * S::A_LOADS + IDX) * 1024);
+    } else if constexpr (IDX < S::LOADS) {
+      constexpr int i = IDX - S::A_LOADS;
+      dma16(bsrc[i] + static_cast<int64_t>(k0) * ldb, sb + S::A_STAGE + (wave_u * S::B_LOADS + i) * 1024);
+    }
+  }
   // This wavefront's transfers of the K step starting at element k0 into the
   // stage at LDS byte address sb (wave_u: the wave index, wave-uniform).
   __device__ __forceinline__ void issue(uint32_t sb, int k0, int wave_u) const {
