@@ -34,9 +34,9 @@ MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM on packed weights (the default layout); the counter
     # summaries are kept beside the profiles
-    "mixtral_prefill": ("a1d9adc195f59f1e", 3922.21e6, 121.75e6),
-    "deepseek": ("a1d9adc195f59f1e", 5340.58e6, 75.60e6),
-    "mixtral_decode_t64": ("a1d9adc195f59f1e", 1891.58e6, 3.67e6),
+    "mixtral_prefill": ("c323e0f4742cfd07", 3924.49e6, 121.82e6),
+    "deepseek": ("c323e0f4742cfd07", 5341.06e6, 75.61e6),
+    "mixtral_decode_t64": ("c323e0f4742cfd07", 1891.54e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.
