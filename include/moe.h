@@ -130,11 +130,13 @@ typedef enum {
  *   PACKED     the copies moe_pack_weights writes (bf16 layers only): each
  *              expert's matrix cut into blocks of 32 rows x Wb columns (Wb =
  *              128 for W1 and W3, 256 for W2), each block stored as one
- *              contiguous run, so one K step of one output tile of the
- *              expert GEMMs reads whole runs instead of a short piece of
- *              each of 32 rows.  For a [K, N] matrix of expert e, with N'
- *              = N rounded up to Wb, element (k, n) sits at
- *                e*K*N' + ((k/32)*(N'/Wb) + n/Wb)*32*Wb + (k%32)*Wb + n%Wb
+ *              contiguous run, column by column (the 32 values of one
+ *              column next to each other), so one K step of one output
+ *              tile of the expert GEMMs reads whole runs instead of a short
+ *              piece of each of 32 rows, already in the k-contiguous order
+ *              the matrix-core operands take.  For a [K, N] matrix of
+ *              expert e, with N' = N rounded up to Wb, element (k, n) sits at
+ *                e*K*N' + ((k/32)*(N'/Wb) + n/Wb)*32*Wb + (n%Wb)*32 + k%32
  *              and the N' - N pad columns hold zeros. */
 typedef enum {
   MOE_WEIGHTS_ROW_MAJOR = 0,

@@ -46,7 +46,8 @@ namespace moe {
 namespace {
 namespace dma {
 
-template <bool SWIGLU, class S>
+template <bool SWIGLU, class S, bool BT>
+// BT: packed weights (B stage in column rows, see TileSources).
 // The second launch bound is the minimum wavefronts per SIMD: BLOCKS_PER_CU
 // workgroups of NW wavefronts over 4 SIMDs, which caps the registers.
 __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grouped_bf16_dma_kernel(
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   const int n0 = tc.ntile * NOUT;
 
   // ---- DMA sources ---------------------------------------------------------
-  TileSources<SWIGLU, S> src;
+  TileSources<SWIGLU, S, BT> src;
   src.init(p, tc, wave, lane, n0, boff);
 
   // LDS byte address of this wavefront's destinations in stage 0
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
     return frag_a<S>(smem + stage * S::STAGE, wm, h, i, lane);
   };
   auto rd_b = [&](int stage, int h, int j) __attribute__((always_inline)) -> bf16x8 {
-    return frag_b<S, SWIGLU>(smem + stage * S::STAGE, wn, h, j, lane);
+    return frag_b<S, SWIGLU, BT>(smem + stage * S::STAGE, wn, h, j, lane);
   };
   // MV: row fragments of this wavefront that hold tile rows (a constant of
   // the specialised pipeline below); the others are neither read nor
@@ -261,11 +262,16 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
 //      one workgroup per CU.  For a few hundred rows per expert (fine-grained
 //      experts, where the weights' HBM traffic is the bound): one M-tile per
 //      expert reads each weight tile once, and on an expert's short tile the
-//      16-row fragments past its end are skipped.
+//      16-row fragments past its end are skipped.  Also for thousands of rows
+//      per expert.  With packed weights the same M-tile is run by 16
+//      wavefronts (4 x 4) of 64 x 64 over 3 stages (96 KB): with the packed
+//      B path the 8-wavefront form spills registers at 4 stages, and the
+//      16-wavefront form measured 0.2-0.3% faster than it at 3.
 using ShapeShort = Shape<32, 256, 64, 4, 1, 4>;
 using ShapeShortN = Shape<32, 128, 64, 4, 1, 4>;
 using ShapeLongA = Shape<128, 256, 32, 8, 2, 3>;
 using ShapeWide = Shape<256, 256, 32, 8, 4, 4>;
+using ShapeWidePacked = Shape<256, 256, 32, 16, 4, 3>;
 
 }  // namespace dma
 
@@ -389,9 +395,10 @@ __global__ __launch_bounds__(256) void gather_blocked_kernel(
   }
 }
 
-// Packed weights: output element o (8 at a time, consecutive threads on
-// consecutive 16 bytes) of expert e is element (k, n) of its row-major
-// [K, N] matrix, or 0 past column N.
+// Packed weights: output elements o..o+7 (consecutive threads on consecutive
+// 16 bytes) of expert e are elements (k..k+7, n) of its row-major [K, N]
+// matrix, or 0 past column N: each 32 x W block is stored column by column.
+// A one-off copy, so the 8 reads along a column are plain 2-byte loads.
 __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t* __restrict__ src,
                                                           int64_t nexp, int K, int N, int W,
                                                           int Npad, uint16_t* __restrict__ dst) {
@@ -405,29 +412,45 @@ __global__ __launch_bounds__(256) void pack_blocks_kernel(const uint16_t* __rest
     const int64_t rem = o - e * per;
     const int64_t blk = rem / (32 * W);
     const int within = static_cast<int>(rem - blk * 32 * W);
-    const int k = static_cast<int>(blk / nbw) * 32 + within / W;
-    const int n = static_cast<int>(blk % nbw) * W + within % W;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (n < N) v = *reinterpret_cast<const u32x4*>(src + (e * K + k) * static_cast<int64_t>(N) + n);
-    *reinterpret_cast<u32x4*>(dst + o) = v;
+    const int k = static_cast<int>(blk / nbw) * 32 + (within & 31);
+    const int n = static_cast<int>(blk % nbw) * W + (within >> 5);
+    uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (n < N) {
+      const uint16_t* col = src + (e * K + k) * static_cast<int64_t>(N) + n;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = col[static_cast<int64_t>(q) * N];
+    }
+    u32x4 w4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w4[q] = static_cast<uint32_t>(v[2 * q]) | (static_cast<uint32_t>(v[2 * q + 1]) << 16);
+    *reinterpret_cast<u32x4*>(dst + o) = w4;
   }
 }
 
 }  // namespace
 
-template <bool SWIGLU, class S>
+template <bool SWIGLU, class S, bool BT>
 hipError_t launch_bf16_shape(const GroupedGemm& g, hipStream_t s) {
   const int cols = SWIGLU ? S::BN / 2 : S::BN;
-  return dma::launch_grid(dma::grouped_bf16_dma_kernel<SWIGLU, S>, g, (g.N + cols - 1) / cols, s, S::NW);
+  return dma::launch_grid(dma::grouped_bf16_dma_kernel<SWIGLU, S, BT>, g, (g.N + cols - 1) / cols, s,
+                          S::NW);
+}
+template <bool SWIGLU, bool BT>
+hipError_t launch_bf16_layout(const GroupedGemm& g, hipStream_t s) {
+  if (g.bm == kGroupedBMShort) {
+    if (g.narrow_n) return launch_bf16_shape<SWIGLU, dma::ShapeShortN, BT>(g, s);
+    return launch_bf16_shape<SWIGLU, dma::ShapeShort, BT>(g, s);
+  }
+  if (g.bm == kGroupedBMWide) {
+    if constexpr (BT) return launch_bf16_shape<SWIGLU, dma::ShapeWidePacked, BT>(g, s);
+    else return launch_bf16_shape<SWIGLU, dma::ShapeWide, BT>(g, s);
+  }
+  return launch_bf16_shape<SWIGLU, dma::ShapeLongA, BT>(g, s);
 }
 template <bool SWIGLU>
 hipError_t launch_bf16(const GroupedGemm& g, hipStream_t s) {
-  if (g.bm == kGroupedBMShort) {
-    if (g.narrow_n) return launch_bf16_shape<SWIGLU, dma::ShapeShortN>(g, s);
-    return launch_bf16_shape<SWIGLU, dma::ShapeShort>(g, s);
-  }
-  if (g.bm == kGroupedBMWide) return launch_bf16_shape<SWIGLU, dma::ShapeWide>(g, s);
-  return launch_bf16_shape<SWIGLU, dma::ShapeLongA>(g, s);
+  if (g.b_block_cols > 0) return launch_bf16_layout<SWIGLU, true>(g, s);
+  return launch_bf16_layout<SWIGLU, false>(g, s);
 }
 hipError_t launch_pack_blocks(const void* src, int64_t nexp, int K, int N, int W, void* dst,
                               hipStream_t s) {

@@ -24,7 +24,8 @@ def reference_pack(W: torch.Tensor, block: int) -> torch.Tensor:
     Np = -(-N // block) * block
     P = torch.zeros((n, K, Np), dtype=W.dtype)
     P[:, :, :N] = W
-    return P.view(n, K // 32, 32, Np // block, block).permute(0, 1, 3, 2, 4).reshape(-1)
+    # [expert, k block, n block, column in block, k in block]
+    return P.view(n, K // 32, 32, Np // block, block).permute(0, 1, 3, 4, 2).reshape(-1)
 
 
 def packed_copies(run: Run, cfg):
