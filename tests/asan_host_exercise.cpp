@@ -108,6 +108,6 @@ int main() {
   int64_t launches[4];
   double ms[4];
   EXPECT(moe_timing_read(names, launches, ms, 4) == 0);
-  printf("asan host driver: %d failures\n", failures);
+  printf("asan host exercise: %d failures\n", failures);
   return failures ? 1 : 0;
 }

@@ -1,6 +1,6 @@
 """The host layer (argument checks, capacity, workspace plans, statistics
 bookkeeping, training helpers) built with AddressSanitizer on the host side
-only and run over tests/asan_host_driver.cpp.  No GPU: the driver only takes
+only and run over tests/asan_host_exercise.cpp.  No GPU: the exercise program only takes
 paths that return before any kernel launch.  The kernels' objects are the
 ones the regular build wrote (_build/obj)."""
 import os
@@ -29,12 +29,12 @@ def test_host_layer_under_asan():
                                      "moe_api.cpp"), "-o", api_o],
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
-    drv_o = os.path.join(OUT, "asan_host_driver.o")
+    drv_o = os.path.join(OUT, "asan_host_exercise.o")
     r = subprocess.run([HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
-                        *asan, "-x", "c++", "-c", os.path.join(ROOT, "tests", "asan_host_driver.cpp"),
+                        *asan, "-x", "c++", "-c", os.path.join(ROOT, "tests", "asan_host_exercise.cpp"),
                         "-o", drv_o], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
-    exe = os.path.join(OUT, "asan_host_driver")
+    exe = os.path.join(OUT, "asan_host_exercise")
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", *asan, drv_o, api_o,
                         *[os.path.join(OBJ, o) for o in KERNEL_OBJS], "-o", exe],
                        capture_output=True, text=True, timeout=600)
