@@ -19,6 +19,21 @@ inline bool router_parts_fit(int64_t T, int E, int d) {
 }
 hipError_t launch_router_parts(const void* x, const void* Wg, int T, int d, int E, int nparts,
                                float* lpart, hipStream_t s);
+// Router scores of a bf16 batch with 8 <= E <= 64 experts (E % 8 == 0) as
+// nparts K parts (lpart[p][t][e], parts T * E apart) on the matrix cores,
+// for the top-k pass to add in part order.  d a multiple of 64 * nparts; the
+// part's transposed W_gate rows must fit the workgroup's 64 KB of LDS; x and
+// Wg 16-byte aligned.
+inline size_t router_narrow_lds(int E, int KP) {
+  return static_cast<size_t>(16) * ((E + 15) / 16) * (KP + 8) * 2;
+}
+inline bool router_narrow_fit(int64_t T, int E, int d, int nparts) {
+  return E >= 8 && E <= 64 && E % 8 == 0 && T >= 1 && T <= (int64_t(1) << 30) &&
+         nparts >= 1 && d > 0 && d % (64 * nparts) == 0 &&
+         router_narrow_lds(E, d / nparts) <= 64 * 1024;
+}
+hipError_t launch_router_narrow(const void* x, const void* Wg, int64_t T, int d, int E,
+                                int nparts, float* lpart, hipStream_t s);
 int topk_group_size(int E);
 // Router scores are read as the sum of `nsplit` partial arrays (split_stride
 // apart) plus the optional bias, in a fixed order; when logits_out is given

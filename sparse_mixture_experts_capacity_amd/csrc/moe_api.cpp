@@ -149,6 +149,7 @@ struct Plan {
   int static_bm = 0;             // M-tile of the GEMMs over all T token rows
   bool mfma_router = false;      // router scores on the MFMA GEMM (bf16, E % 8 == 0)
   bool parts_router = false;     // short batches: the K-part router instead
+  bool narrow_router = false;    // few experts: the narrow MFMA router instead
   int router_split = 1;          // K parts of the router GEMM
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
@@ -377,6 +378,10 @@ int make_plan(const moe_config_t* c, Plan* p) {
     const int64_t mt = (p->T + p->static_bm - 1) / p->static_bm;
     int64_t ks = mt > 0 ? (512 + mt - 1) / mt : 1;
     if (ks > 16) ks = 16;
+    // Many experts (E > 64): each part adds 4 T E bytes of partial sums to
+    // write and read back, and at most 8 parts measured faster (160 experts:
+    // router + top-k 45 against 51 us with 16).
+    if (p->E > 64 && ks > 8) ks = 8;
     if (ks > kk) ks = kk;
     if (ks < 1) ks = 1;
     while (kk % ks) --ks;
@@ -388,6 +393,18 @@ int make_plan(const moe_config_t* c, Plan* p) {
       while (kk % np) --np;
       p->router_split = np;
       p->parts_router = true;
+    } else {
+      // Up to 64 experts: a kernel whose weight operand is E columns wide
+      // rather than a 256-wide GEMM tile, in parts of 256 columns where d
+      // allows at most 16 of them (each wavefront then has its part's token
+      // loads in flight at once), else in the parts above.
+      const int np = p->d % 256 == 0 ? p->d / 256 : 0;
+      if (np >= 1 && np <= 16 && moe::router_narrow_fit(p->T, p->E, p->d, np)) {
+        p->router_split = np;
+        p->narrow_router = true;
+      } else if (moe::router_narrow_fit(p->T, p->E, p->d, p->router_split)) {
+        p->narrow_router = true;
+      }
     }
   }
   // Down projections with few tiles (short batches: a few rows per expert)
@@ -546,6 +563,11 @@ int run_router(const Plan& p, void* ws, const void* x, const void* W_gate,
     Timed t("router", s);
     HIP_TRY(moe::launch_router_parts(x, W_gate, static_cast<int>(p.T), p.d, p.E, p.router_split,
                                      at<float>(ws, p.lpart), s));
+    *sc = Scores{at<float>(ws, p.lpart), p.router_split, p.T * p.E, bias};
+  } else if (p.narrow_router) {
+    Timed t("router", s);
+    HIP_TRY(moe::launch_router_narrow(x, W_gate, p.T, p.d, p.E, p.router_split,
+                                      at<float>(ws, p.lpart), s));
     *sc = Scores{at<float>(ws, p.lpart), p.router_split, p.T * p.E, bias};
   } else if (p.mfma_router) {
     moe::GroupedGemm r{};

@@ -229,6 +229,126 @@ hipError_t launch_router_parts(const void* x, const void* Wg, int T, int d, int 
 }
 
 // ---------------------------------------------------------------------------
+// Router scores of a bf16 batch with few experts (E a multiple of 8, at most
+// 64) in K parts, on the matrix cores ([Mixtral explainer] "Plain
+// explanation" para 3: one score per expert from the token's vector).  Part
+// p of score (t, e) is the sum over columns [p KP, (p+1) KP) of x[t][c]
+// Wg[c][e], and the top-k pass adds the parts in part order.  A workgroup
+// takes one part and 64 tokens.  It stages the part's W_gate rows in LDS
+// transposed: one row of KP values per expert, 16 NJ rows with those past E
+// zero, each row padded by 16 bytes so that the 16 rows one read touches
+// fall in different bank groups.  Each of its four wavefronts multiplies 16
+// tokens with v_mfma_f32_16x16x32_bf16 (lane l: token l % 16, k block
+// l / 16), reading the token fragments straight from memory in chunks of
+// kNarrowSteps K steps (16 bytes per lane each): the first chunk is loaded
+// while the weights are staged, and each next one while the current one is
+// multiplied.  The tiled expert GEMM would give the scores a 256-wide weight
+// tile; here the weight operand is E columns rounded up to 16.
+// ---------------------------------------------------------------------------
+constexpr int kNarrowSteps = 8;
+template <int NJ>
+__global__ __launch_bounds__(256) void router_narrow_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wg, int T, int d, int E,
+    int KP, float* __restrict__ lpart) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t wt[];   // [16 NJ][KP + 8]
+  const int RS = KP + 8;
+  const int part = blockIdx.y;
+  const int64_t k0 = static_cast<int64_t>(part) * KP;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * 64 + wave * 16;
+  const bool active = t0 < T;   // wave-uniform
+  // rows past T repeat row T - 1 (their sums are not stored)
+  const int trow = min(t0 + i16, T - 1);
+  const uint16_t* xr = x + static_cast<int64_t>(trow) * d + k0 + g * 8;
+  const int nsteps = KP / 32;
+  // K steps s0 .. s0+7 of this lane's token fragment; steps past the part
+  // repeat its last step (loaded, never multiplied), so every load is
+  // unconditional and the waits before the MFMAs count exactly.
+  auto load_chunk = [&](bf16x8 (&a)[kNarrowSteps], int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kNarrowSteps; ++c)
+      a[c] = *reinterpret_cast<const bf16x8*>(xr + min(s0 + c, nsteps - 1) * 32);
+  };
+  // The first chunk's token fragments are in flight while the weights are
+  // staged (also in wavefronts past T, whose rows all repeat row T - 1:
+  // unconditional, so nothing waits on them before the staging).
+  bf16x8 a[kNarrowSteps];
+  load_chunk(a, 0);
+  // W_gate rows k0 .. k0+KP: thread -> row kk, 16 bytes (8 experts) at a time
+  const int eg = E >> 3;
+  for (int kk = threadIdx.x; kk < KP; kk += blockDim.x) {
+    const uint16_t* wrow = Wg + (k0 + kk) * E;
+    for (int q = 0; q < eg; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(wrow + q * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wt[(q * 8 + 2 * j) * RS + kk] = static_cast<uint16_t>(v[j] & 0xffffu);
+        wt[(q * 8 + 2 * j + 1) * RS + kk] = static_cast<uint16_t>(v[j] >> 16);
+      }
+    }
+  }
+  for (int r = E; r < 16 * NJ; ++r)
+    for (int kk = threadIdx.x; kk < KP; kk += blockDim.x) wt[r * RS + kk] = 0;
+  __syncthreads();
+  if (!active) return;   // no barrier follows
+
+  const uint16_t* wr = wt + i16 * RS + g * 8;
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsteps; s0 += kNarrowSteps) {
+    // the next chunk's loads go out before this chunk is multiplied
+    bf16x8 an[kNarrowSteps];
+    const bool more = s0 + kNarrowSteps < nsteps;
+    if (more) load_chunk(an, s0 + kNarrowSteps);
+#pragma unroll
+    for (int c = 0; c < kNarrowSteps; ++c) {
+      if (s0 + c < nsteps) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(wr + j * 16 * RS + (s0 + c) * 32);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], b, acc[j], 0, 0, 0);
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < kNarrowSteps; ++c) a[c] = an[c];
+    }
+  }
+  // lane l holds tokens t0 + 4 (l / 16) + r, expert 16 j + l % 16
+  float* out = lpart + static_cast<int64_t>(part) * T * E;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * 16 + i16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + g * 4 + r;
+      if (t < T && e < E) out[static_cast<int64_t>(t) * E + e] = acc[j][r];
+    }
+  }
+}
+
+hipError_t launch_router_narrow(const void* x, const void* Wg, int64_t T, int d, int E,
+                                int nparts, float* lpart, hipStream_t s) {
+  if (!router_narrow_fit(T, E, d, nparts)) return hipErrorInvalidValue;
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* wb = static_cast<const uint16_t*>(Wg);
+  const int KP = d / nparts;
+  const int NJ = (E + 15) / 16;
+  const size_t lds = router_narrow_lds(E, KP);
+  const dim3 grid(static_cast<unsigned>((T + 63) / 64), static_cast<unsigned>(nparts));
+  const int Ti = static_cast<int>(T);
+  if (NJ == 1) router_narrow_kernel<1><<<grid, 256, lds, s>>>(xb, wb, Ti, d, E, KP, lpart);
+  else if (NJ == 2) router_narrow_kernel<2><<<grid, 256, lds, s>>>(xb, wb, Ti, d, E, KP, lpart);
+  else if (NJ == 3) router_narrow_kernel<3><<<grid, 256, lds, s>>>(xb, wb, Ti, d, E, KP, lpart);
+  else router_narrow_kernel<4><<<grid, 256, lds, s>>>(xb, wb, Ti, d, E, KP, lpart);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Top-k + gates + softmax statistics.  A group of G lanes (G a power of two,
 // G >= E/4) handles one token; lane g of the group holds the scores of
 // experts g, g+G, g+2G, g+3G.  k rounds of a group-wide argmax by butterfly

@@ -309,6 +309,19 @@ ROUTE_CASES = {
                                    capacity_factor=1.0, bias=SKEW_BIAS),
     # 5 parts of 128 columns, T at the token bound
     "bf16_parts_T8_d640": Workload("bf16_p8", T=8, d=640, F=64, E=8, k=2),
+    # the narrow MFMA router (E a multiple of 8 up to 64, beyond the K-part
+    # router's batches): one, two and four 16-expert column fragments,
+    # ragged last token groups, a score bias
+    "bf16_narrow_E16": Workload("bf16_n16", T=333, d=384, F=64, E=16, k=4,
+                                gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    "bf16_narrow_E24_bias": Workload("bf16_n24", T=190, d=640, F=64, E=24, k=3,
+                                     capacity_factor=1.0, bias=(2.0,) * 3 + (0.0,) * 21),
+    "bf16_narrow_E64": Workload("bf16_n64", T=257, d=1024, F=64, E=64, k=6,
+                                gating=SOFTMAX_THEN_TOPK, renormalize=False),
+    # d not a multiple of 256: 3 parts of 448 columns, a full chunk of K
+    # steps and a 6-step tail per part
+    "bf16_narrow_long_parts": Workload("bf16_nlong", T=17000, d=1344, F=64, E=8, k=2,
+                                       capacity_factor=1.25),
 }
 
 
