@@ -110,13 +110,13 @@ struct GroupedGemm {
   int64_t c_block_rows;     // SwiGLU output H
   // Packed B (bf16 kernels): 0 = row-major with row stride ldb; otherwise the
   // block width W (128 or 256): element (k, n) of an expert's matrix at
-  // ((k / 32) * (ldb / W) + n / W) * 32 * W + (k % 32) * W + n % W, with ldb
+  // ((k / 32) * (ldb / W) + n / W) * 32 * W + (n % W) * 32 + k % 32, with ldb
   // the padded N (a multiple of W) and b_stride = K * ldb.
   int b_block_cols;
 };
 // Packed copy of nexp row-major [K, N] bf16 matrices in the layout above
 // (block width W, padded width Npad = N rounded up to W; pad columns zero).
-// K % 32 == 0, N % 8 == 0.
+// K % 32 == 0.
 hipError_t launch_pack_blocks(const void* src, int64_t nexp, int K, int N, int W, void* dst,
                               hipStream_t s);
 // Xb = kept token rows x[perm[s] / topk] for slots s < *nrows_dev, K-blocked
