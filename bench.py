@@ -34,9 +34,9 @@ MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM on packed weights (the default layout); the counter
     # summaries are kept beside the profiles
-    "mixtral_prefill": ("cc52cda822aa5599", 3956.06e6, 122.05e6),
-    "deepseek": ("cc52cda822aa5599", 5342.25e6, 75.62e6),
-    "mixtral_decode_t64": ("cc52cda822aa5599", 1886.98e6, 3.67e6),
+    "mixtral_prefill": ("a4bd67f25a1bf969", 4018.20e6, 122.38e6),
+    "deepseek": ("a4bd67f25a1bf969", 5341.25e6, 75.62e6),
+    "mixtral_decode_t64": ("a4bd67f25a1bf969", 1886.96e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.

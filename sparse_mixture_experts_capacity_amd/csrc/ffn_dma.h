@@ -36,16 +36,30 @@ __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
   TileCoords tc{0, 0, 0, 0, 0, 0, false};
   const int ntn_all = ntn * p.ngroups_n;
   const int mtiles = p.tiles ? *p.ntiles : (p.static_rows + TBM - 1) / TBM;
-  const int ks = p.ksplit;
-  const int total = mtiles * ntn_all * ks;
-  const int per = (total + 7) >> 3;
   const int x = blockIdx.x & 7;
   const int i = blockIdx.x >> 3;
-  if (i >= per) return tc;
-  const int LK = x * per + i;
-  if (LK >= total) return tc;
-  tc.kpart = LK % ks;   // K parts of one tile are adjacent: they share A rows
-  const int L = LK / ks;
+  int L;
+  if (p.kcut_slots > 0) {
+    // Two K parts cut unevenly (kcut_steps): each XCD takes a contiguous
+    // eighth of the tiles and runs all their part-0 units before any part-1
+    // unit, so the longer parts go first and the M-tiles of one weight tile
+    // still start each part together.
+    const int ntiles = mtiles * ntn_all;
+    const int tx = (ntiles + 7) >> 3;
+    if (i >= 2 * tx) return tc;
+    tc.kpart = i >= tx ? 1 : 0;
+    L = x * tx + i - tc.kpart * tx;
+    if (L >= ntiles) return tc;
+  } else {
+    const int ks = p.ksplit;
+    const int total = mtiles * ntn_all * ks;
+    const int per = (total + 7) >> 3;
+    if (i >= per) return tc;
+    const int LK = x * per + i;
+    if (LK >= total) return tc;
+    tc.kpart = LK % ks;   // K parts of one tile are adjacent: they share A rows
+    L = LK / ks;
+  }
   int m, n_all;
   if (p.tiles) {
     // expert e owns logical tiles [tstart[e] * ntn_all, tstart[e+1] * ntn_all)
@@ -73,6 +87,29 @@ __device__ __forceinline__ TileCoords tile_coords(const GroupedGemm& p, int ntn,
   tc.ntile = n_all % ntn;
   tc.valid = tc.nrows > 0;
   return tc;
+}
+
+// The K step where part 0 ends when a plain GEMM's two K parts are cut
+// unevenly for `slots` resident workgroups (part-0 units dispatched first).
+// With ntiles = k slots + rem: part 0 takes (k+1)/(k+2) of K when rem
+// (k+2) <= slots, so the slots that ran a long part 0 and then a short part
+// 1 finish with those that ran two long parts; 2/3 when there are fewer
+// tiles than slots but more than half as many; otherwise half.  (Modelled as
+// rounds of equal tiles: 592 tiles on 512 slots take 1.33 tile lengths
+// instead of 1.5 with equal halves.)
+__device__ __forceinline__ int kcut_steps(int nk, int ntiles, int slots) {
+  const int k = ntiles / slots;
+  const int rem = ntiles - k * slots;
+  int num = 1, den = 2;
+  if (k >= 1 && rem * (k + 2) <= slots) {
+    num = k + 1;
+    den = k + 2;
+  } else if (k == 0 && 2 * ntiles > slots) {
+    num = 2;
+    den = 3;
+  }
+  const int cut = (nk * num + den / 2) / den;
+  return min(max(cut, 1), nk - 1);
 }
 
 // ===========================================================================
@@ -446,9 +483,11 @@ __device__ __forceinline__ void store_tile(const GroupedGemm& p, const TileCoord
 // rounded up to whole groups of 8 (one per XCD).
 template <typename Kern>
 hipError_t launch_grid(Kern kern, const GroupedGemm& g, int ntn, hipStream_t s, int waves = 4) {
-  const int64_t logical = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n * g.ksplit;
-  if (logical <= 0) return hipSuccess;
-  const int nblocks = static_cast<int>((logical + 7) / 8 * 8);
+  const int64_t tiles = static_cast<int64_t>(g.max_mtiles) * ntn * g.ngroups_n;
+  if (tiles <= 0) return hipSuccess;
+  // unevenly cut parts: two blocks per tile of each XCD's eighth
+  const int nblocks = g.kcut_slots > 0 ? static_cast<int>(16 * ((tiles + 7) / 8))
+                                       : static_cast<int>((tiles * g.ksplit + 7) / 8 * 8);
   kern<<<nblocks, 64 * waves, 0, s>>>(g, ntn, nblocks);
   return hipGetLastError();
 }

@@ -76,10 +76,16 @@ __global__ __launch_bounds__(64 * S::NW, S::BLOCKS_PER_CU * S::NW / 4) void grou
   // (wave-uniform: M0 takes it).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
-  // This block's share of K: part kpart of ksplit near-equal runs of BK steps.
+  // This block's share of K: part kpart of ksplit near-equal runs of BK
+  // steps, or of two parts cut at kcut_steps.
   const int nk_all = p.K / BK;
-  const int kb0 = static_cast<int>(static_cast<int64_t>(tc.kpart) * nk_all / p.ksplit);
-  const int kb1 = static_cast<int>(static_cast<int64_t>(tc.kpart + 1) * nk_all / p.ksplit);
+  int kb0 = static_cast<int>(static_cast<int64_t>(tc.kpart) * nk_all / p.ksplit);
+  int kb1 = static_cast<int>(static_cast<int64_t>(tc.kpart + 1) * nk_all / p.ksplit);
+  if (p.kcut_slots > 0) {
+    const int cut = kcut_steps(nk_all, *p.ntiles * ntn * p.ngroups_n, p.kcut_slots);
+    kb0 = tc.kpart ? cut : 0;
+    kb1 = tc.kpart ? nk_all : cut;
+  }
   const int kbase = kb0 * BK;
   // step: K step to load; stage: its ring slot (step % NS).
   auto issue = [&](int step, int stage) __attribute__((always_inline)) {

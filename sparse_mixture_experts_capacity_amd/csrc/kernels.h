@@ -113,6 +113,10 @@ struct GroupedGemm {
   // ((k / 32) * (ldb / W) + n / W) * 32 * W + (n % W) * 32 + k % 32, with ldb
   // the padded N (a multiple of W) and b_stride = K * ldb.
   int b_block_cols;
+  // > 0 (plain GEMM, ksplit 2, device tile list): the two K parts are cut at
+  // the step that suits this many resident workgroups for the tiles that
+  // exist, and each XCD runs its tiles' part-0 units first; 0 = equal parts.
+  int kcut_slots;
 };
 // Packed copy of nexp row-major [K, N] bf16 matrices in the layout above
 // (block width W, padded width Npad = N rounded up to W; pad columns zero).

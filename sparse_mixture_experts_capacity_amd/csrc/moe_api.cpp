@@ -151,6 +151,7 @@ struct Plan {
   bool parts_router = false;     // short batches: the K-part router instead
   bool narrow_router = false;    // few experts: the narrow MFMA router instead
   int router_split = 1;          // K parts of the router GEMM
+  int ffn2_kcut_slots = 0;       // > 0: the routed down projection's two K parts cut for this many slots
   int ffn2_split = 1;            // K parts of the routed down projection
   int shared2_split = 1;         // K parts of the shared down projection
   bool small_route = false;      // top-k and dispatch in one workgroup
@@ -425,8 +426,11 @@ int make_plan(const moe_config_t* c, Plan* p) {
     if (p->path == MOE_PATH_AUTO && p->ffn2_split == 1 && p->bm != moe::kGroupedBMShort) {
       const int64_t slots = static_cast<int64_t>(device_cus()) * (p->bm == moe::kGroupedBM ? 2 : 1);
       const int64_t t = mt_est * ntn2;
-      if (slots > 0 && t > slots && t < 4 * slots && (t % slots) != 0 && (t % slots) <= slots / 2)
+      if (slots > 0 && t > slots && t < 4 * slots && (t % slots) != 0 && (t % slots) <= slots / 2) {
         p->ffn2_split = 2;
+        // where to cut K is decided on the device from the tiles that exist
+        p->ffn2_kcut_slots = static_cast<int>(slots);
+      }
     }
     if (p->S > 0) {
       const int64_t mts = (p->T + p->static_bm - 1) / p->static_bm;
@@ -821,7 +825,7 @@ int moe_forward(const void* x, const void* W_gate, const void* W1, const void* W
   g2.A = at<void>(ws, p.H); g2.lda = p.F; g2.perm = nullptr; g2.B = W2; g2.B3 = nullptr;
   g2.ldb = D2; g2.b_stride = static_cast<int64_t>(p.F) * D2; g2.b_block_cols = packed ? kPackW2 : 0;
   g2.K = p.F; g2.N = p.d; g2.C = at<void>(ws, p.Y); g2.ldc = p.d;
-  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d;
+  g2.ksplit = p.ffn2_split; g2.c_split = p.rows_max * p.d; g2.kcut_slots = p.ffn2_kcut_slots;
   g2.narrow_n = p.bm == moe::kGroupedBMShort ? 1 : 0;
   g2.a_block_rows = g1.c_block_rows;   // GEMM2 reads H as GEMM1 wrote it
   g2.c_block_rows = 0;
