@@ -34,9 +34,9 @@ MEASURED_TRAFFIC = {
     # workload: (source digest, fetch bytes, write bytes) per launch of the
     # routed SwiGLU GEMM on packed weights (the default layout); the counter
     # summaries are kept beside the profiles
-    "mixtral_prefill": ("a4bd67f25a1bf969", 4018.20e6, 122.38e6),
-    "deepseek": ("a4bd67f25a1bf969", 5341.25e6, 75.62e6),
-    "mixtral_decode_t64": ("a4bd67f25a1bf969", 1886.96e6, 3.67e6),
+    "mixtral_prefill": ("1ee5ca5811ba4faf", 3942.88e6, 122.20e6),
+    "deepseek": ("1ee5ca5811ba4faf", 5342.00e6, 75.63e6),
+    "mixtral_decode_t64": ("1ee5ca5811ba4faf", 1886.95e6, 3.67e6),
 }
 # The sources that define the routed SwiGLU GEMM and its launch: the kernel,
 # the M-tile list built by the routing passes, the plan and the shared headers.

@@ -553,33 +553,41 @@ hipError_t launch_topk_gate(const float* lpart, int nsplit, int64_t split_stride
 
 // ---------------------------------------------------------------------------
 // Dispatch, pass 1: stable rank of each assignment inside its chunk of
-// kDispatchChunk assignments.  One wavefront walks the chunk 64 assignments
-// at a time; lanes with the same expert are found with 8 ballots (one per
-// bit of the expert id) and ranked by popcount of the lower lanes; LDS
-// counters carry the rank across steps.  Writes the chunk's per-expert
-// totals.
+// kDispatchChunk assignments.  Each of the workgroup's kRankWaves wavefronts
+// walks a quarter of the chunk 64 assignments at a time; lanes with the same
+// expert are found with 8 ballots (one per bit of the expert id) and ranked
+// by popcount of the lower lanes; the wavefront's LDS counters carry the
+// rank across its steps.  The quarters are then joined in order: a rank is
+// offset by the counts of the same expert in the earlier quarters.  Writes
+// the chunk's per-expert totals.  (One wavefront over the whole chunk took
+// four times the serial steps.)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void dispatch_rank_kernel(
+constexpr int kRankWaves = 4;
+static_assert(kDispatchChunk % (kRankWaves * kWave) == 0, "rank chunk");
+__global__ __launch_bounds__(kRankWaves * kWave) void dispatch_rank_kernel(
     const int32_t* __restrict__ topk_idx, int64_t TK, int E,
     int32_t* __restrict__ lrank, int32_t* __restrict__ blkcnt) {
-  __shared__ int cnt[kMaxExperts];
-  const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __shared__ int cnt[kRankWaves][kMaxExperts];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) cnt[i / E][i % E] = 0;
   __syncthreads();
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
+  constexpr int kQuarter = kDispatchChunk / kRankWaves;
+  constexpr int kSteps = kQuarter / kWave;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kDispatchChunk + wave * kQuarter;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   // All of the lane's expert ids are loaded before the first is ranked, so
   // the loads are in flight together rather than one per step.
-  constexpr int kSteps = kDispatchChunk / kWave;
   int ids[kSteps];
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
     const int64_t a = base + it * kWave + lane;
     ids[it] = a < TK ? topk_idx[a] : -1;
   }
+  int* c = cnt[wave];
+  int rk[kSteps];
 #pragma unroll
   for (int it = 0; it < kSteps; ++it) {
-    const int64_t a = base + it * kWave + lane;
     const int ein = ids[it];
     const bool valid = ein >= 0 && ein < E;   // ids outside [0, E) are ignored
     const int e = valid ? ein : 0;
@@ -590,15 +598,30 @@ __global__ __launch_bounds__(64) void dispatch_rank_kernel(
       const uint64_t m = __ballot(bit);
       match &= bit ? m : ~m;
     }
-    const int before = valid ? cnt[e] : 0;
-    __syncthreads();
+    const int before = valid ? c[e] : 0;
+    __builtin_amdgcn_wave_barrier();
     const bool leader = valid && (__ffsll(static_cast<unsigned long long>(match)) - 1 == lane);
-    if (leader) cnt[e] = before + __popcll(match);
-    __syncthreads();
-    if (valid) lrank[a] = before + __popcll(match & lt);
+    if (leader) c[e] = before + __popcll(match);
+    __builtin_amdgcn_wave_barrier();
+    rk[it] = before + __popcll(match & lt);
   }
-  for (int e = lane; e < E; e += kWave)
-    blkcnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kSteps; ++it) {
+    const int64_t a = base + it * kWave + lane;
+    const int ein = ids[it];
+    if (ein >= 0 && ein < E) {
+      int off = 0;
+      for (int w = 0; w < wave; ++w) off += cnt[w][ein];
+      lrank[a] = rk[it] + off;
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) total += cnt[w][e];
+    blkcnt[static_cast<int64_t>(blockIdx.x) * E + e] = total;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1049,7 +1072,7 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t TK, int E, int C,
                            int32_t* perm, int bm, Tile* tiles, int32_t* ntiles,
                            int32_t* tstart, const Reroute* rr, hipStream_t s) {
   const int nblk = static_cast<int>((TK + kDispatchChunk - 1) / kDispatchChunk);
-  dispatch_rank_kernel<<<nblk, 64, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
+  dispatch_rank_kernel<<<nblk, kRankWaves * kWave, 0, s>>>(topk_idx, TK, E, lrank, blkcnt);
   dispatch_scan_kernel<<<1, 256, 0, s>>>(blkcnt, nblk, E, C, counts, kcount,
                                          offsets, bm, tiles, ntiles, tstart);
   if (rr) {
