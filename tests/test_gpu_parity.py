@@ -537,6 +537,30 @@ def test_forward_full_size(name):
 
 
 # --------------------------------------------------------------------------
+# down projections split in two K parts to fill the last round of resident
+# workgroups, cut where the tiles that exist call for (on an MI355X's 512
+# slots): fewer tiles than slots (476, cut at 2/3 of K) and one round plus a
+# small remainder (544, cut at 2/3); d = 4352 also gives the router 4 parts
+# of 1088 columns (several rounds of in-flight K steps).  Packed weights,
+# every element, and the row-major forward's bits.
+# --------------------------------------------------------------------------
+KCUT_CASES = {
+    "below_one_round": Workload("bf16_kcut0", T=1536, d=4352, F=256, E=8, k=2,
+                                capacity_factor=1.25),
+    "one_round_plus": Workload("bf16_kcut1", T=1664, d=4352, F=256, E=8, k=2,
+                               capacity_factor=1.25),
+}
+
+
+@pytest.mark.parametrize("case", sorted(KCUT_CASES))
+def test_forward_down_projection_cut(case):
+    w = KCUT_CASES[case]
+    say(f"[kcut] {case}")
+    run = Run(w)
+    check_layer(run, f"kcut/{case}", packed=True, also_row_major=True)
+
+
+# --------------------------------------------------------------------------
 # both FFN paths: grouped (no K split) and streaming (K split as far as
 # possible), every output element
 # --------------------------------------------------------------------------
